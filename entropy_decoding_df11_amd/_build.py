@@ -1,0 +1,72 @@
+"""Build libdf11.so in-tree: host codec with g++, gfx950 kernels with hipcc.
+
+The shared library links the HIP runtime by its SONAME (libamdhip64.so.7) with
+torch's library directory first on the run path, so that a process that has
+imported torch resolves it to the runtime torch already loaded and torch's
+streams and allocations are valid inside the library.
+"""
+
+from __future__ import annotations
+
+import importlib.util
+import os
+import shutil
+import subprocess
+from typing import List
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_DIR, "include")
+BUILD_DIR = os.path.join(REPO_DIR, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libdf11.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+OFFLOAD_ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={OFFLOAD_ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-mcode-object-version=5",
+    # Packed FP32 instructions are kept out of every HIP build.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def _torch_lib_dir() -> str:
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return ""
+    return os.path.join(os.path.dirname(spec.origin), "lib")
+
+
+def _run(cmd: List[str], verbose: bool) -> None:
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source of the library and return the path of libdf11.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    host_obj = os.path.join(BUILD_DIR, "df11_host.o")
+    dev_obj = os.path.join(BUILD_DIR, "df11_decode.o")
+    _run(["g++", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
+          "-c", os.path.join(CSRC, "df11_host.cpp"), "-o", host_obj], verbose)
+    _run([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, "df11_decode.hip"),
+          "-o", dev_obj], verbose)
+    rpaths = [p for p in (_torch_lib_dir(), os.path.join(ROCM, "lib")) if p]
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, host_obj, dev_obj,
+          *[f"-Wl,-rpath,{p}" for p in rpaths]], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

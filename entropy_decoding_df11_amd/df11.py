@@ -1,0 +1,260 @@
+"""Python API over the DF11 C ABI.
+
+Method: "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan LLM menjadi
+70% ukurannya" (GeekNews).  Every step of encoding and decoding runs in
+libdf11.so; this module only moves arguments.  PyTorch provides device memory
+and streams.
+
+    t = compress(weight_bf16_cpu)          # host encode + upload
+    w = t.decompress()                     # bf16 tensor on the GPU, bit-exact
+    blk = compress_block({"q_proj": q, ...})
+    views = blk.decompress()               # one scratch buffer, a view per weight
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Dict, List, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+from . import _lib
+
+DEFAULT_BYTES_PER_THREAD = 8
+DEFAULT_THREADS_PER_GROUP = 256
+DEFAULT_DECODE_TABLE_BITS = 12
+
+ArrayLike = Union[np.ndarray, "torch.Tensor"]  # noqa: F821
+
+
+def _u16(x: ArrayLike) -> np.ndarray:
+    """BF16 bit patterns as a contiguous uint16 numpy array (host)."""
+    if isinstance(x, np.ndarray):
+        if x.dtype != np.uint16:
+            raise TypeError("numpy input must hold BF16 bit patterns as uint16")
+        return np.ascontiguousarray(x).reshape(-1)
+    import torch
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"expected a bfloat16 tensor, got {x.dtype}")
+    return x.detach().to("cpu").contiguous().reshape(-1).view(torch.int16).numpy().view(np.uint16)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def histogram(bf16: ArrayLike, hist: Optional[np.ndarray] = None) -> np.ndarray:
+    """Accumulate the exponent histogram (uint64[256]) of BF16 data."""
+    w = _u16(bf16)
+    if hist is None:
+        hist = np.zeros(256, dtype=np.uint64)
+    lib = _lib.load()
+    _lib.check(lib.df11_histogram(_ptr(w, ctypes.c_uint16), w.size, _ptr(hist, ctypes.c_uint64)), "df11_histogram")
+    return hist
+
+
+def build_codebook(hist: np.ndarray) -> _lib.Codebook:
+    hist = np.ascontiguousarray(hist, dtype=np.uint64)
+    cb = _lib.Codebook()
+    lib = _lib.load()
+    _lib.check(lib.df11_build_codebook(_ptr(hist, ctypes.c_uint64), ctypes.byref(cb)), "df11_build_codebook")
+    return cb
+
+
+def codebook_arrays(cb: _lib.Codebook) -> Dict[str, np.ndarray]:
+    """Copy a codebook into numpy arrays (code_lengths, codes, luts[n_luts])."""
+    return {
+        "code_lengths": np.ctypeslib.as_array(cb.code_lengths).copy(),
+        "codes": np.ctypeslib.as_array(cb.codes).copy(),
+        "luts": np.ctypeslib.as_array(cb.luts).copy()[: cb.n_luts],
+        "n_luts": int(cb.n_luts),
+        "max_len": int(cb.max_len),
+    }
+
+
+def decode_table(cb: _lib.Codebook, bits: int = DEFAULT_DECODE_TABLE_BITS) -> np.ndarray:
+    lib = _lib.load()
+    nbytes = lib.df11_decode_table_bytes(bits)
+    if nbytes == 0:
+        raise ValueError(f"unsupported decode table width {bits}")
+    table = np.zeros(nbytes // 4, dtype=np.uint32)
+    _lib.check(lib.df11_build_decode_table(ctypes.byref(cb), bits, table.ctypes.data_as(ctypes.c_void_p), nbytes),
+               "df11_build_decode_table")
+    return table
+
+
+@dataclasses.dataclass
+class HostStream:
+    """A DF11 stream in host memory (numpy buffers sized by the header)."""
+
+    header: _lib.Header
+    codebook: _lib.Codebook
+    enc: np.ndarray
+    sm: np.ndarray
+    gaps: np.ndarray
+    out_pos: np.ndarray
+
+    @property
+    def n_elements(self) -> int:
+        return int(self.header.n_elements)
+
+    def compressed_bytes(self) -> int:
+        """Algorithmic size: EncodedExponent (unpadded) + PackedSignMantissa +
+        Gaps (5 bits per thread) + output positions + LUTs + CodeLengths."""
+        h = self.header
+        return int((h.total_bits + 7) // 8 + h.n_elements + (5 * h.n_threads + 7) // 8 + 4 * (h.n_groups + 1)
+                   + 256 * (h.n_luts + 1))
+
+    def header_dict(self) -> Dict[str, int]:
+        return {name: int(getattr(self.header, name)) for name, _ in _lib.Header._fields_}
+
+
+def encode(bf16: ArrayLike, codebook: Optional[_lib.Codebook] = None,
+           bytes_per_thread: int = DEFAULT_BYTES_PER_THREAD,
+           threads_per_group: int = DEFAULT_THREADS_PER_GROUP) -> HostStream:
+    """Encode BF16 data on the host.  With no codebook, one is built from the
+    data's own histogram."""
+    w = _u16(bf16)
+    lib = _lib.load()
+    hist = histogram(w)
+    if codebook is None:
+        codebook = build_codebook(hist)
+    lay = _lib.Layout(bytes_per_thread, threads_per_group)
+    h = _lib.Header()
+    _lib.check(lib.df11_plan(ctypes.byref(codebook), _ptr(hist, ctypes.c_uint64), w.size, ctypes.byref(lay),
+                             ctypes.byref(h)), "df11_plan")
+    enc = np.empty(h.enc_bytes, dtype=np.uint8)
+    sm = np.empty(h.sm_bytes, dtype=np.uint8)
+    gaps = np.empty(h.gaps_bytes, dtype=np.uint8)
+    out_pos = np.empty(h.n_groups + 1, dtype=np.uint32)
+    _lib.check(lib.df11_encode(ctypes.byref(codebook), _ptr(w, ctypes.c_uint16), w.size, ctypes.byref(lay),
+                               ctypes.byref(h), _ptr(enc, ctypes.c_uint8), _ptr(sm, ctypes.c_uint8),
+                               _ptr(gaps, ctypes.c_uint8), _ptr(out_pos, ctypes.c_uint32)), "df11_encode")
+    return HostStream(h, codebook, enc, sm, gaps, out_pos)
+
+
+class DF11Tensor:
+    """A DF11 stream resident in GPU memory, decompressed on demand."""
+
+    def __init__(self, host: HostStream, shape: Sequence[int], device="cuda",
+                 decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS):
+        import torch
+        self.host_header = host.header
+        self.shape = tuple(int(s) for s in shape)
+        self.device = torch.device(device)
+        self.decode_table_bits = decode_table_bits
+
+        def up(a: np.ndarray) -> "torch.Tensor":
+            b = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+            if b.size == 0:
+                b = np.zeros(16, dtype=np.uint8)
+            return torch.from_numpy(b.copy()).to(self.device)
+
+        arrays = codebook_arrays(host.codebook)
+        self._bufs = {
+            "enc": up(host.enc),
+            "sm": up(host.sm),
+            "gaps": up(host.gaps),
+            "out_pos": up(host.out_pos),
+            "luts": up(arrays["luts"]),
+            "code_lengths": up(arrays["code_lengths"]),
+            "decode_table": up(decode_table(host.codebook, decode_table_bits)),
+        }
+        self._compressed_bytes = host.compressed_bytes()
+        s = _lib.DeviceStream()
+        s.h = host.header
+        for name, t in self._bufs.items():
+            setattr(s, name, t.data_ptr())
+        s.decode_table_bits = decode_table_bits
+        self._stream_struct = s
+
+    @property
+    def n_elements(self) -> int:
+        return int(self.host_header.n_elements)
+
+    @property
+    def header(self) -> _lib.Header:
+        return self.host_header
+
+    def compressed_bytes(self) -> int:
+        return self._compressed_bytes
+
+    def device_stream(self) -> _lib.DeviceStream:
+        return self._stream_struct
+
+    def _hip_stream(self, stream) -> ctypes.c_void_p:
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return ctypes.c_void_p(st.cuda_stream)
+
+    def decompress(self, out: Optional["torch.Tensor"] = None, stream=None) -> "torch.Tensor":  # noqa: F821
+        """Decode into out (a new bf16 tensor of the original shape by default),
+        enqueued on stream (torch's current stream by default)."""
+        import torch
+        if out is None:
+            out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
+        if out.dtype != torch.bfloat16 or out.numel() != self.n_elements or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bfloat16 tensor with the stream's element count")
+        lib = _lib.load()
+        _lib.check(lib.df11_decompress(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()),
+                                       self._hip_stream(stream)), "df11_decompress")
+        return out
+
+
+def compress(tensor: ArrayLike, shape: Optional[Sequence[int]] = None, device="cuda",
+             codebook: Optional[_lib.Codebook] = None,
+             decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS) -> DF11Tensor:
+    """Encode a BF16 tensor on the host and upload the stream to the GPU."""
+    if shape is None:
+        shape = tuple(tensor.shape)
+    host = encode(tensor, codebook=codebook)
+    return DF11Tensor(host, shape, device=device, decode_table_bits=decode_table_bits)
+
+
+def decompress(t: DF11Tensor, out=None, stream=None):
+    return t.decompress(out=out, stream=stream)
+
+
+class DF11Block:
+    """Every linear weight of one transformer block as a single DF11 stream
+    with a shared codebook, decompressed in one launch into one scratch buffer
+    ("Dekompresi per transformer block")."""
+
+    def __init__(self, tensor: DF11Tensor, views: List[Tuple[str, int, Tuple[int, ...]]]):
+        self.tensor = tensor
+        self.views = views
+
+    @property
+    def n_elements(self) -> int:
+        return self.tensor.n_elements
+
+    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+        import torch
+        t = self.tensor
+        if scratch is None:
+            scratch = torch.empty(t.n_elements, dtype=torch.bfloat16, device=t.device)
+        if scratch.dtype != torch.bfloat16 or not scratch.is_contiguous():
+            raise ValueError("scratch must be a contiguous bfloat16 tensor")
+        lib = _lib.load()
+        _lib.check(lib.df11_decompress_block(ctypes.byref(t.device_stream()), ctypes.c_void_p(scratch.data_ptr()),
+                                             scratch.numel(), t._hip_stream(stream)), "df11_decompress_block")
+        flat = scratch.reshape(-1)
+        return {name: flat[off:off + int(np.prod(shape))].view(shape) for name, off, shape in self.views}
+
+
+def compress_block(weights: Union[Dict[str, ArrayLike], List[Tuple[str, ArrayLike]]], device="cuda",
+                   decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS) -> DF11Block:
+    """Concatenate the block's weights row-major in the given order, build one
+    codebook from the summed histogram and encode them as one stream."""
+    items = list(weights.items()) if isinstance(weights, dict) else list(weights)
+    parts, views, off = [], [], 0
+    for name, w in items:
+        shape = tuple(int(s) for s in w.shape)
+        flat = _u16(w)
+        parts.append(flat)
+        views.append((name, off, shape))
+        off += flat.size
+    data = np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint16)
+    t = compress(data, shape=(data.size,), device=device, decode_table_bits=decode_table_bits)
+    return DF11Block(t, views)

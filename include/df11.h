@@ -1,0 +1,213 @@
+/*
+ * df11.h -- C ABI of the DF11 (DFloat11) codec for one AMD Instinct MI355X (gfx950).
+ *
+ * The method: "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan LLM
+ * menjadi 70% ukurannya" (GeekNews, id.news.hada.io topic 20542).  Section
+ * names below are that page's headings.
+ *
+ * A BF16 weight keeps its sign and 7-bit mantissa verbatim in one
+ * PackedSignMantissa byte, while its 8-bit exponent is Huffman-coded into the
+ * bit-packed EncodedExponent stream ("Format DFloat11").  Decoding walks a
+ * hierarchy of 256-entry LUTs cut from height-8 subtrees of the code tree, the
+ * unused exponent values 240..255 acting as pointers to lower LUTs, plus a
+ * 256-byte CodeLengths table ("Decoding berbasis LUT hierarkis").  Each GPU
+ * thread decodes the codes that start in its own n-byte segment, from a start
+ * bit stored in Gaps; each thread block's first output index is stored once
+ * ("Kernel GPU 2 tahap dan metadata bantu").
+ *
+ * Conventions for every function:
+ *  - Return value: DF11_OK (0) or a negative df11_status.  Nothing throws across
+ *    this ABI.  Validation runs before any write or launch; on failure no output
+ *    buffer is written and no work is enqueued.
+ *  - The caller owns every buffer, host and device.  The library never
+ *    allocates, frees or synchronises device memory, and keeps no global state;
+ *    host functions are reentrant.
+ *  - Integers in buffers are little-endian; bit streams are MSB-first (bit p of a
+ *    stream is bit 7 - p%8 of byte p/8).
+ *  - "host" arguments are host pointers, "device" arguments are device pointers
+ *    (hipMalloc'd or equivalent) on the current HIP device.
+ */
+#ifndef DF11_H
+#define DF11_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum df11_status {
+    DF11_OK = 0,
+    DF11_E_INVALID_ARG = -1,        /* null pointer, unsupported layout, bad size argument */
+    DF11_E_RESERVED_EXPONENT = -2,  /* input has exponent >= 240 (Inf/NaN or |x| >= 2^113) */
+    DF11_E_CODE_TOO_LONG = -3,      /* a Huffman code would exceed 32 bits */
+    DF11_E_TOO_MANY_LUTS = -4,      /* the code tree needs more than 16 lower LUTs */
+    DF11_E_BUFFER_TOO_SMALL = -5,   /* a caller buffer is smaller than required */
+    DF11_E_BAD_STREAM = -6,         /* header fields or codebook are inconsistent */
+    DF11_E_TOO_LARGE = -7,          /* N >= 2^32 elements in one stream */
+    DF11_E_HIP = -8                 /* a HIP launch or query failed */
+} df11_status;
+
+/* Exponent values 240..255 are pointers inside the LUTs, never symbols. */
+#define DF11_FIRST_POINTER 240
+/* The root LUT plus one lower LUT per pointer value. */
+#define DF11_MAX_LUTS 17
+/* Longest code; Gaps hold 5-bit offsets in [0, 31]. */
+#define DF11_MAX_CODE_LEN 32
+
+/* The codebook shared by all tensors of one stream (host, plain data).
+ *   code_lengths[e]: Huffman code length of exponent e, 0 if unused
+ *                    (the page's CodeLengths table).
+ *   codes[e]:        canonical code of e, right-aligned in code_lengths[e] bits.
+ *   luts[i][x]:      LUT i indexed by the next 8 bits x.  A value v < 240 is an
+ *                    exponent whose code ends within those 8 bits; v >= 240
+ *                    points to LUT 256 - v for the following 8 bits.  LUT 0 is
+ *                    the root; lower LUTs are numbered by depth, then prefix.
+ *   n_luts:          number of LUTs in use (1..17).
+ *   max_len:         longest code length (1..32). */
+typedef struct df11_codebook {
+    uint8_t code_lengths[256];
+    uint32_t codes[256];
+    uint8_t luts[DF11_MAX_LUTS][256];
+    uint32_t n_luts;
+    uint32_t max_len;
+} df11_codebook;
+
+/* Launch-shape parameters stored in the stream.
+ *   bytes_per_thread (n):  EncodedExponent bytes per decoding thread; the
+ *                          page's experiments use 8.  The encoder accepts n >= 4;
+ *                          the GPU decoder supports n == 8.
+ *   threads_per_group (G): threads per output-position block, a multiple of 64;
+ *                          the GPU decoder supports G == 256. */
+typedef struct df11_layout {
+    uint32_t bytes_per_thread;
+    uint32_t threads_per_group;
+} df11_layout;
+
+/* Stream header (host).  Buffer sizes include zero padding:
+ *   enc_bytes     = round_up(n_threads * n, 16) + 16
+ *   sm_bytes      = round_up(n_elements, 64)
+ *   gaps_bytes    = 4 * (ceil(5 * n_threads / 32) + 1)
+ *   out_pos_bytes = 4 * (n_groups + 1)
+ * n_threads = ceil(total_bits / (8 n)), n_groups = ceil(n_threads / G).
+ * max_group_elems is the largest out_pos[g+1] - out_pos[g]; df11_plan leaves it
+ * at its upper bound G * 8n, df11_encode sets the exact value. */
+typedef struct df11_header {
+    uint64_t n_elements;
+    uint64_t total_bits;
+    uint32_t bytes_per_thread;
+    uint32_t threads_per_group;
+    uint64_t n_threads;
+    uint64_t n_groups;
+    uint32_t n_luts;
+    uint32_t max_len;
+    uint64_t enc_bytes;
+    uint64_t sm_bytes;
+    uint64_t gaps_bytes;
+    uint64_t out_pos_bytes;
+    uint32_t max_group_elems;
+    uint32_t reserved;
+} df11_header;
+
+/* A stream resident in device memory (the struct itself is host memory).
+ *   enc          device, h.enc_bytes     EncodedExponent, zero-padded
+ *   sm           device, h.sm_bytes      PackedSignMantissa: sign in bit 7, mantissa in bits 0..6
+ *   gaps         device, h.gaps_bytes    5-bit MSB-first start offsets, one per thread
+ *   out_pos      device, n_groups + 1    first output index of each group; last entry N
+ *   luts         device, n_luts * 256    df11_codebook.luts rows 0..n_luts-1
+ *   code_lengths device, 256             df11_codebook.code_lengths
+ *   decode_table device, df11_decode_table_bytes(decode_table_bits)
+ *                                        built by df11_build_decode_table
+ *   decode_table_bits                    index width of decode_table (10..12) */
+typedef struct df11_device_stream {
+    df11_header h;
+    const uint8_t *enc;
+    const uint8_t *sm;
+    const uint8_t *gaps;
+    const uint32_t *out_pos;
+    const uint8_t *luts;
+    const uint8_t *code_lengths;
+    const void *decode_table;
+    uint32_t decode_table_bits;
+    uint32_t reserved;
+} df11_device_stream;
+
+/* Accumulate the 256-bin exponent histogram of n BF16 words (host).
+ * "Format DFloat11": the Huffman tree is built from the exponent distribution;
+ * call once per tensor to share one codebook across tensors.
+ * bf16: host, n uint16 BF16 bit patterns.  hist: host, 256 counters, accumulated
+ * (not cleared).  DF11_E_RESERVED_EXPONENT if any exponent is >= 240
+ * ("Decoding berbasis LUT hierarkis": those values are reused as pointers);
+ * hist is then left unchanged. */
+int df11_histogram(const uint16_t *bf16, uint64_t n, uint64_t hist[256]);
+
+/* Build the codebook from a histogram (host): Huffman code lengths (ties broken
+ * by (weight, id) with leaf id = exponent, merged node id = 256 + merge index),
+ * canonical codes, CodeLengths and the hierarchical LUTs ("Format DFloat11",
+ * "Decoding berbasis LUT hierarkis").  With fewer than two used exponents the
+ * smallest unused exponents below 240 are added with weight 0.
+ * Errors: DF11_E_RESERVED_EXPONENT (hist[e] > 0 for e >= 240),
+ * DF11_E_CODE_TOO_LONG, DF11_E_TOO_MANY_LUTS.  cb is written only on success. */
+int df11_build_codebook(const uint64_t hist[256], df11_codebook *cb);
+
+/* Exact buffer sizes for n elements whose exponent histogram is hist (host).
+ * hist must be the histogram of exactly the data that df11_encode will see.
+ * Fills every header field; max_group_elems is an upper bound until encode. */
+int df11_plan(const df11_codebook *cb, const uint64_t hist[256], uint64_t n, const df11_layout *lay,
+              df11_header *h);
+
+/* Encode n BF16 words (host) into caller buffers sized by df11_plan:
+ * enc (h->enc_bytes), sm (h->sm_bytes), gaps (h->gaps_bytes), out_pos
+ * (h->n_groups + 1 entries).  h must come from df11_plan for this data; on
+ * success it is completed (total_bits, max_group_elems).  Every byte of the
+ * buffers is written, padding included.
+ * "Kernel GPU 2 tahap dan metadata bantu": gap_t is the bit offset of the first
+ * code starting at or after bit 8 n t (the end of the stream counts as a code
+ * start); out_pos[g] counts the codes that start before thread g G's segment.
+ * Errors: DF11_E_RESERVED_EXPONENT, DF11_E_INVALID_ARG (an exponent without a
+ * code, or h does not match the data), DF11_E_TOO_LARGE. */
+int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const df11_layout *lay,
+                df11_header *h, uint8_t *enc, uint8_t *sm, uint8_t *gaps, uint32_t *out_pos);
+
+/* Size in bytes of the decode table for index width bits (10..12), 0 if unsupported. */
+uint64_t df11_decode_table_bytes(uint32_t bits);
+
+/* Build the GPU decoder's first-level table from the codebook (host).
+ * The table is derived data, not part of the compressed format: for every
+ * bits-wide window it lists the complete codes at the start of the window
+ * (up to six exponents, their start offsets and their total length) so one LDS
+ * lookup resolves several short codes; windows whose first code is longer than
+ * the index width fall back to the page's LUT hierarchy.
+ * table: host, df11_decode_table_bytes(bits) bytes. */
+int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table, uint64_t table_bytes);
+
+/* Decompress a device-resident stream into out (device, h.n_elements uint16,
+ * not aliasing any input), enqueued on hip_stream (a hipStream_t; NULL is the
+ * null stream).  Returns after the launch; buffers must stay alive until the
+ * stream's work completes.  Every element of out is overwritten with the
+ * original BF16 bits ("Kernel GPU 2 tahap dan metadata bantu": per-thread
+ * count, block prefix sum, re-decode into an LDS write buffer, coalesced
+ * write).  A stream whose header is valid but whose payload is corrupt cannot
+ * make the kernel access memory out of bounds; its output is unspecified.
+ * Errors: DF11_E_INVALID_ARG (null pointers, unsupported n, G or
+ * decode_table_bits), DF11_E_BAD_STREAM (header sizes inconsistent),
+ * DF11_E_HIP (launch failed). */
+int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream);
+
+/* Decompress the stream of a whole transformer block -- every linear weight of
+ * the block encoded as one stream with a shared codebook -- into one scratch
+ * buffer just before the block's forward pass ("Dekompresi per transformer
+ * block").  scratch: device, scratch_elems uint16; views into it (element
+ * offset, shape) are kept by the caller.  Same kernel and errors as
+ * df11_decompress, plus DF11_E_BUFFER_TOO_SMALL if scratch_elems < N. */
+int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64_t scratch_elems,
+                          void *hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char *df11_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DF11_H */

@@ -1,0 +1,158 @@
+"""GPU parity: the gfx950 decoder through the C ABI against the original BF16
+bits (the exact result, "identik bit demi bit") and against the oracle.
+
+Method: GeekNews, "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan
+LLM menjadi 70% ukurannya", sections "Kernel GPU 2 tahap dan metadata bantu"
+and "Dekompresi per transformer block".
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_decoding_df11_amd import df11, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    return torch
+
+
+def _note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _to_u16(t):
+    import torch
+    return t.detach().reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _gpu_decode(torch, w, bits=12, shape=None, fill=0x5A5A):
+    t = df11.compress(w, shape=shape or (w.size,), decode_table_bits=bits)
+    out = torch.full(t.shape, fill, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    t.decompress(out=out)
+    torch.cuda.synchronize()
+    return _to_u16(out), t
+
+
+def _fib(n):
+    f = [1, 1]
+    while len(f) < n:
+        f.append(f[-1] + f[-2])
+    return f[:n]
+
+
+def _case(kind, size, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return workloads.f32_to_bf16_bits(rng.standard_normal(size) * 0.02)
+    if kind == "student_t":
+        return workloads.f32_to_bf16_bits(rng.standard_t(5, size) * 0.015)
+    if kind == "uniform_bits":
+        w = rng.integers(0, 65536, 2 * size + 16).astype(np.uint16)
+        return w[((w >> 7) & 0xFF) < 240][:size]
+    if kind == "zeros":
+        return np.zeros(size, np.uint16)
+    if kind == "fib_chain":  # codes up to 29 bits, 4 LUT levels
+        p = np.array(_fib(30)[::-1], np.float64)
+        e = rng.choice(np.arange(90, 120), size, p=p / p.sum())
+        return workloads.f32_to_bf16_bits(np.ldexp(1.0 + rng.integers(0, 128, size) / 128.0, e - 127)
+                                          * rng.choice([-1.0, 1.0], size))
+    if kind == "stress_tuned":  # a 1-bit code and 28+ bit codes
+        return workloads.gen_stress(seed=seed, n=size)
+    if kind == "stress_literal":  # 8 LUTs
+        return workloads.gen_stress(seed=seed, n=size, kind="literal")
+    raise ValueError(kind)
+
+
+SMALL_CASES = [(k, n) for k in ("normal", "student_t", "uniform_bits", "zeros", "fib_chain", "stress_tuned",
+                                "stress_literal")
+               for n in (1, 2, 7, 64, 1000, 6403, 12345, 100003, (1 << 20) + 17)]
+
+
+@pytest.mark.parametrize("kind,size", SMALL_CASES)
+def test_small_cases_bitexact(torch_cuda, kind, size):
+    w = _case(kind, size, seed=size % 97)
+    _note(f"small kind={kind} size={size}")
+    s = oracle.encode(w)
+    ref = oracle.decode_treewalk(s)
+    assert np.array_equal(ref, w)
+    got, t = _gpu_decode(torch_cuda, w)
+    assert np.array_equal(got, w), f"first mismatch at {int(np.argmax(got != w))}"
+
+
+@pytest.mark.parametrize("bits", [10, 11, 12])
+@pytest.mark.parametrize("kind", ["normal", "fib_chain", "stress_tuned", "uniform_bits"])
+def test_decode_table_widths_agree(torch_cuda, bits, kind):
+    w = _case(kind, 300001, seed=bits)
+    _note(f"widths kind={kind} bits={bits}")
+    got, _ = _gpu_decode(torch_cuda, w, bits=bits)
+    assert np.array_equal(got, w)
+
+
+@pytest.mark.parametrize("name", ["single_1024x1024", "proj_4096x4096_outliers", "mlp_14336x4096_t5"])
+def test_workload_parity(torch_cuda, workload, name):
+    w = workload(name)
+    _note(f"workload {name} n={w.size}")
+    got, t = _gpu_decode(torch_cuda, w)
+    assert np.array_equal(got, w)
+    if w.size <= (1 << 24):
+        s = oracle.encode(w)
+        assert np.array_equal(oracle.decode_treewalk(s), got)
+
+
+def test_block_workload_full_size(torch_cuda):
+    """The Llama-3-8B-shaped block as one stream with a shared codebook,
+    decoded in one launch into one scratch buffer; sampled groups checked
+    against the oracle's own encode and tree-walk decode."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block()
+    _note(f"block n={flat.size}")
+    blk = df11.compress_block([(name, flat[off:off + r * c].reshape(r, c)) for name, off, (r, c) in views])
+    scratch = torch.empty(flat.size + 1000, dtype=torch.bfloat16, device="cuda")
+    out = blk.decompress(scratch=scratch)
+    torch.cuda.synchronize()
+    got = _to_u16(scratch[: flat.size])
+    assert np.array_equal(got, flat)
+    for name, off, (r, c) in views:
+        assert tuple(out[name].shape) == (r, c)
+        assert out[name].data_ptr() == scratch.data_ptr() + 2 * off
+    s = oracle.encode(flat)
+    rng = np.random.default_rng(7)
+    ref = np.zeros_like(flat)
+    for g in sorted(set(rng.integers(0, s["n_groups"], 200).tolist()) | {0, s["n_groups"] - 1}):
+        oracle.decode_groups(s, g, g + 1, ref)
+        lo, hi = int(s["out_pos"][g]), int(s["out_pos"][g + 1])
+        assert np.array_equal(ref[lo:hi], got[lo:hi]), g
+
+
+def test_stress_workload_full_size(torch_cuda):
+    w = workloads.gen_stress()
+    _note(f"stress n={w.size}")
+    got, t = _gpu_decode(torch_cuda, w)
+    assert np.array_equal(got, w)
+    assert t.header.max_len >= 28
+
+
+def test_empty_and_repeat_and_side_stream(torch_cuda):
+    torch = torch_cuda
+    t = df11.compress(np.zeros(0, np.uint16), shape=(0,))
+    out = t.decompress()
+    assert out.numel() == 0
+    w = _case("normal", 77777, 3)
+    t = df11.compress(w, shape=(w.size,))
+    side = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            outs.append(t.decompress(stream=side))
+    side.synchronize()
+    for o in outs:
+        assert np.array_equal(_to_u16(o), w)

@@ -1,0 +1,268 @@
+"""Host side of libdf11.so against the oracle, and the C ABI surface.
+
+These run without a GPU: the encoder and codebook builder are host code, and
+df11_decompress validates its arguments before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_decoding_df11_amd import _lib, df11, workloads
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libdf11.so not built")
+    return _lib.load()
+
+
+def _assert_same_stream(host, ref):
+    cb = df11.codebook_arrays(host.codebook)
+    assert np.array_equal(cb["code_lengths"], ref["code_lengths"])
+    assert np.array_equal(cb["codes"], ref["codes"])
+    assert np.array_equal(cb["luts"], ref["luts"])
+    assert cb["n_luts"] == ref["n_luts"] and cb["max_len"] == ref["max_len"]
+    for k in ("enc", "sm", "gaps", "out_pos"):
+        assert np.array_equal(getattr(host, k), ref[k]), k
+    h = host.header_dict()
+    for k in ("n_threads", "n_groups", "enc_bytes", "sm_bytes", "gaps_bytes", "total_bits", "n_elements",
+              "max_group_elems"):
+        assert h[k] == ref[k], k
+    assert h["out_pos_bytes"] == 4 * (ref["n_groups"] + 1)
+
+
+def test_header_exports_match_library():
+    lib = _lib_or_skip()
+    with open(os.path.join(REPO, "include", "df11.h")) as f:
+        text = f.read()
+    declared = sorted(set(re.findall(r"\b(df11_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.df11_status_str(-3) == b"DF11_E_CODE_TOO_LONG"
+    assert lib.df11_status_str(0) == b"DF11_OK"
+
+
+def test_header_structs_match_binding_sizes():
+    # the binding's structs mirror the header: check sizes/offsets with a tiny C probe compiled by gcc
+    import subprocess
+    import tempfile
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "df11.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(df11_codebook), sizeof(df11_layout), sizeof(df11_header),
+         sizeof(df11_device_stream), offsetof(df11_device_stream, enc), offsetof(df11_device_stream, decode_table_bits),
+         offsetof(df11_header, max_group_elems));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "probe.c")
+        exe = os.path.join(d, "probe")
+        with open(c, "w") as f:
+            f.write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(REPO, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(_lib.Codebook), ctypes.sizeof(_lib.Layout), ctypes.sizeof(_lib.Header),
+            ctypes.sizeof(_lib.DeviceStream), _lib.DeviceStream.enc.offset, _lib.DeviceStream.decode_table_bits.offset,
+            _lib.Header.max_group_elems.offset]
+    assert got == want
+
+
+@pytest.mark.parametrize("name", ["single_1024x1024", "proj_4096x4096_outliers"])
+def test_library_encoder_matches_oracle_bytes(workload, name):
+    _lib_or_skip()
+    w = workload(name)
+    _assert_same_stream(df11.encode(w), oracle.encode(w))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_library_encoder_matches_oracle_random(seed):
+    _lib_or_skip()
+    rng = np.random.default_rng(500 + seed)
+    size = int(rng.choice([0, 1, 2, 3, 63, 64, 65, 1000, 4097, 33333]))
+    n = int(rng.choice([4, 5, 8, 12, 16]))
+    G = int(rng.choice([64, 128, 256]))
+    kind = seed % 4
+    if kind == 0:
+        w = workloads.f32_to_bf16_bits(rng.standard_normal(size) * 0.02)
+    elif kind == 1:
+        w = rng.integers(0, 65536, size * 2).astype(np.uint16)
+        w = w[((w >> 7) & 0xFF) < 240][:size]
+    elif kind == 2:
+        w = np.full(size, 0x3F80 if seed % 2 else 0x0000, np.uint16)
+    else:
+        p = np.array([2.0 ** -min(k, 30) for k in range(1, 32)])
+        e = rng.choice(np.arange(100, 131), size, p=p / p.sum())
+        w = workloads.f32_to_bf16_bits(np.ldexp(1.0, e - 127))
+    _assert_same_stream(df11.encode(w, bytes_per_thread=n, threads_per_group=G), oracle.encode(w, n=n, G=G))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_library_codebook_matches_oracle_on_random_histograms(seed):
+    _lib_or_skip()
+    rng = np.random.default_rng(seed)
+    hist = np.zeros(256, np.uint64)
+    k = int(rng.integers(1, 240))
+    syms = rng.choice(240, k, replace=False)
+    style = seed % 3
+    if style == 0:
+        hist[syms] = rng.integers(1, 1000, k)
+    elif style == 1:
+        hist[syms] = np.round(1e12 * rng.power(0.2, k) ** 8).astype(np.uint64) + 1
+    else:
+        hist[syms] = rng.zipf(1.3, k).astype(np.uint64)
+    try:
+        ref = oracle.codebook(hist)
+    except oracle.OracleError as e:
+        with pytest.raises(_lib.Df11Error) as ei:
+            df11.build_codebook(hist)
+        assert ei.value.status == e.code
+        return
+    cb = df11.codebook_arrays(df11.build_codebook(hist))
+    for key in ("code_lengths", "codes", "luts", "n_luts", "max_len"):
+        assert np.array_equal(cb[key], ref[key]), key
+
+
+def _fib(n):
+    f = [1, 1]
+    while len(f) < n:
+        f.append(f[-1] + f[-2])
+    return f[:n]
+
+
+def test_library_error_paths():
+    _lib_or_skip()
+    # reserved exponent
+    with pytest.raises(_lib.Df11Error) as ei:
+        df11.histogram(np.array([0x3F80, 0x7F80], np.uint16))
+    assert ei.value.status == -2
+    # code longer than 32 bits
+    hist = np.zeros(256, np.uint64)
+    hist[60:94] = _fib(34)
+    with pytest.raises(_lib.Df11Error) as ei:
+        df11.build_codebook(hist)
+    assert ei.value.status == -3
+    # more than 16 lower LUTs (17 internal nodes at depth 8)
+    hist = np.zeros(256, np.uint64)
+    hist[:240] = [4] * 33 + [2] * 173 + [1] * 34
+    with pytest.raises(_lib.Df11Error) as ei:
+        df11.build_codebook(hist)
+    assert ei.value.status == -4
+    # bad layouts
+    w = np.array([0x3F80] * 10, np.uint16)
+    for n, G in ((3, 256), (8, 100), (8, 0)):
+        with pytest.raises(_lib.Df11Error) as ei:
+            df11.encode(w, bytes_per_thread=n, threads_per_group=G)
+        assert ei.value.status == -1
+    # an exponent missing from the codebook
+    cb = df11.build_codebook(df11.histogram(np.array([0x3F80, 0x3F00], np.uint16)))
+    with pytest.raises(_lib.Df11Error) as ei:
+        df11.encode(np.array([0x4000], np.uint16), codebook=cb)
+    assert ei.value.status == -1
+    # decode table sizes
+    lib = _lib.load()
+    assert lib.df11_decode_table_bytes(9) == 0 and lib.df11_decode_table_bytes(13) == 0
+    assert lib.df11_decode_table_bytes(12) == 8 << 12
+    buf = np.zeros(10, np.uint32)
+    assert lib.df11_build_decode_table(ctypes.byref(cb), 12, buf.ctypes.data_as(ctypes.c_void_p), 40) == -5
+
+
+def _fake_device_stream(host):
+    """A device-stream struct whose pointers are never dereferenced (validation only)."""
+    s = _lib.DeviceStream()
+    s.h = host.header
+    addr = 1 << 40
+    for name in ("enc", "sm", "gaps", "out_pos", "luts", "code_lengths", "decode_table"):
+        setattr(s, name, addr)
+        addr += 1 << 32
+    s.decode_table_bits = 12
+    return s
+
+
+def test_decompress_validation_runs_before_any_launch():
+    lib = _lib_or_skip()
+    host = df11.encode(workloads.gen_single_matrix(rows=64, cols=64))
+    out = ctypes.c_void_p(1 << 48)
+    # null stream struct
+    assert lib.df11_decompress(None, out, None) == -1
+    s = _fake_device_stream(host)
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.bytes_per_thread = 4
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.enc_bytes += 16
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -6
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.n_luts = 18
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -6
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.decode_table_bits = 9
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.sm = (1 << 40) + 8  # misaligned
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.n_elements = 1 << 32
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -7
+    # output aliasing an input
+    assert lib.df11_decompress(ctypes.byref(s), ctypes.c_void_p(s.sm), None) == -1
+    # misaligned output
+    assert lib.df11_decompress(ctypes.byref(s), ctypes.c_void_p((1 << 48) + 2), None) == -1
+    # scratch too small for the block entry point
+    assert lib.df11_decompress_block(ctypes.byref(s), out, host.n_elements - 1, None) == -5
+    # an empty stream is a valid no-op that launches nothing
+    empty = df11.encode(np.zeros(0, np.uint16))
+    es = _lib.DeviceStream()
+    es.h = empty.header
+    assert lib.df11_decompress(ctypes.byref(es), None, None) == 0
+
+
+def _greedy_window(lens, codes, x, bits, max_syms):
+    """The complete codes at the start of a bits-wide window (brute force over the code table)."""
+    syms, starts, used = [], [], 0
+    while len(syms) < max_syms:
+        found = None
+        for s in range(256):
+            l = int(lens[s])
+            if l and used + l <= bits and ((x >> (bits - used - l)) & ((1 << l) - 1)) == int(codes[s]):
+                found = (s, l)
+                break
+        if found is None:
+            break
+        syms.append(found[0])
+        starts.append(used)
+        used += found[1]
+    return syms, starts, used
+
+
+@pytest.mark.parametrize("bits", [10, 12])
+@pytest.mark.parametrize("case", ["single_1024x1024", "stress"])
+def test_decode_table_matches_code_table(workload, bits, case):
+    _lib_or_skip()
+    w = workload("single_1024x1024") if case == "single_1024x1024" else workloads.gen_stress(n=1 << 20)
+    ref = oracle.codebook(oracle.histogram(w))
+    cb = df11.build_codebook(df11.histogram(w))
+    table = df11.decode_table(cb, bits)
+    lo, hi = table[: 1 << bits], table[1 << bits:]
+    rot = lambda e: ((e >> 1) | (e << 7)) & 0xFF
+    for x in range(1 << bits):
+        syms, starts, used = _greedy_window(ref["code_lengths"], ref["codes"], x, bits, 6)
+        h = int(hi[x])
+        if not syms:
+            assert h >> 16 == 0
+            assert (h & 0xFF) == ref["luts"][0][x >> (bits - 8)] >= 240
+            continue
+        assert h >> 28 == used
+        assert (h >> 16) & 0xFFF == sum(1 << s for s in starts)
+        got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [(h >> (8 * j)) & 0xFF for j in range(2)]
+        assert got[: len(syms)] == [rot(s) for s in syms]
