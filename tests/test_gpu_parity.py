@@ -55,9 +55,10 @@ def _case(kind, size, seed):
         return workloads.f32_to_bf16_bits(rng.standard_normal(size) * 0.02)
     if kind == "student_t":
         return workloads.f32_to_bf16_bits(rng.standard_t(5, size) * 0.015)
-    if kind == "uniform_bits":
-        w = rng.integers(0, 65536, 2 * size + 16).astype(np.uint16)
-        return w[((w >> 7) & 0xFF) < 240][:size]
+    if kind == "uniform_bits":  # flat: uniform sign/mantissa, exponents uniform over 60 values
+        e = rng.integers(90, 150, size)
+        return workloads.f32_to_bf16_bits(np.ldexp(1.0 + rng.integers(0, 128, size) / 128.0, e - 127)
+                                          * rng.choice([-1.0, 1.0], size))
     if kind == "zeros":
         return np.zeros(size, np.uint16)
     if kind == "fib_chain":  # codes up to 29 bits, 4 LUT levels
