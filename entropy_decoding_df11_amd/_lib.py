@@ -91,7 +91,7 @@ class DeviceStream(ctypes.Structure):
         ("code_lengths", ctypes.c_void_p),
         ("decode_table", ctypes.c_void_p),
         ("decode_table_bits", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("groups_per_workgroup", ctypes.c_uint32),
     ]
 
 

@@ -46,6 +46,7 @@ constexpr uint32_t kWaveSize = 64;
 constexpr uint32_t kWaves = kThreadsPerGroup / kWaveSize;
 constexpr uint32_t kSegBits = 8 * kBytesPerThread;
 constexpr int kPrefetchChunks = 4;  // 8-element sign/mantissa chunks held in registers per thread
+constexpr uint32_t kDefaultGroupsPerWorkgroup = 2;
 
 struct DecodeArgs {
     const uint8_t *enc;
@@ -61,21 +62,13 @@ struct DecodeArgs {
     uint32_t n_threads;
     uint32_t n_groups;
     uint32_t n_luts;
-    uint32_t ebuf_cap;  // bytes of the LDS exponent buffer, a multiple of 16
+    uint32_t ebuf_cap;       // bytes of the LDS exponent buffer, a multiple of 16
+    uint32_t last_seg_bits;  // payload bits in the last thread's segment (1..64)
+    uint32_t sm_chunks;      // 8-byte chunks in the PackedSignMantissa buffer
     uint32_t pad;
 };
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
-
-// Bits [p, p + 32) of the thread's 96-bit window, p < 64.  v0..v2 hold the
-// window shifted right by one bit, so the funnel shift amount 31 - p (taken
-// mod 32 by v_alignbit) stays in range for every p, including p = 0 and 32.
-__device__ __forceinline__ uint32_t window_bits(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t p) {
-    const bool low = p < 32;
-    const uint32_t x = low ? v0 : v1;
-    const uint32_t y = low ? v1 : v2;
-    return __builtin_amdgcn_alignbit(x, y, ~p);
-}
 
 // Continue a code longer than the first-level window through the LUT
 // hierarchy.  ptr is the root LUT's pointer value for the window's first byte.
@@ -128,11 +121,35 @@ __device__ __forceinline__ uint4 merge8(uint64_t sm8, uint64_t r8) {
     return o;
 }
 
-// Store chunk c (elements 8c .. 8c+7) restricted to [base, end).
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+using LdsU8 = __attribute__((address_space(3))) uint8_t;
+using LdsU32 = __attribute__((address_space(3))) uint32_t;
+
+// 32-bit LDS offset of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LdsU8 *)p));
+}
+
+// OR up to 5 bytes (lo, then the low byte of hi8; higher bytes zero) into LDS
+// at byte offset off.  LDS stores that are not naturally aligned are several
+// times slower on gfx950, so the bytes are shifted into the two aligned dwords
+// they span and combined with aligned atomic ORs; bytes that are zero leave
+// their neighbours untouched.
+__device__ __forceinline__ void lds_or5(uint32_t off, uint32_t lo, uint32_t hi8) {
+    const uint64_t x = ((static_cast<uint64_t>(hi8) << 32) | lo) << ((off & 3u) * 8u);
+    LdsU32 *d = (LdsU32 *)(uintptr_t)(off & ~3u);
+    __hip_atomic_fetch_or(d, static_cast<uint32_t>(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(d + 1, static_cast<uint32_t>(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Store chunk c (elements 8c .. 8c+7) restricted to [base, end).  Whole chunks
+// are written with one 16-byte store that bypasses cache allocation: the BF16
+// output is written once and read later by another kernel.
 __device__ __forceinline__ void store_chunk(uint16_t *out, uint32_t c, uint4 v, uint32_t base, uint32_t end) {
     const uint32_t first = 8u * c;
     if (first >= base && first + 8u <= end) {
-        *reinterpret_cast<uint4 *>(out + first) = v;
+        u32x4 x = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(out + first));
     } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -143,88 +160,204 @@ __device__ __forceinline__ void store_chunk(uint16_t *out, uint32_t c, uint4 v, 
     }
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreadsPerGroup) void df11_decode_kernel(DecodeArgs a) {
-    // Dynamic LDS: lo table | hi table | LUTs | CodeLengths | exponent buffer | wave sums.
-    // The tables start at LDS address 0 so lookups need no base add.
+// out_pos is read-only for the whole kernel and indexed by a wave-uniform
+// group number: reading it through the constant address space gives scalar
+// loads, which are counted apart from the vector-memory operations.
+using ConstU32 = const __attribute__((address_space(4))) uint32_t;
+
+__device__ __forceinline__ uint32_t out_pos_at(const DecodeArgs &a, uint32_t g) {
+    return ((const ConstU32 *)a.out_pos)[min(g, a.n_groups)];
+}
+
+// Number of 8-element chunks that hold the outputs [base, end).
+__device__ __forceinline__ uint32_t group_chunks(uint32_t base, uint32_t end) {
+    return end > base ? ((end + 7u) >> 3) - (base >> 3) : 0u;
+}
+
+// Per-thread inputs of one group, loaded one loop iteration before they are
+// used.  On gfx9 one counter tracks loads and stores in issue order, so a
+// group's inputs are loaded before the previous group's stores are issued:
+// waiting for them then does not wait for those stores.
+struct GroupLoad {
+    uint32_t e0, e1, e2;           // the thread's EncodedExponent words (bytes 8t .. 8t+11)
+    uint32_t g0, g1;               // the two Gaps words that hold its 5 bits
+    uint64_t sm[kPrefetchChunks];  // sign/mantissa chunks ltid + 256 j of the group
+};
+
+// Issues the same loads for every group (addresses clamped into the buffers,
+// values of out-of-range items unused) so that the number of operations in
+// flight is the same on every path.
+__device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g, uint32_t ltid, uint32_t base,
+                                                uint32_t end) {
+    GroupLoad r;
+    const uint32_t t = min(g * kThreadsPerGroup + ltid, a.n_threads - 1u);
+    const uint32_t *e32 = reinterpret_cast<const uint32_t *>(a.enc + 8ull * t);
+    r.e0 = e32[0];
+    r.e1 = e32[1];
+    r.e2 = e32[2];
+    const uint64_t gbit = 5ull * t;
+    const uint32_t *g32 = reinterpret_cast<const uint32_t *>(a.gaps) + (gbit >> 5);
+    r.g0 = g32[0];
+    r.g1 = g32[1];
+    const uint32_t c0 = base >> 3;
+    const uint32_t nch = group_chunks(base, end);
+#pragma unroll
+    for (int j = 0; j < kPrefetchChunks; ++j) {
+        const uint32_t k = ltid + j * kThreadsPerGroup;
+        const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
+        r.sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
+    }
+    return r;
+}
+
+// Bits [p, p + 32) of the thread's 96-bit window for p < 64, with the
+// position passed as acc whose low byte is 255 - p.  v0..v2 hold the window
+// shifted right by one bit, so the funnel shift amount 31 - p (taken mod 32
+// by v_alignbit, which reads only the low 5 bits of acc) stays in range for
+// every p, including p = 0 and 32.  p < 32 exactly when the low byte is >= 224.
+__device__ __forceinline__ uint32_t window_at(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t acc) {
+    const bool low = (acc & 0xFFu) >= 0xE0u;
+    return __builtin_amdgcn_alignbit(low ? v0 : v1, low ? v1 : v2, acc);
+}
+
+// Merge one decoded group's exponents with its sign/mantissa bytes and store
+// BF16.  LDS byte 8k + i of the group's buffer holds element 8 (base/8 + k) + i;
+// every chunk read is zeroed again for the next group that uses the buffer.
+__device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, const uint64_t (&sm)[kPrefetchChunks],
+                                            uint32_t base, uint32_t end, uint32_t ltid) {
+    const uint32_t c0 = base >> 3;
+    const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
+#pragma unroll
+    for (int j = 0; j < kPrefetchChunks; ++j) {
+        const uint32_t k = ltid + j * kThreadsPerGroup;
+        if (k < n_chunks) {
+            uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
+            const uint64_t r8 = *cell;
+            *cell = 0;
+            store_chunk(a.out, c0 + k, merge8(sm[j], r8), base, end);
+        }
+    }
+    for (uint32_t k = ltid + kPrefetchChunks * kThreadsPerGroup; k < n_chunks; k += kThreadsPerGroup) {
+        const uint64_t s8 = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k));
+        uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
+        const uint64_t r8 = *cell;
+        *cell = 0;
+        store_chunk(a.out, c0 + k, merge8(s8, r8), base, end);
+    }
+    // Codes past the group's last output reach at most 4 bytes into the next chunk.
+    if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+}
+
+// GPW groups of 256 threads share one workgroup (and one copy of the decode
+// tables in LDS).  Each workgroup owns a contiguous range of "super-groups" of
+// GPW consecutive groups.  Iteration s first merges and stores super-group
+// s - 1 (decoded in the previous iteration into the other half of a
+// double-buffered LDS exponent buffer), then issues the loads of super-group
+// s + 1, then decodes super-group s.  Every wait for loaded data therefore
+// comes a whole decode phase after the last stores were issued.
+template <int K, int GPW>
+__global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
+    // Static LDS: the first-level table (lo words | hi words | start masks) at a
+    // fixed address, so a lookup's address is its index times the entry size.
+    // Dynamic LDS: LUTs | CodeLengths | GPW x 2 exponent buffers | wave sums.
+    __shared__ __align__(16) uint32_t s_tab[(10u << K) / 4u];
     extern __shared__ __align__(16) uint8_t smem[];
-    uint32_t *s_lo = reinterpret_cast<uint32_t *>(smem);
-    uint32_t *s_hi = s_lo + (1u << K);
-    uint8_t *s_luts = smem + (8u << K);
+    const uint32_t *s_lo = s_tab;
+    const uint32_t *s_hi = s_tab + (1u << K);
+    const uint16_t *s_mask = reinterpret_cast<const uint16_t *>(s_tab + (2u << K));
+    uint8_t *s_luts = smem;
     uint8_t *s_clen = s_luts + a.n_luts * 256u;
-    uint8_t *s_ebuf = s_clen + 256u;
-    uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_ebuf + a.ebuf_cap);
     const uint32_t tid = threadIdx.x;
+    const uint32_t slot = __builtin_amdgcn_readfirstlane(tid / kThreadsPerGroup);
+    const uint32_t ltid = tid % kThreadsPerGroup;
     const uint32_t lane = tid & (kWaveSize - 1);
-    const uint32_t wave = tid / kWaveSize;
+    const uint32_t wave = ltid / kWaveSize;
+    uint8_t *s_ebuf2 = s_clen + 256u + slot * 2u * a.ebuf_cap;
+    uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * 2u * a.ebuf_cap) + slot * kWaves;
+
+    const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
+    const uint32_t s_begin = static_cast<uint32_t>(static_cast<uint64_t>(blockIdx.x) * n_super / gridDim.x);
+    const uint32_t s_end = static_cast<uint32_t>(static_cast<uint64_t>(blockIdx.x + 1) * n_super / gridDim.x);
+    if (s_begin >= s_end) return;  // whole workgroup
+
+    // Pipeline state: out_pos two super-groups ahead (scalar), thread inputs
+    // one ahead, sign/mantissa bytes of the group waiting to be merged.
+    const uint32_t g_first = s_begin * GPW + slot;
+    uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
+    uint32_t nx_base = out_pos_at(a, g_first + GPW), nx_end = out_pos_at(a, g_first + GPW + 1);
+    GroupLoad cur = load_group(a, g_first, ltid, cur_base, cur_end);
+    uint64_t prev_sm[kPrefetchChunks] = {};
+    uint32_t prev_base = 0, prev_end = 0;
 
     // Stage the first-level table, the LUT hierarchy and CodeLengths.
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(a.dtab);
-        uint4 *dst = reinterpret_cast<uint4 *>(smem);
-        for (uint32_t i = tid; i < (8u << K) / 16u; i += kThreadsPerGroup) dst[i] = src[i];
+        uint4 *dst = reinterpret_cast<uint4 *>(s_tab);
+        for (uint32_t i = tid; i < (10u << K) / 16u; i += kThreadsPerGroup * GPW) dst[i] = src[i];
         const uint32_t *l32 = reinterpret_cast<const uint32_t *>(a.luts);
         uint32_t *d32 = reinterpret_cast<uint32_t *>(s_luts);
-        for (uint32_t i = tid; i < a.n_luts * 64u; i += kThreadsPerGroup) d32[i] = l32[i];
+        for (uint32_t i = tid; i < a.n_luts * 64u; i += kThreadsPerGroup * GPW) d32[i] = l32[i];
         if (tid < 64) reinterpret_cast<uint32_t *>(s_clen)[tid] = reinterpret_cast<const uint32_t *>(a.code_lengths)[tid];
+        // Phase 2 ORs exponents into the buffers, so they start out zero (and
+        // the merge zeroes every chunk it consumes).
+        uint4 *z = reinterpret_cast<uint4 *>(s_clen + 256u);
+        for (uint32_t i = tid; i < GPW * 2u * a.ebuf_cap / 16u; i += kThreadsPerGroup * GPW)
+            z[i] = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
 
-    for (uint32_t g = blockIdx.x; g < a.n_groups; g += gridDim.x) {
-        const uint32_t t = g * kThreadsPerGroup + tid;
+    for (uint32_t s = s_begin; s < s_end; ++s) {
+        const uint32_t g = s * GPW + slot;
+        uint8_t *s_ebuf = s_ebuf2 + (s & 1u) * a.ebuf_cap;
 
-        // Output range of the group, clamped so a corrupt out_pos stays in bounds.
-        uint32_t end = min(a.out_pos[g + 1], a.n_elements);
-        uint32_t base = min(a.out_pos[g], end);
+        // 1. Merge and store the super-group decoded in the previous iteration.
+        if (s > s_begin) merge_group(a, s_ebuf2 + ((s - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
+
+        // 2. Loads of the next super-group.
+        const uint32_t nn_base = out_pos_at(a, g + 2 * GPW), nn_end = out_pos_at(a, g + 2 * GPW + 1);
+        const GroupLoad nx = load_group(a, g + GPW, ltid, nx_base, nx_end);
+
+        // 3. Decode this super-group.  Output range of the group, clamped so a
+        // corrupt out_pos stays in bounds.
+        const uint32_t end = min(cur_end, a.n_elements);
+        const uint32_t base = min(cur_base, end);
         const uint32_t lead = base & 7u;
-        const uint32_t c0 = base >> 3;
-        uint32_t n_chunks = end > base ? ((end + 7u) >> 3) - c0 : 0u;
-        n_chunks = min(n_chunks, a.ebuf_cap / 8u);
 
-        uint64_t smv[kPrefetchChunks];
-#pragma unroll
-        for (int j = 0; j < kPrefetchChunks; ++j) {
-            const uint32_t k = tid + j * kThreadsPerGroup;
-            smv[j] = k < n_chunks ? *reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k)) : 0ull;
-        }
-
-        uint32_t w0 = 0, w1 = 0, w2 = 0, gap = 0, seg_end = 0;
-        if (t < a.n_threads) {
-            const uint32_t *e32 = reinterpret_cast<const uint32_t *>(a.enc + 8ull * t);
-            w0 = bswap32(e32[0]);
-            w1 = bswap32(e32[1]);
-            w2 = bswap32(e32[2]);
+        const uint32_t t = g * kThreadsPerGroup + ltid;
+        uint32_t gap = 0, seg_end = 0;
+        if (g < a.n_groups && t < a.n_threads) {
             const uint64_t gbit = 5ull * t;
-            const uint32_t *g32 = reinterpret_cast<const uint32_t *>(a.gaps) + (gbit >> 5);
-            const uint64_t gw = (static_cast<uint64_t>(bswap32(g32[0])) << 32) | bswap32(g32[1]);
+            const uint64_t gw = (static_cast<uint64_t>(bswap32(cur.g0)) << 32) | bswap32(cur.g1);
             gap = static_cast<uint32_t>((gw << (gbit & 31)) >> 59);
-            const uint64_t rem = a.total_bits - static_cast<uint64_t>(kSegBits) * t;
-            seg_end = rem < kSegBits ? static_cast<uint32_t>(rem) : kSegBits;
+            seg_end = t + 1 < a.n_threads ? kSegBits : a.last_seg_bits;
         }
+        const uint32_t w0 = bswap32(cur.e0), w1 = bswap32(cur.e1), w2 = bswap32(cur.e2);
         const uint32_t v0 = w0 >> 1;
         const uint32_t v1 = __builtin_amdgcn_alignbit(w0, w1, 1);
         const uint32_t v2 = __builtin_amdgcn_alignbit(w1, w2, 1);
 
-        // Phase 1: count the codes that start in [gap, seg_end).
-        uint32_t cnt = 0, last_p = 0, last_mask = 0;
-        for (uint32_t p = gap; p < seg_end;) {
-            const uint32_t win = window_bits(v0, v1, v2, p);
-            const uint32_t hi = s_hi[win >> (32 - K)];
-            uint32_t nb = hi >> 28;
-            uint32_t mask = (hi >> 16) & 0xFFFu;
-            if (nb == 0) {
+        // Phase 1: count the codes that start in [gap, seg_end).  acc holds
+        // (count << 8) | (255 - p); one table increment adds m codes and nb bits.
+        const uint32_t n_end = 255u - seg_end;
+        uint32_t acc = 255u - gap, last = acc;
+        while ((acc & 0xFFu) > n_end) {
+            const uint32_t win = window_at(v0, v1, v2, acc);
+            uint32_t inc = s_hi[win >> (32 - K)] >> 16;
+            if (inc == 0) {  // first code longer than the window
                 uint32_t len;
-                walk_luts(win, hi & 0xFFu, s_luts, s_clen, a.n_luts, len);
-                nb = len;
-                mask = 1;
+                walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
+                inc = 256u - len;
             }
-            last_p = p;
-            last_mask = mask;
-            cnt += __popc(mask);
-            p += nb;
+            last = acc;
+            acc += inc;
         }
-        // The last lookup may list codes that start at or after seg_end.
-        cnt -= __popc(last_mask >> min(seg_end - last_p, 31u));
+        uint32_t cnt = acc >> 8;
+        if (cnt) {
+            // The last lookup may list codes that start at or after seg_end.
+            const uint32_t p_last = 255u - (last & 0xFFu);
+            const uint32_t mask = s_mask[window_at(v0, v1, v2, last) >> (32 - K)];
+            cnt -= __popc(mask >> min(seg_end - p_last, 31u));
+        }
 
         // Offsets within the group.
         const uint32_t incl = wave_inclusive_scan(cnt);
@@ -233,68 +366,43 @@ __global__ __launch_bounds__(kThreadsPerGroup) void df11_decode_kernel(DecodeArg
         uint32_t wave_off = 0;
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
-        uint32_t o = lead + wave_off + incl - cnt;
-        const uint32_t e_end = min(o + cnt, a.ebuf_cap);
+        const uint32_t o_start = lead + wave_off + incl - cnt;
+        const uint32_t o_end = min(o_start + cnt, a.ebuf_cap - 8u);
 
-        // Phase 2: decode again and write the (rotated) exponents into LDS.
-        for (uint32_t p = gap; o < e_end && p < seg_end;) {
-            const uint32_t win = window_bits(v0, v1, v2, p);
+        // Phase 2: decode again and OR the (rotated) exponents into the zeroed
+        // LDS buffer at their output positions.  acc2 holds
+        // (LDS address << 8) | (255 - p).  A thread's last lookup may list codes
+        // that start past its segment; those are the next thread's first codes,
+        // decoded at the same code boundaries, so they land on the next
+        // thread's first outputs with the same values (or, after the group's
+        // last output, in the chunk the merge zeroes).
+        const uint32_t ebase = lds_offset(s_ebuf);
+        for (uint32_t acc2 = ((ebase + o_start) << 8) | (255u - gap); acc2 < ((ebase + o_end) << 8);) {
+            const uint32_t win = window_at(v0, v1, v2, acc2);
             const uint32_t idx = win >> (32 - K);
             uint32_t lo = s_lo[idx];
             uint32_t hi = s_hi[idx];
-            uint32_t nb = hi >> 28;
-            uint32_t m = __popc((hi >> 16) & 0xFFFu);
-            if (nb == 0) {
+            if (hi < 0x10000u) {  // first code longer than the window
                 uint32_t len;
-                const uint32_t e = walk_luts(win, hi & 0xFFu, s_luts, s_clen, a.n_luts, len);
-                lo = df11::rotate_exponent(e);
-                hi = 0;
-                nb = len;
-                m = 1;
+                lo = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len));
+                hi = (256u - len) << 16;
             }
-            const uint64_t syms = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi & 0xFFFFu) << 32);
-            if (o + 8u <= e_end) {
-                __builtin_memcpy(s_ebuf + o, &syms, 8);
-            } else {
-                // Near the end of this thread's range: write exactly the bytes that belong to it.
-                const uint32_t k = min(m, e_end - o);
-                uint32_t q = o;
-                uint64_t rest = syms;
-                if (k & 4u) {
-                    const uint32_t v = static_cast<uint32_t>(rest);
-                    __builtin_memcpy(s_ebuf + q, &v, 4);
-                    q += 4;
-                    rest >>= 32;
-                }
-                if (k & 2u) {
-                    const uint16_t v = static_cast<uint16_t>(rest);
-                    __builtin_memcpy(s_ebuf + q, &v, 2);
-                    q += 2;
-                    rest >>= 16;
-                }
-                if (k & 1u) s_ebuf[q] = static_cast<uint8_t>(rest);
-            }
-            o += m;
-            p += nb;
+            lds_or5(acc2 >> 8, lo, hi & 0xFFu);
+            acc2 += hi >> 16;
         }
         __syncthreads();
 
-        // Merge and store.  LDS byte 8k + i holds element 8 (c0 + k) + i.
 #pragma unroll
-        for (int j = 0; j < kPrefetchChunks; ++j) {
-            const uint32_t k = tid + j * kThreadsPerGroup;
-            if (k < n_chunks) {
-                const uint64_t r8 = *reinterpret_cast<const uint64_t *>(s_ebuf + 8u * k);
-                store_chunk(a.out, c0 + k, merge8(smv[j], r8), base, end);
-            }
-        }
-        for (uint32_t k = tid + kPrefetchChunks * kThreadsPerGroup; k < n_chunks; k += kThreadsPerGroup) {
-            const uint64_t s8 = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k));
-            const uint64_t r8 = *reinterpret_cast<const uint64_t *>(s_ebuf + 8u * k);
-            store_chunk(a.out, c0 + k, merge8(s8, r8), base, end);
-        }
-        // The next group's scan barrier orders these LDS reads before its phase-2 writes.
+        for (int j = 0; j < kPrefetchChunks; ++j) prev_sm[j] = cur.sm[j];
+        prev_base = base;
+        prev_end = end;
+        cur = nx;
+        cur_base = nx_base;
+        cur_end = nx_end;
+        nx_base = nn_base;
+        nx_end = nn_end;
     }
+    merge_group(a, s_ebuf2 + ((s_end - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -313,6 +421,9 @@ int validate(const df11_device_stream *s) {
     if (h.n_elements >= (1ull << 32)) return DF11_E_TOO_LARGE;
     if (h.n_elements == 0) return h.total_bits == 0 ? DF11_OK : DF11_E_BAD_STREAM;
     if (df11_decode_table_bytes(s->decode_table_bits) == 0) return DF11_E_INVALID_ARG;
+    if (s->groups_per_workgroup != 0 && s->groups_per_workgroup != 1 && s->groups_per_workgroup != 2 &&
+        s->groups_per_workgroup != 4)
+        return DF11_E_INVALID_ARG;
     if (!s->enc || !s->sm || !s->gaps || !s->out_pos || !s->luts || !s->code_lengths || !s->decode_table)
         return DF11_E_INVALID_ARG;
     if (!aligned(s->enc, 16) || !aligned(s->sm, 16) || !aligned(s->gaps, 4) || !aligned(s->out_pos, 4) ||
@@ -332,23 +443,33 @@ int validate(const df11_device_stream *s) {
     return DF11_OK;
 }
 
-template <int K>
+template <int K, int GPW>
 int launch(const DecodeArgs &a, hipStream_t stream) {
-    const size_t lds = (8u << K) + a.n_luts * 256u + 256u + a.ebuf_cap + 4u * kWaves;
+    const size_t lds = a.n_luts * 256u + 256u + GPW * (2u * a.ebuf_cap + 4u * kWaves);  // beyond the static table
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return DF11_E_HIP;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, df11_decode_kernel<K>, kThreadsPerGroup, lds) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, df11_decode_kernel<K, GPW>, kThreadsPerGroup * GPW,
+                                                     lds) != hipSuccess ||
         per_cu < 1)
         return DF11_E_HIP;
+    const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
-    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(a.n_groups, resident));
+    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_super, resident));
     (void)hipGetLastError();
-    hipLaunchKernelGGL(df11_decode_kernel<K>, dim3(grid), dim3(kThreadsPerGroup), lds, stream, a);
+    hipLaunchKernelGGL((df11_decode_kernel<K, GPW>), dim3(grid), dim3(kThreadsPerGroup * GPW), lds, stream, a);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+}
+
+template <int K>
+int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream) {
+    switch (gpw) {
+    case 1: return launch<K, 1>(a, stream);
+    case 4: return launch<K, 4>(a, stream);
+    default: return launch<K, 2>(a, stream);
+    }
 }
 
 int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream) {
@@ -382,10 +503,13 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     // lead (< 8) + the group's elements, rounded up to whole 8-byte chunks, plus
     // slack for the 8-byte LDS writes.
     a.ebuf_cap = static_cast<uint32_t>(round_up(static_cast<uint64_t>(h.max_group_elems) + 16, 16));
+    a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
+    a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
+    const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
     switch (bits) {
-    case 10: return launch<10>(a, stream);
-    case 11: return launch<11>(a, stream);
-    case 12: return launch<12>(a, stream);
+    case 10: return launch_k<10>(a, gpw, stream);
+    case 11: return launch_k<11>(a, gpw, stream);
+    case 12: return launch_k<12>(a, gpw, stream);
     default: return DF11_E_INVALID_ARG;
     }
 }

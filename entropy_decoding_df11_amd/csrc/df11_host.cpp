@@ -324,7 +324,7 @@ int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const
 
 uint64_t df11_decode_table_bytes(uint32_t bits) {
     if (bits < df11::kDecodeTableMinBits || bits > df11::kDecodeTableMaxBits) return 0;
-    return 8ull << bits;
+    return 10ull << bits;  // lo and hi (4 bytes each) and mask (2 bytes) per entry
 }
 
 int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table, uint64_t table_bytes) {
@@ -350,6 +350,7 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
     const uint32_t size = 1u << bits;
     uint32_t *lo = static_cast<uint32_t *>(table);
     uint32_t *hi = lo + size;
+    uint16_t *mask_out = reinterpret_cast<uint16_t *>(hi + size);
     for (uint32_t x = 0; x < size; ++x) {
         uint32_t used = 0, mask = 0, m = 0;
         uint8_t syms[df11::kDecodeTableMaxSyms] = {0};
@@ -370,18 +371,14 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
             used += static_cast<uint32_t>(len);
         }
         uint32_t lo_word = 0, hi_word = 0;
-        if (m == 0) {
-            // First code longer than the window: record the root LUT entry
-            // (a pointer) for the hierarchical walk.
-            hi_word = cb->luts[0][x >> (bits - 8)];
-        } else {
-            for (uint32_t j = 0; j < 4 && j < m; ++j) lo_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * j);
-            for (uint32_t j = 4; j < m; ++j) hi_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * (j - 4));
-            hi_word |= mask << 16;
-            hi_word |= used << 28;
-        }
+        for (uint32_t j = 0; j < 4 && j < m; ++j)
+            lo_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * j);
+        for (uint32_t j = 4; j < m; ++j)
+            hi_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * (j - 4));
+        if (m) hi_word |= ((m << 8) - used) << 16;
         lo[x] = lo_word;
         hi[x] = hi_word;
+        mask_out[x] = static_cast<uint16_t>(m ? mask : 1u);
     }
     return DF11_OK;
 }

@@ -7,19 +7,23 @@
 namespace df11 {
 
 // First-level decode table: indexed by the next `bits` bits of the stream.
-// Entry x is two 32-bit words stored in two arrays (lo[x], then hi[x]):
-//   lo: up to four exponents (byte j = j-th complete code of the window)
-//   hi: bits 0..15  exponents 4 and 5,
-//       bits 16..27 start mask (bit j set: a listed code starts at offset j),
-//       bits 28..31 total length of the listed codes (0: the first code is
-//                   longer than the window; bits 0..7 then hold the root LUT's
-//                   pointer value for the window's first 8 bits).
-// Exponents are stored rotated right by one bit, (e >> 1) | ((e & 1) << 7), so
-// that the decoder's merge with the sign/mantissa byte is a single bitfield
-// insert per BF16 pair.
+// Entry x is stored in three arrays, lo[2^bits] and hi[2^bits] (uint32) and
+// mask[2^bits] (uint16):
+//   lo:   exponents 0..3 of the complete codes at the start of the window
+//         (byte j = j-th code; unused bytes are zero)
+//   hi:   bits 0..7   exponent 4 (zero when unused), bits 8..15 zero,
+//         bits 16..31 increment (m << 8) - nb, where m (1..5) is the number of
+//                     codes listed and nb their total length; 0 when the first
+//                     code is longer than the window
+//   mask: bit j set when a listed code starts at offset j of the window (1 for
+//         a window whose first code is longer than the window)
+// The increment advances a decoder accumulator (offset << 8) | (255 - p) by m
+// outputs and nb bits in one add.  Exponents are stored rotated right by one
+// bit, (e >> 1) | ((e & 1) << 7), so that the decoder's merge with the
+// sign/mantissa byte is a single bitfield insert per BF16 pair.
 constexpr uint32_t kDecodeTableMinBits = 10;
 constexpr uint32_t kDecodeTableMaxBits = 12;
-constexpr uint32_t kDecodeTableMaxSyms = 6;
+constexpr uint32_t kDecodeTableMaxSyms = 5;
 
 inline constexpr uint32_t rotate_exponent(uint32_t e) { return ((e >> 1) | (e << 7)) & 0xFFu; }
 

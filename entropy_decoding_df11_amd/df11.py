@@ -23,7 +23,7 @@ from . import _lib
 
 DEFAULT_BYTES_PER_THREAD = 8
 DEFAULT_THREADS_PER_GROUP = 256
-DEFAULT_DECODE_TABLE_BITS = 12
+DEFAULT_DECODE_TABLE_BITS = 11
 
 ArrayLike = Union[np.ndarray, "torch.Tensor"]  # noqa: F821
 
@@ -138,7 +138,7 @@ class DF11Tensor:
     """A DF11 stream resident in GPU memory, decompressed on demand."""
 
     def __init__(self, host: HostStream, shape: Sequence[int], device="cuda",
-                 decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS):
+                 decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS, groups_per_workgroup: int = 0):
         import torch
         self.host_header = host.header
         self.shape = tuple(int(s) for s in shape)
@@ -167,7 +167,12 @@ class DF11Tensor:
         for name, t in self._bufs.items():
             setattr(s, name, t.data_ptr())
         s.decode_table_bits = decode_table_bits
+        s.groups_per_workgroup = groups_per_workgroup
         self._stream_struct = s
+
+    def set_groups_per_workgroup(self, gpw: int) -> None:
+        """Launch shape: groups decoded together by one workgroup (0 = default, 1, 2, 4)."""
+        self._stream_struct.groups_per_workgroup = gpw
 
     @property
     def n_elements(self) -> int:

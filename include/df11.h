@@ -118,7 +118,9 @@ typedef struct df11_header {
  *   code_lengths device, 256             df11_codebook.code_lengths
  *   decode_table device, df11_decode_table_bytes(decode_table_bits)
  *                                        built by df11_build_decode_table
- *   decode_table_bits                    index width of decode_table (10..12) */
+ *   decode_table_bits                    index width of decode_table (10..12)
+ *   groups_per_workgroup                 launch shape: groups decoded together by one
+ *                                        workgroup (1, 2 or 4); 0 picks the default */
 typedef struct df11_device_stream {
     df11_header h;
     const uint8_t *enc;
@@ -129,7 +131,7 @@ typedef struct df11_device_stream {
     const uint8_t *code_lengths;
     const void *decode_table;
     uint32_t decode_table_bits;
-    uint32_t reserved;
+    uint32_t groups_per_workgroup;
 } df11_device_stream;
 
 /* Accumulate the 256-bin exponent histogram of n BF16 words (host).

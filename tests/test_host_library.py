@@ -172,7 +172,7 @@ def test_library_error_paths():
     # decode table sizes
     lib = _lib.load()
     assert lib.df11_decode_table_bytes(9) == 0 and lib.df11_decode_table_bytes(13) == 0
-    assert lib.df11_decode_table_bytes(12) == 8 << 12
+    assert lib.df11_decode_table_bytes(12) == 10 << 12
     buf = np.zeros(10, np.uint32)
     assert lib.df11_build_decode_table(ctypes.byref(cb), 12, buf.ctypes.data_as(ctypes.c_void_p), 40) == -5
 
@@ -253,16 +253,19 @@ def test_decode_table_matches_code_table(workload, bits, case):
     ref = oracle.codebook(oracle.histogram(w))
     cb = df11.build_codebook(df11.histogram(w))
     table = df11.decode_table(cb, bits)
-    lo, hi = table[: 1 << bits], table[1 << bits:]
+    size = 1 << bits
+    assert table.nbytes == 10 * size
+    lo, hi = table[:size], table[size:2 * size]
+    mask = table[2 * size:].view(np.uint16)
     rot = lambda e: ((e >> 1) | (e << 7)) & 0xFF
-    for x in range(1 << bits):
-        syms, starts, used = _greedy_window(ref["code_lengths"], ref["codes"], x, bits, 6)
+    for x in range(size):
+        syms, starts, used = _greedy_window(ref["code_lengths"], ref["codes"], x, bits, 5)
         h = int(hi[x])
         if not syms:
-            assert h >> 16 == 0
-            assert (h & 0xFF) == ref["luts"][0][x >> (bits - 8)] >= 240
+            assert h == 0 and int(lo[x]) == 0 and int(mask[x]) == 1
+            assert ref["luts"][0][x >> (bits - 8)] >= 240
             continue
-        assert h >> 28 == used
-        assert (h >> 16) & 0xFFF == sum(1 << s for s in starts)
-        got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [(h >> (8 * j)) & 0xFF for j in range(2)]
-        assert got[: len(syms)] == [rot(s) for s in syms]
+        assert h >> 16 == (len(syms) << 8) - used
+        assert int(mask[x]) == sum(1 << s for s in starts)
+        got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [h & 0xFF, (h >> 8) & 0xFF]
+        assert got == [rot(s) for s in syms] + [0] * (6 - len(syms))
