@@ -108,16 +108,21 @@ __device__ __forceinline__ uint32_t bitfield_insert(uint32_t mask, uint32_t a, u
 
 // Merge 8 rotated exponents with 8 sign/mantissa bytes into 8 BF16 words.
 // With r = exponent rotated right by one bit, a BF16 is
-//   low byte  = (r & 0x80) | (sm & 0x7F),   high byte = (sm & 0x80) | (r & 0x7F).
+//   low byte  = (r & 0x80) | (sm & 0x7F),   high byte = (sm & 0x80) | (r & 0x7F),
+// so two bitfield inserts give the low and high bytes of four outputs and two
+// byte permutes interleave them.
+__device__ __forceinline__ void merge4(uint32_t s4, uint32_t r4, uint32_t &out01, uint32_t &out23) {
+    const uint32_t lo = bitfield_insert(0x7F7F7F7Fu, s4, r4);
+    const uint32_t hi = bitfield_insert(0x80808080u, s4, r4);
+    // v_perm byte selectors: 0..3 pick bytes of the second operand (lo), 4..7 of the first (hi).
+    out01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    out23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
 __device__ __forceinline__ uint4 merge8(uint64_t sm8, uint64_t r8) {
-    const uint32_t s0 = static_cast<uint32_t>(sm8), s1 = static_cast<uint32_t>(sm8 >> 32);
-    const uint32_t r0 = static_cast<uint32_t>(r8), r1 = static_cast<uint32_t>(r8 >> 32);
-    constexpr uint32_t kFromSm = 0x807F807Fu;
     uint4 o;
-    o.x = bitfield_insert(kFromSm, __builtin_amdgcn_perm(s0, s0, 0x01010000u), __builtin_amdgcn_perm(r0, r0, 0x01010000u));
-    o.y = bitfield_insert(kFromSm, __builtin_amdgcn_perm(s0, s0, 0x03030202u), __builtin_amdgcn_perm(r0, r0, 0x03030202u));
-    o.z = bitfield_insert(kFromSm, __builtin_amdgcn_perm(s1, s1, 0x01010000u), __builtin_amdgcn_perm(r1, r1, 0x01010000u));
-    o.w = bitfield_insert(kFromSm, __builtin_amdgcn_perm(s1, s1, 0x03030202u), __builtin_amdgcn_perm(r1, r1, 0x03030202u));
+    merge4(static_cast<uint32_t>(sm8), static_cast<uint32_t>(r8), o.x, o.y);
+    merge4(static_cast<uint32_t>(sm8 >> 32), static_cast<uint32_t>(r8 >> 32), o.z, o.w);
     return o;
 }
 
@@ -131,13 +136,16 @@ __device__ __forceinline__ uint32_t lds_offset(const uint8_t *p) {
 }
 
 // OR up to 5 bytes (lo, then the low byte of hi8; higher bytes zero) into LDS
-// at byte offset off.  LDS stores that are not naturally aligned are several
-// times slower on gfx950, so the bytes are shifted into the two aligned dwords
-// they span and combined with aligned atomic ORs; bytes that are zero leave
-// their neighbours untouched.
-__device__ __forceinline__ void lds_or5(uint32_t off, uint32_t lo, uint32_t hi8) {
-    const uint64_t x = ((static_cast<uint64_t>(hi8) << 32) | lo) << ((off & 3u) * 8u);
-    LdsU32 *d = (LdsU32 *)(uintptr_t)(off & ~3u);
+// at the byte address held in acc = (address << 11) | p, p < 256.  LDS stores
+// that are not naturally aligned are several times slower on gfx950, so the
+// bytes are shifted into the two aligned dwords they span and combined with
+// aligned atomic ORs; bytes that are zero leave their neighbours untouched.
+// limit caps the address (so a corrupt stream cannot reach past its buffer).
+__device__ __forceinline__ void lds_or5(uint32_t acc, uint32_t limit, uint32_t lo, uint32_t hi8) {
+    const uint32_t addr = min(acc >> 11, limit);
+    const uint32_t shift = (addr & 3u) * 8u;
+    const uint64_t x = ((static_cast<uint64_t>(hi8) << 32) | lo) << shift;
+    LdsU32 *d = (LdsU32 *)(uintptr_t)(addr & ~3u);
     __hip_atomic_fetch_or(d, static_cast<uint32_t>(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __hip_atomic_fetch_or(d + 1, static_cast<uint32_t>(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -210,14 +218,9 @@ __device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g,
     return r;
 }
 
-// Bits [p, p + 32) of the thread's 96-bit window for p < 64, with the
-// position passed as acc whose low byte is 255 - p.  v0..v2 hold the window
-// shifted right by one bit, so the funnel shift amount 31 - p (taken mod 32
-// by v_alignbit, which reads only the low 5 bits of acc) stays in range for
-// every p, including p = 0 and 32.  p < 32 exactly when the low byte is >= 224.
-__device__ __forceinline__ uint32_t window_at(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t acc) {
-    const bool low = (acc & 0xFFu) >= 0xE0u;
-    return __builtin_amdgcn_alignbit(low ? v0 : v1, low ? v1 : v2, acc);
+// Bits [p, p + 32) of the thread's 96-bit window (w0 w1 w2, MSB-first), p < 64.
+__device__ __forceinline__ uint32_t window_at(uint64_t pa, uint64_t pb, uint32_t p) {
+    return static_cast<uint32_t>((p < 32u ? pa << p : pb << (p - 32u)) >> 32);
 }
 
 // Merge one decoded group's exponents with its sign/mantissa bytes and store
@@ -265,6 +268,8 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     const uint32_t *s_lo = s_tab;
     const uint32_t *s_hi = s_tab + (1u << K);
     const uint16_t *s_mask = reinterpret_cast<const uint16_t *>(s_tab + (2u << K));
+    // The increment (high half of each hi word), read with one 16-bit load.
+    const uint16_t *s_inc = reinterpret_cast<const uint16_t *>(s_hi) + 1;
     uint8_t *s_luts = smem;
     uint8_t *s_clen = s_luts + a.n_luts * 256u;
     const uint32_t tid = threadIdx.x;
@@ -332,30 +337,48 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
             seg_end = t + 1 < a.n_threads ? kSegBits : a.last_seg_bits;
         }
         const uint32_t w0 = bswap32(cur.e0), w1 = bswap32(cur.e1), w2 = bswap32(cur.e2);
-        const uint32_t v0 = w0 >> 1;
-        const uint32_t v1 = __builtin_amdgcn_alignbit(w0, w1, 1);
-        const uint32_t v2 = __builtin_amdgcn_alignbit(w1, w2, 1);
+        // Lookups that start in bits [0, 32) of the segment read the pair w0 w1
+        // and those that start later read w1 w2, each with one 64-bit shift by
+        // the start bit: a code read from bit p < 32 plus the K-bit window ends
+        // before bit 64 of its pair.  Positions are kept in accumulators
+        // (x << 11) | p; a table increment (m << 11) + nb adds m to x and nb to p.
+        const uint64_t pa = (static_cast<uint64_t>(w0) << 32) | w1;
+        const uint64_t pb = (static_cast<uint64_t>(w1) << 32) | w2;
+        const uint32_t end_a = min(seg_end, 32u);
+        const uint32_t end_b = seg_end > 32u ? seg_end - 32u : 0u;
 
-        // Phase 1: count the codes that start in [gap, seg_end).  acc holds
-        // (count << 8) | (255 - p); one table increment adds m codes and nb bits.
-        const uint32_t n_end = 255u - seg_end;
-        uint32_t acc = 255u - gap, last = acc;
-        while ((acc & 0xFFu) > n_end) {
-            const uint32_t win = window_at(v0, v1, v2, acc);
-            uint32_t inc = s_hi[win >> (32 - K)] >> 16;
+        // Phase 1: count the codes that start in [gap, seg_end).
+        uint32_t acc = gap, last = 0;
+        while ((acc & 0xFFu) < end_a) {
+            const uint32_t win = static_cast<uint32_t>((pa << (acc & 63u)) >> 32);
+            uint32_t inc = s_inc[2u * (win >> (32 - K))];
             if (inc == 0) {  // first code longer than the window
                 uint32_t len;
                 walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
-                inc = 256u - len;
+                inc = (1u << 11) + len;
             }
             last = acc;
             acc += inc;
         }
-        uint32_t cnt = acc >> 8;
+        if (end_b) {
+            acc -= 32u;
+            while ((acc & 0xFFu) < end_b) {
+                const uint32_t win = static_cast<uint32_t>((pb << (acc & 63u)) >> 32);
+                uint32_t inc = s_inc[2u * (win >> (32 - K))];
+                if (inc == 0) {
+                    uint32_t len;
+                    walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
+                    inc = (1u << 11) + len;
+                }
+                last = acc + 32u;
+                acc += inc;
+            }
+        }
+        uint32_t cnt = acc >> 11;
         if (cnt) {
             // The last lookup may list codes that start at or after seg_end.
-            const uint32_t p_last = 255u - (last & 0xFFu);
-            const uint32_t mask = s_mask[window_at(v0, v1, v2, last) >> (32 - K)];
+            const uint32_t p_last = last & 0xFFu;
+            const uint32_t mask = s_mask[window_at(pa, pb, p_last) >> (32 - K)];
             cnt -= __popc(mask >> min(seg_end - p_last, 31u));
         }
 
@@ -369,26 +392,44 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t o_start = lead + wave_off + incl - cnt;
         const uint32_t o_end = min(o_start + cnt, a.ebuf_cap - 8u);
 
-        // Phase 2: decode again and OR the (rotated) exponents into the zeroed
-        // LDS buffer at their output positions.  acc2 holds
-        // (LDS address << 8) | (255 - p).  A thread's last lookup may list codes
-        // that start past its segment; those are the next thread's first codes,
-        // decoded at the same code boundaries, so they land on the next
-        // thread's first outputs with the same values (or, after the group's
-        // last output, in the chunk the merge zeroes).
+        // Phase 2: decode the same lookups again and OR the (rotated) exponents
+        // into the zeroed LDS buffer at their output positions (accumulator x =
+        // LDS byte address).  A thread's last lookup may list codes that start
+        // past its segment; those are the next thread's first codes, decoded at
+        // the same code boundaries, so they land on the next thread's first
+        // outputs with the same values (or, after the group's last output, in
+        // the chunk the merge zeroes).
         const uint32_t ebase = lds_offset(s_ebuf);
-        for (uint32_t acc2 = ((ebase + o_start) << 8) | (255u - gap); acc2 < ((ebase + o_end) << 8);) {
-            const uint32_t win = window_at(v0, v1, v2, acc2);
+        const uint32_t elimit = ebase + a.ebuf_cap - 8u;
+        uint32_t acc2 = ((ebase + o_start) << 11) | gap;
+        while ((acc2 & 0xFFu) < end_a) {
+            const uint32_t win = static_cast<uint32_t>((pa << (acc2 & 63u)) >> 32);
             const uint32_t idx = win >> (32 - K);
             uint32_t lo = s_lo[idx];
             uint32_t hi = s_hi[idx];
             if (hi < 0x10000u) {  // first code longer than the window
                 uint32_t len;
                 lo = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len));
-                hi = (256u - len) << 16;
+                hi = ((1u << 11) + len) << 16;
             }
-            lds_or5(acc2 >> 8, lo, hi & 0xFFu);
+            lds_or5(acc2, elimit, lo, hi & 0xFFu);
             acc2 += hi >> 16;
+        }
+        if (end_b) {
+            acc2 -= 32u;
+            while ((acc2 & 0xFFu) < end_b) {
+                const uint32_t win = static_cast<uint32_t>((pb << (acc2 & 63u)) >> 32);
+                const uint32_t idx = win >> (32 - K);
+                uint32_t lo = s_lo[idx];
+                uint32_t hi = s_hi[idx];
+                if (hi < 0x10000u) {
+                    uint32_t len;
+                    lo = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len));
+                    hi = ((1u << 11) + len) << 16;
+                }
+                lds_or5(acc2, elimit, lo, hi & 0xFFu);
+                acc2 += hi >> 16;
+            }
         }
         __syncthreads();
 

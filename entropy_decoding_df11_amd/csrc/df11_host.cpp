@@ -375,7 +375,7 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
             lo_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * j);
         for (uint32_t j = 4; j < m; ++j)
             hi_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * (j - 4));
-        if (m) hi_word |= ((m << 8) - used) << 16;
+        if (m) hi_word |= ((m << 11) + used) << 16;
         lo[x] = lo_word;
         hi[x] = hi_word;
         mask_out[x] = static_cast<uint16_t>(m ? mask : 1u);

@@ -12,15 +12,16 @@ namespace df11 {
 //   lo:   exponents 0..3 of the complete codes at the start of the window
 //         (byte j = j-th code; unused bytes are zero)
 //   hi:   bits 0..7   exponent 4 (zero when unused), bits 8..15 zero,
-//         bits 16..31 increment (m << 8) - nb, where m (1..5) is the number of
+//         bits 16..31 increment (m << 11) + nb, where m (1..5) is the number of
 //                     codes listed and nb their total length; 0 when the first
 //                     code is longer than the window
 //   mask: bit j set when a listed code starts at offset j of the window (1 for
 //         a window whose first code is longer than the window)
-// The increment advances a decoder accumulator (offset << 8) | (255 - p) by m
-// outputs and nb bits in one add.  Exponents are stored rotated right by one
-// bit, (e >> 1) | ((e & 1) << 7), so that the decoder's merge with the
-// sign/mantissa byte is a single bitfield insert per BF16 pair.
+// The increment advances a decoder accumulator (x << 11) | p, p < 256, by m in
+// x and nb in p with one add; x is a count of codes or an LDS byte address.
+// Exponents are stored rotated right by one bit, (e >> 1) | ((e & 1) << 7), so
+// that each byte of a BF16 word is one bitfield insert of a rotated exponent
+// byte and a sign/mantissa byte.
 constexpr uint32_t kDecodeTableMinBits = 10;
 constexpr uint32_t kDecodeTableMaxBits = 12;
 constexpr uint32_t kDecodeTableMaxSyms = 5;

@@ -265,7 +265,7 @@ def test_decode_table_matches_code_table(workload, bits, case):
             assert h == 0 and int(lo[x]) == 0 and int(mask[x]) == 1
             assert ref["luts"][0][x >> (bits - 8)] >= 240
             continue
-        assert h >> 16 == (len(syms) << 8) - used
+        assert h >> 16 == (len(syms) << 11) + used
         assert int(mask[x]) == sum(1 << s for s in starts)
         got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [h & 0xFF, (h >> 8) & 0xFF]
         assert got == [rot(s) for s in syms] + [0] * (6 - len(syms))
