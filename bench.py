@@ -9,8 +9,9 @@ in HBM.  Prints one JSON line.
   algorithmic bytes per step = EncodedExponent + PackedSignMantissa + Gaps
               + output positions + LUTs + CodeLengths (all unpadded) read,
               plus 2 bytes per BF16 weight written
-  roofline  = the same bytes / the decode kernel's mean duration (HIP events
-              around each launch on its stream) against the 8 TB/s HBM peak
+  roofline  = the same bytes / the decode kernel's mean duration (a pair of
+              HIP events per launch that the kernel dispatch itself records on
+              its stream, hipExtLaunchKernel) against the 8 TB/s HBM peak
   cpu_baseline = the CPU oracle's tree-walk decoder, group-parallel over the
               host's cores, on the same workload
 """
@@ -66,6 +67,95 @@ def _cpu_baseline(flat: np.ndarray, threads: int):
     return algo / dt / 1e9, dt, ok
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _pmc_per_dispatch(run_dir, counter):
+    """{dispatch id: (kernel name, grid size, counter summed over instances)}"""
+    per = {}
+    for r in _read_csv(os.path.join(run_dir, "run_counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, grid, v = per.get(d, (r["Kernel_Name"], int(r["Grid_Size"]), 0.0))
+        per[d] = (name, grid, v + float(r["Counter_Value"]))
+    return per
+
+
+def summarize_profiles(prof_dir: str, commands: dict) -> None:
+    """Turn the rocprofv3 output of one kernel-trace run and two PMC runs of this
+    script into the committed summaries under profiles/.
+
+    prof_dir holds trace/ (--kernel-trace --stats), fetch/ (--pmc FETCH_SIZE),
+    write/ (--pmc WRITE_SIZE) and bench.json (the JSON line of the trace run).
+    FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by the ratio
+    of known bytes to counted bytes of the plain copy kernel the same run
+    launches (10 copies of a buffer of known size)."""
+    stats = _read_csv(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))
+    with open(os.path.join(prof_dir, "bench.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
+    copy_bytes = algo // 2
+
+    def split(per):
+        dec = [v for (name, _, v) in per.values() if "df11_decode" in name]
+        cpy = [v for (name, _, v) in per.values() if "copyBuffer" in name and abs(v * 1024 - copy_bytes) < 0.6 * copy_bytes]
+        return dec, cpy
+
+    fetch_dec, fetch_cpy = split(_pmc_per_dispatch(os.path.join(prof_dir, "fetch"), "FETCH_SIZE"))
+    write_dec, write_cpy = split(_pmc_per_dispatch(os.path.join(prof_dir, "write"), "WRITE_SIZE"))
+    if not (fetch_dec and fetch_cpy and write_dec and write_cpy):
+        raise SystemExit("summarize: decode or copy dispatches missing from the PMC runs")
+    kib = lambda xs: float(np.median(xs))
+    fetch_scale = copy_bytes / (kib(fetch_cpy) * 1024)
+    write_scale = copy_bytes / (kib(write_cpy) * 1024)
+    read_b = kib(fetch_dec) * 1024 * fetch_scale
+    write_b = kib(write_dec) * 1024 * write_scale
+
+    dec_row = [r for r in stats if "df11_decode" in r["Name"]]
+    lines = ["# df11_decode_kernel on llama3_8b_block: rocprofv3 kernel trace", "",
+             "Command (from the repository root on a one-GPU MI355X box):", "",
+             "    " + commands["trace"], "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in stats[:6]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
+    avg_us = float(dec_row[0]["AverageNs"]) / 1e3
+    lines += ["", f"Decode kernel average {avg_us:.2f} us per launch for {algo} algorithmic bytes "
+              f"({algo / (avg_us * 1e-6) / 1e9:.1f} GB/s, {algo / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s). "
+              f"The same run's bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with HIP events "
+              f"on the launch stream (the events add the launch gap).", "",
+             "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
+    with open(os.path.join(os.path.dirname(PMC_SUMMARY), "df11_decode_kernel_llama3_8b_block_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+    pmc = {
+        "kernel": "df11_decode_kernel",
+        "workload": "llama3_8b_block",
+        "kernel_source_sha256_16": _kernel_hash(),
+        "commands": {"fetch": commands["fetch"], "write": commands["write"]},
+        "decode_fetch_kib_per_dispatch": kib(fetch_dec),
+        "decode_write_kib_per_dispatch": kib(write_dec),
+        "copy_bytes_per_dispatch": copy_bytes,
+        "copy_fetch_kib_per_dispatch": kib(fetch_cpy),
+        "copy_write_kib_per_dispatch": kib(write_cpy),
+        "fetch_scale": round(fetch_scale, 4),
+        "write_scale": round(write_scale, 4),
+        "hbm_read_bytes_per_launch": int(read_b),
+        "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(read_b + write_b),
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": round((read_b + write_b) / algo, 4),
+    }
+    with open(PMC_SUMMARY, "w") as f:
+        json.dump(pmc, f, indent=1)
+        f.write("\n")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,7 +164,21 @@ def main() -> int:
     ap.add_argument("--decode-table-bits", type=int, default=11)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: usable host cores)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 runs of this script under DIR, then exit")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        pre = "cd /tmp && export TMPDIR=/tmp && "   # R = repository root, D = R/gpurun_out/prof
+        summarize_profiles(args.summarize_profiles, {
+            "trace": pre + "rocprofv3 --kernel-trace --stats -d $D/trace -o run --output-format csv "
+                           "-- python3 $R/bench.py --steps 20 --warmup 3 --no-cpu-baseline > $D/bench.json",
+            "fetch": pre + "rocprofv3 --pmc FETCH_SIZE -d $D/fetch -o run --output-format csv "
+                           "-- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
+                           "-- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        })
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: DF11 decoding needs no exchange between GPUs, and every "
@@ -111,12 +215,12 @@ def main() -> int:
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + ends:  # create the events outside the timed region
+        e.record(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        blk.decompress(scratch=scratch)
-        ends[i].record(stream)
+        blk.decompress(scratch=scratch, events=(starts[i], ends[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]

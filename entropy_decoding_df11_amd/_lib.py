@@ -35,6 +35,7 @@ EXPORTED = [
     "df11_build_decode_table",
     "df11_decompress",
     "df11_decompress_block",
+    "df11_decompress_timed",
     "df11_status_str",
 ]
 
@@ -128,6 +129,8 @@ def load() -> ctypes.CDLL:
         "df11_decompress": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p]),
         "df11_decompress_block": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint64,
                                                  ctypes.c_void_p]),
+        "df11_decompress_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p]),
         "df11_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

@@ -23,11 +23,12 @@
 //      16-byte coalesced stores.
 //
 // Decoding a code: the next K bits index a first-level LDS table that lists
-// every complete code at the start of the window (up to six), so one lookup
+// every complete code at the start of the window (up to five), so one lookup
 // resolves several of the 2-3 bit codes that dominate LLM exponents.  A window
 // whose first code is longer than K bits continues in the page's LUT hierarchy
 // (256-entry LUTs, values 240..255 pointing to lower LUTs) and CodeLengths,
 // which are also staged in LDS.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,6 +48,14 @@ constexpr uint32_t kWaves = kThreadsPerGroup / kWaveSize;
 constexpr uint32_t kSegBits = 8 * kBytesPerThread;
 constexpr int kPrefetchChunks = 4;  // 8-element sign/mantissa chunks held in registers per thread
 constexpr uint32_t kDefaultGroupsPerWorkgroup = 2;
+// Bytes of an exponent buffer that one thread's phase 2 can reach past its
+// first output: at most 64 + 11 codes start in the bits it walks (every code
+// is at least one bit), and the last OR touches the 8 aligned bytes around
+// its address.  A thread's start offset is clamped this far below the end of
+// the buffer, which no valid stream reaches (the buffer holds the largest
+// group plus this much), so a corrupt one stays inside it.
+constexpr uint32_t kDecodeReach = 96;
+constexpr uint32_t kLongCode = df11::kLongCodeIncrement;
 
 struct DecodeArgs {
     const uint8_t *enc;
@@ -135,19 +144,17 @@ __device__ __forceinline__ uint32_t lds_offset(const uint8_t *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LdsU8 *)p));
 }
 
-// OR up to 5 bytes (lo, then the low byte of hi8; higher bytes zero) into LDS
-// at the byte address held in acc = (address << 11) | p, p < 256.  LDS stores
-// that are not naturally aligned are several times slower on gfx950, so the
-// bytes are shifted into the two aligned dwords they span and combined with
-// aligned atomic ORs; bytes that are zero leave their neighbours untouched.
-// limit caps the address (so a corrupt stream cannot reach past its buffer).
-__device__ __forceinline__ void lds_or5(uint32_t acc, uint32_t limit, uint32_t lo, uint32_t hi8) {
-    const uint32_t addr = min(acc >> 11, limit);
-    const uint32_t shift = (addr & 3u) * 8u;
-    const uint64_t x = ((static_cast<uint64_t>(hi8) << 32) | lo) << shift;
-    LdsU32 *d = (LdsU32 *)(uintptr_t)(addr & ~3u);
-    __hip_atomic_fetch_or(d, static_cast<uint32_t>(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_or(d + 1, static_cast<uint32_t>(x >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// OR the 5-byte exponent run x (byte 0 first; unused bytes zero) into LDS at
+// the byte address held in acc = (address << 11) | p, p < 256.  LDS stores
+// that are not naturally aligned are several times slower on gfx950, so x is
+// shifted into the two aligned dwords it spans and combined with aligned
+// atomic ORs; zero bytes leave their neighbours untouched.  Bits 8..10 of acc
+// are zero, so bits 8..12 are (address & 3) * 8, the shift.
+__device__ __forceinline__ void or_exponents(uint32_t acc, uint64_t x) {
+    const uint64_t xs = x << __builtin_amdgcn_ubfe(acc, 8, 5);
+    LdsU32 *d = (LdsU32 *)(uintptr_t)((acc >> 11) & ~3u);
+    __hip_atomic_fetch_or(d, static_cast<uint32_t>(xs), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(d + 1, static_cast<uint32_t>(xs >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Store chunk c (elements 8c .. 8c+7) restricted to [base, end).  Whole chunks
@@ -176,6 +183,8 @@ using ConstU32 = const __attribute__((address_space(4))) uint32_t;
 __device__ __forceinline__ uint32_t out_pos_at(const DecodeArgs &a, uint32_t g) {
     return ((const ConstU32 *)a.out_pos)[min(g, a.n_groups)];
 }
+
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Number of 8-element chunks that hold the outputs [base, end).
 __device__ __forceinline__ uint32_t group_chunks(uint32_t base, uint32_t end) {
@@ -218,6 +227,18 @@ __device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g,
     return r;
 }
 
+// Byte offset of the first-level table entry (one uint32 per entry in each
+// array) for the K-bit window at bit p = acc & 63 of the 64-bit pair.
+template <int K>
+__device__ __forceinline__ uint32_t entry_offset(uint64_t pair, uint32_t acc) {
+    return (static_cast<uint32_t>((pair << (acc & 63u)) >> 32) >> (30 - K)) & ~3u;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_at(const void *base, uint32_t byte_offset) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const uint8_t *>(base) + byte_offset);
+}
+
 // Bits [p, p + 32) of the thread's 96-bit window (w0 w1 w2, MSB-first), p < 64.
 __device__ __forceinline__ uint32_t window_at(uint64_t pa, uint64_t pb, uint32_t p) {
     return static_cast<uint32_t>((p < 32u ? pa << p : pb << (p - 32u)) >> 32);
@@ -252,12 +273,17 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
 }
 
 // GPW groups of 256 threads share one workgroup (and one copy of the decode
-// tables in LDS).  Each workgroup owns a contiguous range of "super-groups" of
-// GPW consecutive groups.  Iteration s first merges and stores super-group
-// s - 1 (decoded in the previous iteration into the other half of a
-// double-buffered LDS exponent buffer), then issues the loads of super-group
-// s + 1, then decodes super-group s.  Every wait for loaded data therefore
-// comes a whole decode phase after the last stores were issued.
+// tables in LDS).  Super-groups (GPW consecutive groups) are dealt to the
+// workgroups round-robin, so at any moment the whole grid reads and writes
+// one compact window of each buffer rather than one region per workgroup,
+// which HBM serves markedly faster.  (Neighbouring super-groups thus run on
+// different XCDs, since workgroup i goes to XCD i mod 8; grouping them per
+// XCD instead measured slower, as it splits the window into eight.)
+// Iteration i first merges and
+// stores the super-group decoded in iteration i - 1 (held in the other half
+// of a double-buffered LDS exponent buffer), then issues the loads of the
+// super-group of iteration i + 1, then decodes its own.  Every wait for loaded
+// data therefore comes a whole decode phase after the last stores were issued.
 template <int K, int GPW>
 __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
     // Static LDS: the first-level table (lo words | hi words | start masks) at a
@@ -266,10 +292,8 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     __shared__ __align__(16) uint32_t s_tab[(10u << K) / 4u];
     extern __shared__ __align__(16) uint8_t smem[];
     const uint32_t *s_lo = s_tab;
-    const uint32_t *s_hi = s_tab + (1u << K);
-    const uint16_t *s_mask = reinterpret_cast<const uint16_t *>(s_tab + (2u << K));
-    // The increment (high half of each hi word), read with one 16-bit load.
-    const uint16_t *s_inc = reinterpret_cast<const uint16_t *>(s_hi) + 1;
+    const uint32_t *s_aux = s_tab + (1u << K);
+    const uint16_t *s_start = reinterpret_cast<const uint16_t *>(s_tab + (2u << K));
     uint8_t *s_luts = smem;
     uint8_t *s_clen = s_luts + a.n_luts * 256u;
     const uint32_t tid = threadIdx.x;
@@ -281,15 +305,17 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * 2u * a.ebuf_cap) + slot * kWaves;
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
-    const uint32_t s_begin = static_cast<uint32_t>(static_cast<uint64_t>(blockIdx.x) * n_super / gridDim.x);
-    const uint32_t s_end = static_cast<uint32_t>(static_cast<uint64_t>(blockIdx.x + 1) * n_super / gridDim.x);
-    if (s_begin >= s_end) return;  // whole workgroup
+    const uint32_t n_wg = gridDim.x;
+    const uint32_t wg = blockIdx.x;
+    if (wg >= n_super) return;  // whole workgroup
+    const uint32_t n_iter = (n_super - wg + n_wg - 1) / n_wg;
 
     // Pipeline state: out_pos two super-groups ahead (scalar), thread inputs
     // one ahead, sign/mantissa bytes of the group waiting to be merged.
-    const uint32_t g_first = s_begin * GPW + slot;
+    const uint32_t g_first = wg * GPW + slot;
+    const uint32_t g_step = n_wg * GPW;
     uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
-    uint32_t nx_base = out_pos_at(a, g_first + GPW), nx_end = out_pos_at(a, g_first + GPW + 1);
+    uint32_t nx_base = out_pos_at(a, g_first + g_step), nx_end = out_pos_at(a, g_first + g_step + 1);
     GroupLoad cur = load_group(a, g_first, ltid, cur_base, cur_end);
     uint64_t prev_sm[kPrefetchChunks] = {};
     uint32_t prev_base = 0, prev_end = 0;
@@ -311,21 +337,23 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     }
     __syncthreads();
 
-    for (uint32_t s = s_begin; s < s_end; ++s) {
-        const uint32_t g = s * GPW + slot;
-        uint8_t *s_ebuf = s_ebuf2 + (s & 1u) * a.ebuf_cap;
+    for (uint32_t it = 0; it < n_iter; ++it) {
+        const uint32_t g = g_first + it * g_step;
+        uint8_t *s_ebuf = s_ebuf2 + (it & 1u) * a.ebuf_cap;
 
         // 1. Merge and store the super-group decoded in the previous iteration.
-        if (s > s_begin) merge_group(a, s_ebuf2 + ((s - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
+        if (it > 0) merge_group(a, s_ebuf2 + ((it - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
 
-        // 2. Loads of the next super-group.
-        const uint32_t nn_base = out_pos_at(a, g + 2 * GPW), nn_end = out_pos_at(a, g + 2 * GPW + 1);
-        const GroupLoad nx = load_group(a, g + GPW, ltid, nx_base, nx_end);
+        // 2. Loads of the next super-group (group numbers past the end are
+        // clamped inside the loads and never decoded).
+        const uint32_t g_nn = min(g + 2u * g_step, a.n_groups);
+        const uint32_t nn_base = out_pos_at(a, g_nn), nn_end = out_pos_at(a, g_nn + 1);
+        const GroupLoad nx = load_group(a, min(g + g_step, a.n_groups), ltid, uniform(nx_base), uniform(nx_end));
 
         // 3. Decode this super-group.  Output range of the group, clamped so a
         // corrupt out_pos stays in bounds.
-        const uint32_t end = min(cur_end, a.n_elements);
-        const uint32_t base = min(cur_base, end);
+        const uint32_t end = min(uniform(cur_end), a.n_elements);
+        const uint32_t base = min(uniform(cur_base), end);
         const uint32_t lead = base & 7u;
 
         const uint32_t t = g * kThreadsPerGroup + ltid;
@@ -347,38 +375,48 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t end_a = min(seg_end, 32u);
         const uint32_t end_b = seg_end > 32u ? seg_end - 32u : 0u;
 
-        // Phase 1: count the codes that start in [gap, seg_end).
-        uint32_t acc = gap, last = 0;
-        while ((acc & 0xFFu) < end_a) {
+        // Phase 1: count the codes that start in [gap, seg_end).  The fast
+        // loops only look up the table; a window whose first code is longer
+        // than K bits adds kLongCode to p, which ends the loop, and that code
+        // is finished through the LUT hierarchy before the loop resumes.
+        uint32_t acc = gap, inc = 0;
+        for (;;) {
+            while ((acc & 0xFFu) < end_a) {
+                inc = lds_at<uint16_t>(s_aux, entry_offset<K>(pa, acc));
+                acc += inc;
+            }
+            if (!(acc & kLongCode)) break;
+            acc -= kLongCode;
             const uint32_t win = static_cast<uint32_t>((pa << (acc & 63u)) >> 32);
-            uint32_t inc = s_inc[2u * (win >> (32 - K))];
-            if (inc == 0) {  // first code longer than the window
+            uint32_t len;
+            walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
+            inc = (1u << 11) + len;
+            acc += inc;
+        }
+        uint32_t shift_back = 0;
+        if (end_b) {
+            acc -= 32u;
+            shift_back = 32u;
+            for (;;) {
+                while ((acc & 0xFFu) < end_b) {
+                    inc = lds_at<uint16_t>(s_aux, entry_offset<K>(pb, acc));
+                    acc += inc;
+                }
+                if (!(acc & kLongCode)) break;
+                acc -= kLongCode;
+                const uint32_t win = static_cast<uint32_t>((pb << (acc & 63u)) >> 32);
                 uint32_t len;
                 walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
                 inc = (1u << 11) + len;
-            }
-            last = acc;
-            acc += inc;
-        }
-        if (end_b) {
-            acc -= 32u;
-            while ((acc & 0xFFu) < end_b) {
-                const uint32_t win = static_cast<uint32_t>((pb << (acc & 63u)) >> 32);
-                uint32_t inc = s_inc[2u * (win >> (32 - K))];
-                if (inc == 0) {
-                    uint32_t len;
-                    walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
-                    inc = (1u << 11) + len;
-                }
-                last = acc + 32u;
                 acc += inc;
             }
         }
         uint32_t cnt = acc >> 11;
         if (cnt) {
-            // The last lookup may list codes that start at or after seg_end.
-            const uint32_t p_last = last & 0xFFu;
-            const uint32_t mask = s_mask[window_at(pa, pb, p_last) >> (32 - K)];
+            // The last lookup, at p_last, may list codes that start at or
+            // after seg_end; its start mask says how many.
+            const uint32_t p_last = (acc + shift_back - inc) & 0xFFu;
+            const uint32_t mask = s_start[window_at(pa, pb, p_last) >> (32 - K)];
             cnt -= __popc(mask >> min(seg_end - p_last, 31u));
         }
 
@@ -389,8 +427,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         uint32_t wave_off = 0;
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
-        const uint32_t o_start = lead + wave_off + incl - cnt;
-        const uint32_t o_end = min(o_start + cnt, a.ebuf_cap - 8u);
+        const uint32_t o_start = min(lead + wave_off + incl - cnt, a.ebuf_cap - kDecodeReach);
 
         // Phase 2: decode the same lookups again and OR the (rotated) exponents
         // into the zeroed LDS buffer at their output positions (accumulator x =
@@ -399,36 +436,40 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         // the same code boundaries, so they land on the next thread's first
         // outputs with the same values (or, after the group's last output, in
         // the chunk the merge zeroes).
-        const uint32_t ebase = lds_offset(s_ebuf);
-        const uint32_t elimit = ebase + a.ebuf_cap - 8u;
-        uint32_t acc2 = ((ebase + o_start) << 11) | gap;
-        while ((acc2 & 0xFFu) < end_a) {
-            const uint32_t win = static_cast<uint32_t>((pa << (acc2 & 63u)) >> 32);
-            const uint32_t idx = win >> (32 - K);
-            uint32_t lo = s_lo[idx];
-            uint32_t hi = s_hi[idx];
-            if (hi < 0x10000u) {  // first code longer than the window
-                uint32_t len;
-                lo = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len));
-                hi = ((1u << 11) + len) << 16;
+        uint32_t acc2 = ((lds_offset(s_ebuf) + o_start) << 11) | gap;
+        for (;;) {
+            while ((acc2 & 0xFFu) < end_a) {
+                // lo and aux are one paired LDS read.
+                const uint32_t off = entry_offset<K>(pa, acc2);
+                const uint32_t w = lds_at<uint32_t>(s_aux, off);
+                const uint32_t at = acc2;
+                acc2 += w & 0xFFFFu;
+                or_exponents(at, (static_cast<uint64_t>(w >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
             }
-            lds_or5(acc2, elimit, lo, hi & 0xFFu);
-            acc2 += hi >> 16;
+            if (!(acc2 & kLongCode)) break;
+            acc2 -= kLongCode;
+            const uint32_t win = static_cast<uint32_t>((pa << (acc2 & 63u)) >> 32);
+            uint32_t len;
+            or_exponents(acc2, df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len)));
+            acc2 += (1u << 11) + len;
         }
         if (end_b) {
             acc2 -= 32u;
-            while ((acc2 & 0xFFu) < end_b) {
-                const uint32_t win = static_cast<uint32_t>((pb << (acc2 & 63u)) >> 32);
-                const uint32_t idx = win >> (32 - K);
-                uint32_t lo = s_lo[idx];
-                uint32_t hi = s_hi[idx];
-                if (hi < 0x10000u) {
-                    uint32_t len;
-                    lo = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len));
-                    hi = ((1u << 11) + len) << 16;
+            for (;;) {
+                while ((acc2 & 0xFFu) < end_b) {
+                    const uint32_t off = entry_offset<K>(pb, acc2);
+                    const uint32_t w = lds_at<uint32_t>(s_aux, off);
+                    const uint32_t at = acc2;
+                    acc2 += w & 0xFFFFu;
+                    or_exponents(at, (static_cast<uint64_t>(w >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
                 }
-                lds_or5(acc2, elimit, lo, hi & 0xFFu);
-                acc2 += hi >> 16;
+                if (!(acc2 & kLongCode)) break;
+                acc2 -= kLongCode;
+                const uint32_t win = static_cast<uint32_t>((pb << (acc2 & 63u)) >> 32);
+                uint32_t len;
+                or_exponents(acc2,
+                             df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len)));
+                acc2 += (1u << 11) + len;
             }
         }
         __syncthreads();
@@ -443,7 +484,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         nx_base = nn_base;
         nx_end = nn_end;
     }
-    merge_group(a, s_ebuf2 + ((s_end - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
+    merge_group(a, s_ebuf2 + ((n_iter - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -484,36 +525,58 @@ int validate(const df11_device_stream *s) {
     return DF11_OK;
 }
 
+// Workgroups of this kernel instance that fit on one CU, per device (0 until
+// first queried).
 template <int K, int GPW>
-int launch(const DecodeArgs &a, hipStream_t stream) {
+int resident_per_cu(int dev, size_t lds) {
+    static int cache[64] = {};
+    static size_t cache_lds[64] = {};
+    if (dev >= 0 && dev < 64 && cache[dev] > 0 && cache_lds[dev] == lds) return cache[dev];
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, df11_decode_kernel<K, GPW>, kThreadsPerGroup * GPW,
+                                                     lds) != hipSuccess)
+        return 0;
+    if (dev >= 0 && dev < 64) {
+        cache[dev] = per_cu;
+        cache_lds[dev] = lds;
+    }
+    return per_cu;
+}
+
+template <int K, int GPW>
+int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const size_t lds = a.n_luts * 256u + 256u + GPW * (2u * a.ebuf_cap + 4u * kWaves);  // beyond the static table
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return DF11_E_HIP;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, df11_decode_kernel<K, GPW>, kThreadsPerGroup * GPW,
-                                                     lds) != hipSuccess ||
-        per_cu < 1)
-        return DF11_E_HIP;
+    const int per_cu = resident_per_cu<K, GPW>(dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_super, resident));
     (void)hipGetLastError();
-    hipLaunchKernelGGL((df11_decode_kernel<K, GPW>), dim3(grid), dim3(kThreadsPerGroup * GPW), lds, stream, a);
+    DecodeArgs args = a;
+    void *params[] = {&args};
+    // hipExtLaunchKernel records start / stop (when given) at the kernel's own
+    // start and end, not around the launch.
+    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>), dim3(grid),
+                           dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) != hipSuccess)
+        return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
 
 template <int K>
-int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream) {
+int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     switch (gpw) {
-    case 1: return launch<K, 1>(a, stream);
-    case 4: return launch<K, 4>(a, stream);
-    default: return launch<K, 2>(a, stream);
+    case 1: return launch<K, 1>(a, stream, start, stop);
+    case 4: return launch<K, 4>(a, stream, start, stop);
+    default: return launch<K, 2>(a, stream, start, stop);
     }
 }
 
-int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream) {
+int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop) {
     int rc = validate(s);
     if (rc) return rc;
     const df11_header &h = s->h;
@@ -543,14 +606,14 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     a.n_luts = h.n_luts;
     // lead (< 8) + the group's elements, rounded up to whole 8-byte chunks, plus
     // slack for the 8-byte LDS writes.
-    a.ebuf_cap = static_cast<uint32_t>(round_up(static_cast<uint64_t>(h.max_group_elems) + 16, 16));
+    a.ebuf_cap = static_cast<uint32_t>(round_up(static_cast<uint64_t>(h.max_group_elems) + 8 + kDecodeReach, 16));
     a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
     a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
     const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
     switch (bits) {
-    case 10: return launch_k<10>(a, gpw, stream);
-    case 11: return launch_k<11>(a, gpw, stream);
-    case 12: return launch_k<12>(a, gpw, stream);
+    case 10: return launch_k<10>(a, gpw, stream, start, stop);
+    case 11: return launch_k<11>(a, gpw, stream, start, stop);
+    case 12: return launch_k<12>(a, gpw, stream, start, stop);
     default: return DF11_E_INVALID_ARG;
     }
 }
@@ -560,13 +623,19 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
 extern "C" {
 
 int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream) {
-    return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream));
+    return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
 }
 
 int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64_t scratch_elems, void *hip_stream) {
     if (!s) return DF11_E_INVALID_ARG;
     if (scratch_elems < s->h.n_elements) return DF11_E_BUFFER_TOO_SMALL;
-    return decompress_impl(s, scratch, static_cast<hipStream_t>(hip_stream));
+    return decompress_impl(s, scratch, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
+}
+
+int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,
+                          void *stop_event) {
+    return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"

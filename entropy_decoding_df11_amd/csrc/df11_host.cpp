@@ -324,7 +324,7 @@ int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const
 
 uint64_t df11_decode_table_bytes(uint32_t bits) {
     if (bits < df11::kDecodeTableMinBits || bits > df11::kDecodeTableMaxBits) return 0;
-    return 10ull << bits;  // lo and hi (4 bytes each) and mask (2 bytes) per entry
+    return 10ull << bits;  // lo and aux words and a 16-bit start mask per entry
 }
 
 int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table, uint64_t table_bytes) {
@@ -349,8 +349,8 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
     }
     const uint32_t size = 1u << bits;
     uint32_t *lo = static_cast<uint32_t *>(table);
-    uint32_t *hi = lo + size;
-    uint16_t *mask_out = reinterpret_cast<uint16_t *>(hi + size);
+    uint32_t *aux = lo + size;
+    uint16_t *starts = reinterpret_cast<uint16_t *>(aux + size);
     for (uint32_t x = 0; x < size; ++x) {
         uint32_t used = 0, mask = 0, m = 0;
         uint8_t syms[df11::kDecodeTableMaxSyms] = {0};
@@ -370,15 +370,13 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
             mask |= 1u << used;
             used += static_cast<uint32_t>(len);
         }
-        uint32_t lo_word = 0, hi_word = 0;
+        uint32_t lo_word = 0;
         for (uint32_t j = 0; j < 4 && j < m; ++j)
             lo_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * j);
-        for (uint32_t j = 4; j < m; ++j)
-            hi_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * (j - 4));
-        if (m) hi_word |= ((m << 11) + used) << 16;
         lo[x] = lo_word;
-        hi[x] = hi_word;
-        mask_out[x] = static_cast<uint16_t>(m ? mask : 1u);
+        aux[x] = m ? (((m << 11) + used) | ((m > 4 ? df11::rotate_exponent(syms[4]) : 0u) << 16))
+                   : df11::kLongCodeIncrement;
+        starts[x] = static_cast<uint16_t>(m ? mask : 1u);
     }
     return DF11_OK;
 }

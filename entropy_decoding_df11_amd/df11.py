@@ -193,18 +193,41 @@ class DF11Tensor:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         return ctypes.c_void_p(st.cuda_stream)
 
-    def decompress(self, out: Optional["torch.Tensor"] = None, stream=None) -> "torch.Tensor":  # noqa: F821
+    def decompress(self, out: Optional["torch.Tensor"] = None, stream=None, events=None) -> "torch.Tensor":  # noqa: F821
         """Decode into out (a new bf16 tensor of the original shape by default),
-        enqueued on stream (torch's current stream by default)."""
+        enqueued on stream (torch's current stream by default).  events, a pair
+        of torch.cuda.Event(enable_timing=True), are recorded at the decode
+        kernel's own start and end."""
         import torch
         if out is None:
             out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
         if out.dtype != torch.bfloat16 or out.numel() != self.n_elements or not out.is_contiguous():
             raise ValueError("out must be a contiguous bfloat16 tensor with the stream's element count")
-        lib = _lib.load()
-        _lib.check(lib.df11_decompress(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()),
-                                       self._hip_stream(stream)), "df11_decompress")
+        self._launch(out, stream, events)
         return out
+
+    def _launch(self, out: "torch.Tensor", stream, events) -> None:  # noqa: F821
+        lib = _lib.load()
+        st = self._hip_stream(stream)
+        if events is None:
+            _lib.check(lib.df11_decompress(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()), st),
+                       "df11_decompress")
+            return
+        start, stop = events
+        _lib.check(lib.df11_decompress_timed(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()), st,
+                                             ctypes.c_void_p(_event_handle(start, st)),
+                                             ctypes.c_void_p(_event_handle(stop, st))), "df11_decompress_timed")
+
+
+def _event_handle(ev, stream: ctypes.c_void_p) -> int:
+    """The hipEvent_t behind a torch.cuda.Event, created by recording it once
+    on the launch stream (the decode launch records it again)."""
+    import torch
+    if not isinstance(ev, torch.cuda.Event):
+        raise TypeError("events must be torch.cuda.Event objects")
+    if ev.cuda_event == 0:
+        ev.record(torch.cuda.ExternalStream(stream.value) if stream.value else torch.cuda.default_stream())
+    return ev.cuda_event
 
 
 def compress(tensor: ArrayLike, shape: Optional[Sequence[int]] = None, device="cuda",
@@ -234,16 +257,25 @@ class DF11Block:
     def n_elements(self) -> int:
         return self.tensor.n_elements
 
-    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None,
+                   events=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+        """Decode the block into scratch (at least n_elements bf16; a new one
+        by default) and return a view per weight.  events: as for
+        DF11Tensor.decompress."""
         import torch
         t = self.tensor
         if scratch is None:
             scratch = torch.empty(t.n_elements, dtype=torch.bfloat16, device=t.device)
         if scratch.dtype != torch.bfloat16 or not scratch.is_contiguous():
             raise ValueError("scratch must be a contiguous bfloat16 tensor")
-        lib = _lib.load()
-        _lib.check(lib.df11_decompress_block(ctypes.byref(t.device_stream()), ctypes.c_void_p(scratch.data_ptr()),
-                                             scratch.numel(), t._hip_stream(stream)), "df11_decompress_block")
+        if events is not None:
+            if scratch.numel() < t.n_elements:
+                raise _lib.Df11Error(-5, "df11_decompress_timed")
+            t._launch(scratch, stream, events)
+        else:
+            lib = _lib.load()
+            _lib.check(lib.df11_decompress_block(ctypes.byref(t.device_stream()), ctypes.c_void_p(scratch.data_ptr()),
+                                                 scratch.numel(), t._hip_stream(stream)), "df11_decompress_block")
         flat = scratch.reshape(-1)
         return {name: flat[off:off + int(np.prod(shape))].view(shape) for name, off, shape in self.views}
 

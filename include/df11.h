@@ -177,7 +177,7 @@ uint64_t df11_decode_table_bytes(uint32_t bits);
 /* Build the GPU decoder's first-level table from the codebook (host).
  * The table is derived data, not part of the compressed format: for every
  * bits-wide window it lists the complete codes at the start of the window
- * (up to six exponents, their start offsets and their total length) so one LDS
+ * (up to five exponents, their start offsets and their total length) so one LDS
  * lookup resolves several short codes; windows whose first code is longer than
  * the index width fall back to the page's LUT hierarchy.
  * table: host, df11_decode_table_bytes(bits) bytes. */
@@ -204,6 +204,15 @@ int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream
  * df11_decompress, plus DF11_E_BUFFER_TOO_SMALL if scratch_elems < N. */
 int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64_t scratch_elems,
                           void *hip_stream);
+
+/* df11_decompress with the decode kernel timed by the GPU: start_event and
+ * stop_event (hipEvent_t created by the caller, either may be NULL) are
+ * recorded when the kernel itself starts and ends, so hipEventElapsedTime of
+ * the pair is the kernel's duration without the launch gap.  Used to measure
+ * the decoder; same arguments, output and errors as df11_decompress.  With a
+ * stream of N = 0 nothing is launched and the events are not recorded. */
+int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,
+                          void *stop_event);
 
 /* Static, human-readable name of a status code. */
 const char *df11_status_str(int status);

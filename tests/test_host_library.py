@@ -255,17 +255,20 @@ def test_decode_table_matches_code_table(workload, bits, case):
     table = df11.decode_table(cb, bits)
     size = 1 << bits
     assert table.nbytes == 10 * size
-    lo, hi = table[:size], table[size:2 * size]
-    mask = table[2 * size:].view(np.uint16)
+    lo, aux = table[:size], table[size:2 * size]
+    starts_mask = table[2 * size:].view(np.uint16)
     rot = lambda e: ((e >> 1) | (e << 7)) & 0xFF
     for x in range(size):
         syms, starts, used = _greedy_window(ref["code_lengths"], ref["codes"], x, bits, 5)
-        h = int(hi[x])
+        a = int(aux[x])
         if not syms:
-            assert h == 0 and int(lo[x]) == 0 and int(mask[x]) == 1
+            # long first code: only the position field moves (by 128), and the
+            # code starts at offset 0
+            assert int(lo[x]) == 0 and a == 0x80 and int(starts_mask[x]) == 1
             assert ref["luts"][0][x >> (bits - 8)] >= 240
             continue
-        assert h >> 16 == (len(syms) << 11) + used
-        assert int(mask[x]) == sum(1 << s for s in starts)
-        got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [h & 0xFF, (h >> 8) & 0xFF]
-        assert got == [rot(s) for s in syms] + [0] * (6 - len(syms))
+        assert a & 0xFFFF == (len(syms) << 11) + used
+        assert int(starts_mask[x]) == sum(1 << s for s in starts)
+        assert a >> 24 == 0
+        got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [(a >> 16) & 0xFF]
+        assert got == [rot(s) for s in syms] + [0] * (5 - len(syms))
