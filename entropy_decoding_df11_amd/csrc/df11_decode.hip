@@ -56,6 +56,9 @@ constexpr uint32_t kDefaultGroupsPerWorkgroup = 2;
 // group plus this much), so a corrupt one stays inside it.
 constexpr uint32_t kDecodeReach = 96;
 constexpr uint32_t kLongCode = df11::kLongCodeIncrement;
+// Table lookups per 32-bit half segment whose entries phase 1 keeps in
+// registers for phase 2 (LLM-like exponent streams need 3..5 at K = 11).
+constexpr int kSavedSteps = 6;
 
 struct DecodeArgs {
     const uint8_t *enc;
@@ -272,6 +275,77 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
 }
 
+// Phase 1 over one half of a segment: table lookups from bit p = acc & 0xFF
+// of the 64-bit pair while p < end, advancing acc by each increment (inc keeps
+// the last one).  The entries of the first kSavedSteps lookups go to
+// slo/saux[first ..] (zero for lookups after the lane's last), with a window
+// whose first code is too long replaced by that code alone (rotated exponent,
+// increment (1 << 11) + length).  Further lookups are counted only, and set
+// spill.
+template <int K>
+__device__ __forceinline__ void count_half(uint64_t pair, uint32_t end, uint32_t &acc, uint32_t &inc,
+                                           uint32_t (&slo)[2 * kSavedSteps], uint32_t (&saux)[2 * kSavedSteps],
+                                           int first, bool &spill, const uint32_t *s_lo, const uint32_t *s_aux,
+                                           const uint8_t *s_luts, const uint8_t *s_clen, uint32_t n_luts) {
+#pragma unroll
+    for (int j = 0; j < kSavedSteps; ++j) {
+        const uint32_t off = entry_offset<K>(pair, acc);
+        uint32_t l = lds_at<uint32_t>(s_lo, off);
+        uint32_t x = lds_at<uint32_t>(s_aux, off);
+        const bool act = (acc & 0xFFu) < end;
+        if (act && x == kLongCode) {
+            const uint32_t win = static_cast<uint32_t>((pair << (acc & 63u)) >> 32);
+            uint32_t len;
+            l = df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, n_luts, len));
+            x = (1u << 11) + len;
+        }
+        slo[first + j] = act ? l : 0u;
+        saux[first + j] = act ? x : 0u;
+        inc = act ? (x & 0xFFFFu) : inc;
+        acc += act ? (x & 0xFFFFu) : 0u;
+    }
+    if ((acc & 0xFFu) < end) {
+        spill = true;
+        for (;;) {
+            while ((acc & 0xFFu) < end) {
+                inc = lds_at<uint16_t>(s_aux, entry_offset<K>(pair, acc));
+                acc += inc;
+            }
+            if (!(acc & kLongCode)) break;
+            acc -= kLongCode;
+            const uint32_t win = static_cast<uint32_t>((pair << (acc & 63u)) >> 32);
+            uint32_t len;
+            walk_luts(win, s_luts[win >> 24], s_luts, s_clen, n_luts, len);
+            inc = (1u << 11) + len;
+            acc += inc;
+        }
+    }
+}
+
+// Phase 2 over one half without kept entries: the same lookups as phase 1,
+// each ORing its exponent run at the LDS address in acc2.
+template <int K>
+__device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_t &acc2, const uint32_t *s_lo,
+                                            const uint32_t *s_aux, const uint8_t *s_luts, const uint8_t *s_clen,
+                                            uint32_t n_luts) {
+    for (;;) {
+        while ((acc2 & 0xFFu) < end) {
+            // lo and aux are one paired LDS read.
+            const uint32_t off = entry_offset<K>(pair, acc2);
+            const uint32_t w = lds_at<uint32_t>(s_aux, off);
+            const uint32_t at = acc2;
+            acc2 += w & 0xFFFFu;
+            or_exponents(at, (static_cast<uint64_t>(w >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
+        }
+        if (!(acc2 & kLongCode)) break;
+        acc2 -= kLongCode;
+        const uint32_t win = static_cast<uint32_t>((pair << (acc2 & 63u)) >> 32);
+        uint32_t len;
+        or_exponents(acc2, df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, n_luts, len)));
+        acc2 += (1u << 11) + len;
+    }
+}
+
 // GPW groups of 256 threads share one workgroup (and one copy of the decode
 // tables in LDS).  Super-groups (GPW consecutive groups) are dealt to the
 // workgroups round-robin, so at any moment the whole grid reads and writes
@@ -279,16 +353,19 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
 // which HBM serves markedly faster.  (Neighbouring super-groups thus run on
 // different XCDs, since workgroup i goes to XCD i mod 8; grouping them per
 // XCD instead measured slower, as it splits the window into eight.)
-// Iteration i first merges and
-// stores the super-group decoded in iteration i - 1 (held in the other half
-// of a double-buffered LDS exponent buffer), then issues the loads of the
-// super-group of iteration i + 1, then decodes its own.  Every wait for loaded
-// data therefore comes a whole decode phase after the last stores were issued.
+// Iteration i first merges and stores the super-group decoded in iteration
+// i - 1 (reading and re-zeroing its LDS exponent buffer), then issues the
+// loads of the super-group of iteration i + 1, then decodes its own: phase 1,
+// the scan (whose barrier also orders the merge's reads before this
+// iteration's phase-2 writes, so one buffer per group suffices), phase 2 and a
+// barrier.  Every wait for loaded data therefore comes a whole decode phase
+// after the last stores were issued.  One buffer per group (rather than two)
+// keeps the LDS of a 512-thread workgroup small enough for four per CU.
 template <int K, int GPW>
 __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
-    // Static LDS: the first-level table (lo words | hi words | start masks) at a
-    // fixed address, so a lookup's address is its index times the entry size.
-    // Dynamic LDS: LUTs | CodeLengths | GPW x 2 exponent buffers | wave sums.
+    // Static LDS: the first-level table (lo words | aux words | start masks)
+    // at a fixed address, so a lookup's address is its index times 4.
+    // Dynamic LDS: LUTs | CodeLengths | GPW exponent buffers | wave sums.
     __shared__ __align__(16) uint32_t s_tab[(10u << K) / 4u];
     extern __shared__ __align__(16) uint8_t smem[];
     const uint32_t *s_lo = s_tab;
@@ -301,8 +378,8 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     const uint32_t ltid = tid % kThreadsPerGroup;
     const uint32_t lane = tid & (kWaveSize - 1);
     const uint32_t wave = ltid / kWaveSize;
-    uint8_t *s_ebuf2 = s_clen + 256u + slot * 2u * a.ebuf_cap;
-    uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * 2u * a.ebuf_cap) + slot * kWaves;
+    uint8_t *s_ebuf = s_clen + 256u + slot * a.ebuf_cap;
+    uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + slot * kWaves;
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint32_t n_wg = gridDim.x;
@@ -320,29 +397,47 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     uint64_t prev_sm[kPrefetchChunks] = {};
     uint32_t prev_base = 0, prev_end = 0;
 
-    // Stage the first-level table, the LUT hierarchy and CodeLengths.
+    // Stage the first-level table, the LUT hierarchy and CodeLengths.  Every
+    // load is issued before any of them is written to LDS, so staging costs
+    // one memory round trip rather than one per loop pass (the whole grid
+    // waits for it at the start of every launch).
     {
+        constexpr uint32_t kThreads = kThreadsPerGroup * GPW;
+        constexpr uint32_t kTabVecs = (10u << K) / 16u;
+        constexpr uint32_t kTabPer = (kTabVecs + kThreads - 1) / kThreads;
+        constexpr uint32_t kLutPer = (DF11_MAX_LUTS * 64u + kThreads - 1) / kThreads;
         const uint4 *src = reinterpret_cast<const uint4 *>(a.dtab);
-        uint4 *dst = reinterpret_cast<uint4 *>(s_tab);
-        for (uint32_t i = tid; i < (10u << K) / 16u; i += kThreadsPerGroup * GPW) dst[i] = src[i];
         const uint32_t *l32 = reinterpret_cast<const uint32_t *>(a.luts);
-        uint32_t *d32 = reinterpret_cast<uint32_t *>(s_luts);
-        for (uint32_t i = tid; i < a.n_luts * 64u; i += kThreadsPerGroup * GPW) d32[i] = l32[i];
-        if (tid < 64) reinterpret_cast<uint32_t *>(s_clen)[tid] = reinterpret_cast<const uint32_t *>(a.code_lengths)[tid];
+        const uint32_t lut_words = a.n_luts * 64u;
+        uint4 tv[kTabPer];
+        uint32_t lv[kLutPer];
+#pragma unroll
+        for (uint32_t j = 0; j < kTabPer; ++j) tv[j] = src[min(tid + j * kThreads, kTabVecs - 1u)];
+#pragma unroll
+        for (uint32_t j = 0; j < kLutPer; ++j) lv[j] = l32[min(tid + j * kThreads, lut_words - 1u)];
+        const uint32_t cv = reinterpret_cast<const uint32_t *>(a.code_lengths)[tid & 63u];
         // Phase 2 ORs exponents into the buffers, so they start out zero (and
         // the merge zeroes every chunk it consumes).
         uint4 *z = reinterpret_cast<uint4 *>(s_clen + 256u);
-        for (uint32_t i = tid; i < GPW * 2u * a.ebuf_cap / 16u; i += kThreadsPerGroup * GPW)
-            z[i] = make_uint4(0, 0, 0, 0);
+        for (uint32_t i = tid; i < GPW * a.ebuf_cap / 16u; i += kThreads) z[i] = make_uint4(0, 0, 0, 0);
+        // Unconditional stores (indices clamped like the loads: extra lanes
+        // write the last element's value to it again), so the compiler cannot
+        // sink each load into a branch next to its store.
+        uint4 *dst = reinterpret_cast<uint4 *>(s_tab);
+#pragma unroll
+        for (uint32_t j = 0; j < kTabPer; ++j) dst[min(tid + j * kThreads, kTabVecs - 1u)] = tv[j];
+        uint32_t *d32 = reinterpret_cast<uint32_t *>(s_luts);
+#pragma unroll
+        for (uint32_t j = 0; j < kLutPer; ++j) d32[min(tid + j * kThreads, lut_words - 1u)] = lv[j];
+        reinterpret_cast<uint32_t *>(s_clen)[tid & 63u] = cv;
     }
     __syncthreads();
 
     for (uint32_t it = 0; it < n_iter; ++it) {
         const uint32_t g = g_first + it * g_step;
-        uint8_t *s_ebuf = s_ebuf2 + (it & 1u) * a.ebuf_cap;
 
         // 1. Merge and store the super-group decoded in the previous iteration.
-        if (it > 0) merge_group(a, s_ebuf2 + ((it - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
+        if (it > 0) merge_group(a, s_ebuf, prev_sm, prev_base, prev_end, ltid);
 
         // 2. Loads of the next super-group (group numbers past the end are
         // clamped inside the loads and never decoded).
@@ -375,42 +470,23 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t end_a = min(seg_end, 32u);
         const uint32_t end_b = seg_end > 32u ? seg_end - 32u : 0u;
 
-        // Phase 1: count the codes that start in [gap, seg_end).  The fast
-        // loops only look up the table; a window whose first code is longer
-        // than K bits adds kLongCode to p, which ends the loop, and that code
-        // is finished through the LUT hierarchy before the loop resumes.
+        // Phase 1: walk the codes that start in [gap, seg_end) and count them.
+        // The first kSavedSteps lookups of each half keep their table entries
+        // (exponent run and increment) in registers, so that phase 2 only has
+        // to OR them into place; a lookup whose window starts with a code
+        // longer than K bits is finished through the LUT hierarchy and kept in
+        // the same form.  A lane with more lookups in a half finishes counting
+        // in a loop, and its wave then decodes phase 2 again from the stream.
+        uint32_t slo[2 * kSavedSteps], saux[2 * kSavedSteps];
         uint32_t acc = gap, inc = 0;
-        for (;;) {
-            while ((acc & 0xFFu) < end_a) {
-                inc = lds_at<uint16_t>(s_aux, entry_offset<K>(pa, acc));
-                acc += inc;
-            }
-            if (!(acc & kLongCode)) break;
-            acc -= kLongCode;
-            const uint32_t win = static_cast<uint32_t>((pa << (acc & 63u)) >> 32);
-            uint32_t len;
-            walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
-            inc = (1u << 11) + len;
-            acc += inc;
-        }
+        bool spill = false;
+        count_half<K>(pa, end_a, acc, inc, slo, saux, 0, spill, s_lo, s_aux, s_luts, s_clen, a.n_luts);
         uint32_t shift_back = 0;
         if (end_b) {
             acc -= 32u;
             shift_back = 32u;
-            for (;;) {
-                while ((acc & 0xFFu) < end_b) {
-                    inc = lds_at<uint16_t>(s_aux, entry_offset<K>(pb, acc));
-                    acc += inc;
-                }
-                if (!(acc & kLongCode)) break;
-                acc -= kLongCode;
-                const uint32_t win = static_cast<uint32_t>((pb << (acc & 63u)) >> 32);
-                uint32_t len;
-                walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len);
-                inc = (1u << 11) + len;
-                acc += inc;
-            }
         }
+        count_half<K>(pb, end_b, acc, inc, slo, saux, kSavedSteps, spill, s_lo, s_aux, s_luts, s_clen, a.n_luts);
         uint32_t cnt = acc >> 11;
         if (cnt) {
             // The last lookup, at p_last, may list codes that start at or
@@ -429,47 +505,28 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
         const uint32_t o_start = min(lead + wave_off + incl - cnt, a.ebuf_cap - kDecodeReach);
 
-        // Phase 2: decode the same lookups again and OR the (rotated) exponents
-        // into the zeroed LDS buffer at their output positions (accumulator x =
-        // LDS byte address).  A thread's last lookup may list codes that start
-        // past its segment; those are the next thread's first codes, decoded at
-        // the same code boundaries, so they land on the next thread's first
-        // outputs with the same values (or, after the group's last output, in
-        // the chunk the merge zeroes).
-        uint32_t acc2 = ((lds_offset(s_ebuf) + o_start) << 11) | gap;
-        for (;;) {
-            while ((acc2 & 0xFFu) < end_a) {
-                // lo and aux are one paired LDS read.
-                const uint32_t off = entry_offset<K>(pa, acc2);
-                const uint32_t w = lds_at<uint32_t>(s_aux, off);
-                const uint32_t at = acc2;
-                acc2 += w & 0xFFFFu;
-                or_exponents(at, (static_cast<uint64_t>(w >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
+        // Phase 2: OR the (rotated) exponents into the zeroed LDS buffer at
+        // their output positions (accumulator x = LDS byte address).  A
+        // thread's last lookup may list codes that start past its segment;
+        // those are the next thread's first codes, decoded at the same code
+        // boundaries, so they land on the next thread's first outputs with the
+        // same values (or, after the group's last output, in the chunk the
+        // merge zeroes).
+        if (!__builtin_amdgcn_ballot_w64(spill)) {
+            uint32_t acc2 = (lds_offset(s_ebuf) + o_start) << 11;
+#pragma unroll
+            for (int j = 0; j < 2 * kSavedSteps; ++j) {
+                if (!__builtin_amdgcn_ballot_w64(saux[j] != 0u)) continue;
+                or_exponents(acc2, (static_cast<uint64_t>(saux[j] >> 16) << 32) | slo[j]);
+                acc2 += saux[j] & 0xFFFFu;
             }
-            if (!(acc2 & kLongCode)) break;
-            acc2 -= kLongCode;
-            const uint32_t win = static_cast<uint32_t>((pa << (acc2 & 63u)) >> 32);
-            uint32_t len;
-            or_exponents(acc2, df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len)));
-            acc2 += (1u << 11) + len;
-        }
-        if (end_b) {
-            acc2 -= 32u;
-            for (;;) {
-                while ((acc2 & 0xFFu) < end_b) {
-                    const uint32_t off = entry_offset<K>(pb, acc2);
-                    const uint32_t w = lds_at<uint32_t>(s_aux, off);
-                    const uint32_t at = acc2;
-                    acc2 += w & 0xFFFFu;
-                    or_exponents(at, (static_cast<uint64_t>(w >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
-                }
-                if (!(acc2 & kLongCode)) break;
-                acc2 -= kLongCode;
-                const uint32_t win = static_cast<uint32_t>((pb << (acc2 & 63u)) >> 32);
-                uint32_t len;
-                or_exponents(acc2,
-                             df11::rotate_exponent(walk_luts(win, s_luts[win >> 24], s_luts, s_clen, a.n_luts, len)));
-                acc2 += (1u << 11) + len;
+        } else {
+            // Some lane needed more lookups than were kept: decode again.
+            uint32_t acc2 = ((lds_offset(s_ebuf) + o_start) << 11) | gap;
+            decode_half<K>(pa, end_a, acc2, s_lo, s_aux, s_luts, s_clen, a.n_luts);
+            if (end_b) {
+                acc2 -= 32u;
+                decode_half<K>(pb, end_b, acc2, s_lo, s_aux, s_luts, s_clen, a.n_luts);
             }
         }
         __syncthreads();
@@ -484,7 +541,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         nx_base = nn_base;
         nx_end = nn_end;
     }
-    merge_group(a, s_ebuf2 + ((n_iter - 1u) & 1u) * a.ebuf_cap, prev_sm, prev_base, prev_end, ltid);
+    merge_group(a, s_ebuf, prev_sm, prev_base, prev_end, ltid);
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -545,7 +602,7 @@ int resident_per_cu(int dev, size_t lds) {
 
 template <int K, int GPW>
 int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = a.n_luts * 256u + 256u + GPW * (2u * a.ebuf_cap + 4u * kWaves);  // beyond the static table
+    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves);  // beyond the static table
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
     int cus = 0;
