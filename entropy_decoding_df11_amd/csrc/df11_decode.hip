@@ -57,8 +57,9 @@ constexpr uint32_t kDefaultGroupsPerWorkgroup = 2;
 constexpr uint32_t kDecodeReach = 96;
 constexpr uint32_t kLongCode = df11::kLongCodeIncrement;
 // Table lookups per 32-bit half segment whose entries phase 1 keeps in
-// registers for phase 2 (LLM-like exponent streams need 3..5 at K = 11).
-constexpr int kSavedSteps = 6;
+// registers for phase 2 (LLM-like exponent streams need 3..5 at K = 11; a
+// wave that needs more decodes phase 2 again from the stream).
+constexpr int kSavedSteps = 5;
 
 struct DecodeArgs {
     const uint8_t *enc;
@@ -187,7 +188,7 @@ __device__ __forceinline__ uint32_t out_pos_at(const DecodeArgs &a, uint32_t g) 
     return ((const ConstU32 *)a.out_pos)[min(g, a.n_groups)];
 }
 
-__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
 
 // Number of 8-element chunks that hold the outputs [base, end).
 __device__ __forceinline__ uint32_t group_chunks(uint32_t base, uint32_t end) {
@@ -199,35 +200,40 @@ __device__ __forceinline__ uint32_t group_chunks(uint32_t base, uint32_t end) {
 // group's inputs are loaded before the previous group's stores are issued:
 // waiting for them then does not wait for those stores.
 struct GroupLoad {
-    uint32_t e0, e1, e2;           // the thread's EncodedExponent words (bytes 8t .. 8t+11)
+    uint32_t e0, e1, e2, e3;       // the thread's EncodedExponent words (bytes 8t .. 8t+15)
     uint32_t g0, g1;               // the two Gaps words that hold its 5 bits
-    uint64_t sm[kPrefetchChunks];  // sign/mantissa chunks ltid + 256 j of the group
 };
 
 // Issues the same loads for every group (addresses clamped into the buffers,
 // values of out-of-range items unused) so that the number of operations in
 // flight is the same on every path.
-__device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g, uint32_t ltid, uint32_t base,
-                                                uint32_t end) {
+__device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g, uint32_t ltid) {
     GroupLoad r;
     const uint32_t t = min(g * kThreadsPerGroup + ltid, a.n_threads - 1u);
     const uint32_t *e32 = reinterpret_cast<const uint32_t *>(a.enc + 8ull * t);
     r.e0 = e32[0];
     r.e1 = e32[1];
     r.e2 = e32[2];
+    r.e3 = e32[3];
     const uint64_t gbit = 5ull * t;
     const uint32_t *g32 = reinterpret_cast<const uint32_t *>(a.gaps) + (gbit >> 5);
     r.g0 = g32[0];
     r.g1 = g32[1];
+    return r;
+}
+
+// Sign/mantissa chunks ltid + 256 j of the group with outputs [base, end),
+// loaded (clamped like load_group) one iteration before the merge uses them.
+__device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
+                                        uint64_t (&sm)[kPrefetchChunks]) {
     const uint32_t c0 = base >> 3;
     const uint32_t nch = group_chunks(base, end);
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
         const uint32_t k = ltid + j * kThreadsPerGroup;
         const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
-        r.sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
+        sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
     }
-    return r;
 }
 
 // Byte offset of the first-level table entry (one uint32 per entry in each
@@ -250,10 +256,16 @@ __device__ __forceinline__ uint32_t window_at(uint64_t pa, uint64_t pb, uint32_t
 // Merge one decoded group's exponents with its sign/mantissa bytes and store
 // BF16.  LDS byte 8k + i of the group's buffer holds element 8 (base/8 + k) + i;
 // every chunk read is zeroed again for the next group that uses the buffer.
+// skip_first: the previous group's workgroup wrote the chunk this group shares
+// with it; whole_last: this group's buffer also holds the next group's
+// elements of their shared chunk, which is written whole.
 __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, const uint64_t (&sm)[kPrefetchChunks],
-                                            uint32_t base, uint32_t end, uint32_t ltid) {
+                                            uint32_t base, uint32_t end, uint32_t ltid, bool skip_first,
+                                            bool whole_last) {
     const uint32_t c0 = base >> 3;
     const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
+    const uint32_t store_base = skip_first ? (base + 7u) & ~7u : base;
+    const uint32_t store_end = whole_last ? (end + 7u) & ~7u : end;
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
         const uint32_t k = ltid + j * kThreadsPerGroup;
@@ -261,7 +273,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
             uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
             const uint64_t r8 = *cell;
             *cell = 0;
-            store_chunk(a.out, c0 + k, merge8(sm[j], r8), base, end);
+            store_chunk(a.out, c0 + k, merge8(sm[j], r8), store_base, store_end);
         }
     }
     for (uint32_t k = ltid + kPrefetchChunks * kThreadsPerGroup; k < n_chunks; k += kThreadsPerGroup) {
@@ -269,10 +281,56 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
         uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
         const uint64_t r8 = *cell;
         *cell = 0;
-        store_chunk(a.out, c0 + k, merge8(s8, r8), base, end);
+        store_chunk(a.out, c0 + k, merge8(s8, r8), store_base, store_end);
     }
     // Codes past the group's last output reach at most 4 bytes into the next chunk.
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+}
+
+// Group edges.  When a group's first element is not a multiple of 8, the
+// group shares an 8-element output chunk with the previous group; stored
+// separately, each half of it would be a partial write of one cache line from
+// each of two workgroups.  Instead the previous group's workgroup writes the
+// whole chunk, decoding the c codes that open the group (c = elements of the
+// group in that chunk), when they can be decoded from the first 64 bits of the
+// group's first segment: the c-th code ends at or before bit 64 - K (so every
+// K-bit window used lies in those bits) and none of them is longer than K
+// bits.  The previous group's last thread holds those 64 bits as its third and
+// fourth words and the group's first thread as its first two; both evaluate
+// the rule from the stream alone, so they agree without communicating.
+//
+// boundary_codes walks from bit q of the pair, a code start preceded by `cum`
+// of the c codes, and returns whether the rule holds; with write set it also
+// ORs each lookup's exponents at the LDS accumulator acc2.
+template <int K>
+__device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32_t cum, uint32_t c, uint32_t acc2,
+                                               bool write, const uint32_t *s_lo, const uint32_t *s_aux,
+                                               const uint16_t *s_start) {
+    constexpr uint32_t kLastEnd = 64u - K;
+    while (cum < c) {
+        if (q > kLastEnd) return false;
+        const uint32_t off = entry_offset<K>(pair, q);
+        const uint32_t x = lds_at<uint32_t>(s_aux, off);
+        if (x == kLongCode) return false;
+        const uint32_t m = (x >> 11) & 7u;
+        if (write) or_exponents(acc2, (static_cast<uint64_t>(x >> 16) << 32) | lds_at<uint32_t>(s_lo, off));
+        if (cum + m >= c) {
+            // End of the c-th code: the next listed code's start, or the end
+            // of the listed run.
+            const uint32_t j = c - cum;
+            uint32_t code_end = q + (x & 0xFFu);
+            if (j < m) {
+                uint32_t starts = lds_at<uint16_t>(s_start, off >> 1);
+                for (uint32_t i = 0; i < j; ++i) starts &= starts - 1u;
+                code_end = q + __builtin_ctz(starts);
+            }
+            return code_end <= kLastEnd;
+        }
+        acc2 += m << 11;
+        cum += m;
+        q += x & 0xFFu;
+    }
+    return true;
 }
 
 // Phase 1 over one half of a segment: table lookups from bit p = acc & 0xFF
@@ -380,6 +438,9 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     const uint32_t wave = ltid / kWaveSize;
     uint8_t *s_ebuf = s_clen + 256u + slot * a.ebuf_cap;
     uint32_t *s_wsum = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + slot * kWaves;
+    // Per group: [0] the previous group wrote the shared first chunk, [1] this
+    // group's last chunk is written whole (see boundary_codes).
+    uint32_t *s_edge = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * kWaves + slot * 2u;
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint32_t n_wg = gridDim.x;
@@ -387,14 +448,14 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     if (wg >= n_super) return;  // whole workgroup
     const uint32_t n_iter = (n_super - wg + n_wg - 1) / n_wg;
 
-    // Pipeline state: out_pos two super-groups ahead (scalar), thread inputs
-    // one ahead, sign/mantissa bytes of the group waiting to be merged.
+    // Pipeline state: the group's output range (scalar) and thread inputs one
+    // super-group ahead; the sign/mantissa chunks of the group waiting to be
+    // merged.
     const uint32_t g_first = wg * GPW + slot;
     const uint32_t g_step = n_wg * GPW;
     uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
-    uint32_t nx_base = out_pos_at(a, g_first + g_step), nx_end = out_pos_at(a, g_first + g_step + 1);
-    GroupLoad cur = load_group(a, g_first, ltid, cur_base, cur_end);
-    uint64_t prev_sm[kPrefetchChunks] = {};
+    GroupLoad cur = load_group(a, g_first, ltid);
+    uint64_t sm[kPrefetchChunks] = {};  // the previous group's, until the merge, then this group's
     uint32_t prev_base = 0, prev_end = 0;
 
     // Stage the first-level table, the LUT hierarchy and CodeLengths.  Every
@@ -437,18 +498,21 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t g = g_first + it * g_step;
 
         // 1. Merge and store the super-group decoded in the previous iteration.
-        if (it > 0) merge_group(a, s_ebuf, prev_sm, prev_base, prev_end, ltid);
+        if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
 
-        // 2. Loads of the next super-group (group numbers past the end are
-        // clamped inside the loads and never decoded).
-        const uint32_t g_nn = min(g + 2u * g_step, a.n_groups);
-        const uint32_t nn_base = out_pos_at(a, g_nn), nn_end = out_pos_at(a, g_nn + 1);
-        const GroupLoad nx = load_group(a, min(g + g_step, a.n_groups), ltid, uniform(nx_base), uniform(nx_end));
+        // 2. Loads: the next super-group's thread inputs and output range
+        // (group numbers past the end are clamped inside the loads and never
+        // decoded), and this group's sign/mantissa chunks for the next
+        // iteration's merge.  The output range is clamped so that a corrupt
+        // out_pos stays in bounds.
+        const uint32_t end = min(cur_end, a.n_elements);
+        const uint32_t base = min(cur_base, end);
+        const uint32_t g_nx = min(g + g_step, a.n_groups);
+        const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
+        const GroupLoad nx = load_group(a, g_nx, ltid);
+        load_sm(a, base, end, ltid, sm);
 
-        // 3. Decode this super-group.  Output range of the group, clamped so a
-        // corrupt out_pos stays in bounds.
-        const uint32_t end = min(uniform(cur_end), a.n_elements);
-        const uint32_t base = min(uniform(cur_base), end);
+        // 3. Decode this super-group.
         const uint32_t lead = base & 7u;
 
         const uint32_t t = g * kThreadsPerGroup + ltid;
@@ -459,7 +523,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
             gap = static_cast<uint32_t>((gw << (gbit & 31)) >> 59);
             seg_end = t + 1 < a.n_threads ? kSegBits : a.last_seg_bits;
         }
-        const uint32_t w0 = bswap32(cur.e0), w1 = bswap32(cur.e1), w2 = bswap32(cur.e2);
+        const uint32_t w0 = bswap32(cur.e0), w1 = bswap32(cur.e1), w2 = bswap32(cur.e2), w3 = bswap32(cur.e3);
         // Lookups that start in bits [0, 32) of the segment read the pair w0 w1
         // and those that start later read w1 w2, each with one 64-bit shift by
         // the start bit: a code read from bit p < 32 plus the K-bit window ends
@@ -487,13 +551,14 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
             shift_back = 32u;
         }
         count_half<K>(pb, end_b, acc, inc, slo, saux, kSavedSteps, spill, s_lo, s_aux, s_luts, s_clen, a.n_luts);
-        uint32_t cnt = acc >> 11;
+        uint32_t cnt = acc >> 11, past = 0;
         if (cnt) {
             // The last lookup, at p_last, may list codes that start at or
             // after seg_end; its start mask says how many.
             const uint32_t p_last = (acc + shift_back - inc) & 0xFFu;
             const uint32_t mask = s_start[window_at(pa, pb, p_last) >> (32 - K)];
-            cnt -= __popc(mask >> min(seg_end - p_last, 31u));
+            past = __popc(mask >> min(seg_end - p_last, 31u));
+            cnt -= past;
         }
 
         // Offsets within the group.
@@ -512,8 +577,9 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         // boundaries, so they land on the next thread's first outputs with the
         // same values (or, after the group's last output, in the chunk the
         // merge zeroes).
+        uint32_t acc2;
         if (!__builtin_amdgcn_ballot_w64(spill)) {
-            uint32_t acc2 = (lds_offset(s_ebuf) + o_start) << 11;
+            acc2 = (lds_offset(s_ebuf) + o_start) << 11;
 #pragma unroll
             for (int j = 0; j < 2 * kSavedSteps; ++j) {
                 if (!__builtin_amdgcn_ballot_w64(saux[j] != 0u)) continue;
@@ -522,26 +588,43 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
             }
         } else {
             // Some lane needed more lookups than were kept: decode again.
-            uint32_t acc2 = ((lds_offset(s_ebuf) + o_start) << 11) | gap;
+            acc2 = ((lds_offset(s_ebuf) + o_start) << 11) | gap;
             decode_half<K>(pa, end_a, acc2, s_lo, s_aux, s_luts, s_clen, a.n_luts);
             if (end_b) {
                 acc2 -= 32u;
                 decode_half<K>(pb, end_b, acc2, s_lo, s_aux, s_luts, s_clen, a.n_luts);
             }
         }
+
+        // Group edges (see boundary_codes).  acc2 now addresses the byte after
+        // the last code this thread listed, `past` of which opened the next
+        // segment, which ends this thread's phase-1 walk at bit p_end.
+        if (ltid == kThreadsPerGroup - 1u) {
+            bool whole = false;
+            const uint32_t c = (8u - (end & 7u)) & 7u;
+            if (g + 2u < a.n_groups && c) {
+                const uint32_t p_end = (acc & 0xFFu) + shift_back;
+                whole = boundary_codes<K>((static_cast<uint64_t>(w2) << 32) | w3, p_end - kSegBits, past, c, acc2,
+                                          true, s_lo, s_aux, s_start);
+            }
+            s_edge[1] = whole;
+        }
+        if (ltid == 0) {
+            bool skip = false;
+            const uint32_t c = (8u - (base & 7u)) & 7u;
+            if (g >= 1u && g + 1u < a.n_groups && c)
+                skip = boundary_codes<K>(pa, gap, 0, c, 0, false, s_lo, s_aux, s_start);
+            s_edge[0] = skip;
+        }
         __syncthreads();
 
-#pragma unroll
-        for (int j = 0; j < kPrefetchChunks; ++j) prev_sm[j] = cur.sm[j];
         prev_base = base;
         prev_end = end;
         cur = nx;
         cur_base = nx_base;
         cur_end = nx_end;
-        nx_base = nn_base;
-        nx_end = nn_end;
     }
-    merge_group(a, s_ebuf, prev_sm, prev_base, prev_end, ltid);
+    merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -602,7 +685,7 @@ int resident_per_cu(int dev, size_t lds) {
 
 template <int K, int GPW>
 int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves);  // beyond the static table
+    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u);  // beyond the static table
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
     int cus = 0;
