@@ -24,6 +24,7 @@ STATUS_NAMES = {
     -8: "DF11_E_HIP",
 }
 MAX_LUTS = 17
+SCHEDULE_WORDS = 144  # DF11_SCHEDULE_WORDS
 
 # Every function the header declares; the ABI test checks each is exported.
 EXPORTED = [
@@ -93,6 +94,7 @@ class DeviceStream(ctypes.Structure):
         ("decode_table", ctypes.c_void_p),
         ("decode_table_bits", ctypes.c_uint32),
         ("groups_per_workgroup", ctypes.c_uint32),
+        ("schedule", ctypes.c_void_p),
     ]
 
 

@@ -79,6 +79,7 @@ struct DecodeArgs {
     uint32_t last_seg_bits;  // payload bits in the last thread's segment (1..64)
     uint32_t sm_chunks;      // 8-byte chunks in the PackedSignMantissa buffer
     uint32_t pad;
+    uint32_t *sched;         // work counter (dynamic schedule) or null
 };
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
@@ -333,6 +334,37 @@ __device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32
     return true;
 }
 
+// Dynamic schedule.  Workgroups run at different speeds (a CU favours its
+// oldest waves), so after three static rounds (super-groups wg, wg + grid,
+// wg + 2 grid) each workgroup takes its next super-groups from one of eight
+// pools: pool x = wg mod 8 hands out 3 grid + x + 8 v for v = 0, 1, ... from
+// its own counter, so that the ticket fetches of the whole grid are spread
+// over eight addresses (one address would serialise them).  Thread 0 fetches
+// a ticket every iteration, three iterations before the loads that need it,
+// and hands it to the other waves through LDS.  A workgroup's tickets
+// increase, so it stops at its first ticket past the end having processed
+// every earlier one.  On exit every workgroup counts itself in the done word;
+// the last one zeroes every word for the next launch.
+constexpr uint32_t kPools = 8;
+constexpr uint64_t kDynamicMinRounds = 12;
+constexpr uint32_t kPoolStride = DF11_SCHEDULE_WORDS / (kPools + 1);  // words: one cache line per counter
+
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *sched, uint32_t pool) {
+    return __hip_atomic_fetch_add(sched + pool * kPoolStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void finish_schedule(uint32_t *sched, uint32_t n_wg) {
+    if (!sched || threadIdx.x != 0) return;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's ticket fetches are complete
+    uint32_t *done_word = sched + kPools * kPoolStride;
+    const uint32_t done = __hip_atomic_fetch_add(done_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == n_wg - 1u) {
+        for (uint32_t x = 0; x < kPools; ++x)
+            __hip_atomic_store(sched + x * kPoolStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Phase 1 over one half of a segment: table lookups from bit p = acc & 0xFF
 // of the 64-bit pair while p < end, advancing acc by each increment (inc keeps
 // the last one).  The entries of the first kSavedSteps lookups go to
@@ -441,18 +473,22 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     // Per group: [0] the previous group wrote the shared first chunk, [1] this
     // group's last chunk is written whole (see boundary_codes).
     uint32_t *s_edge = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * kWaves + slot * 2u;
+    // The next super-group of the dynamic schedule, from thread 0.
+    uint32_t *s_ticket = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * (kWaves + 2u);
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint32_t n_wg = gridDim.x;
     const uint32_t wg = blockIdx.x;
-    if (wg >= n_super) return;  // whole workgroup
-    const uint32_t n_iter = (n_super - wg + n_wg - 1) / n_wg;
+    uint32_t *const sched = a.sched;
+    if (wg >= n_super) {  // whole workgroup
+        finish_schedule(sched, n_wg);
+        return;
+    }
 
     // Pipeline state: the group's output range (scalar) and thread inputs one
     // super-group ahead; the sign/mantissa chunks of the group waiting to be
     // merged.
     const uint32_t g_first = wg * GPW + slot;
-    const uint32_t g_step = n_wg * GPW;
     uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
     GroupLoad cur = load_group(a, g_first, ltid);
     uint64_t sm[kPrefetchChunks] = {};  // the previous group's, until the merge, then this group's
@@ -494,8 +530,13 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     }
     __syncthreads();
 
-    for (uint32_t it = 0; it < n_iter; ++it) {
-        const uint32_t g = g_first + it * g_step;
+    uint32_t s_cur = wg, ticket = 0;
+    for (uint32_t it = 0; s_cur < n_super; ++it) {
+        const uint32_t g = s_cur * GPW + slot;
+        // Rounds 0..2 are static; the ticket for round it + 1 >= 3 was
+        // written to LDS in iteration it - 1.
+        const uint32_t s_nx =
+            (sched && it >= 2u) ? __builtin_amdgcn_readfirstlane(*s_ticket) : min(s_cur + n_wg, n_super);
 
         // 1. Merge and store the super-group decoded in the previous iteration.
         if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
@@ -507,10 +548,12 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         // out_pos stays in bounds.
         const uint32_t end = min(cur_end, a.n_elements);
         const uint32_t base = min(cur_base, end);
-        const uint32_t g_nx = min(g + g_step, a.n_groups);
+        const uint32_t g_nx = min(s_nx * GPW + slot, a.n_groups);
         const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
         const GroupLoad nx = load_group(a, g_nx, ltid);
         load_sm(a, base, end, ltid, sm);
+        uint32_t fetched = 0;
+        if (sched && tid == 0) fetched = take_ticket(sched, wg % kPools);  // for round it + 3
 
         // 3. Decode this super-group.
         const uint32_t lead = base & 7u;
@@ -569,6 +612,9 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
         const uint32_t o_start = min(lead + wave_off + incl - cnt, a.ebuf_cap - kDecodeReach);
+        // Round it + 2's ticket (fetched last iteration) for the other waves;
+        // they read it after the next barrier, at the top of iteration it + 1.
+        if (sched && tid == 0 && it >= 1u) *s_ticket = 3u * n_wg + wg % kPools + kPools * ticket;
 
         // Phase 2: OR the (rotated) exponents into the zeroed LDS buffer at
         // their output positions (accumulator x = LDS byte address).  A
@@ -623,8 +669,11 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         cur = nx;
         cur_base = nx_base;
         cur_end = nx_end;
+        ticket = fetched;
+        s_cur = s_nx;
     }
     merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+    finish_schedule(sched, n_wg);
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -649,7 +698,8 @@ int validate(const df11_device_stream *s) {
     if (!s->enc || !s->sm || !s->gaps || !s->out_pos || !s->luts || !s->code_lengths || !s->decode_table)
         return DF11_E_INVALID_ARG;
     if (!aligned(s->enc, 16) || !aligned(s->sm, 16) || !aligned(s->gaps, 4) || !aligned(s->out_pos, 4) ||
-        !aligned(s->luts, 4) || !aligned(s->code_lengths, 4) || !aligned(s->decode_table, 16))
+        !aligned(s->luts, 4) || !aligned(s->code_lengths, 4) || !aligned(s->decode_table, 16) ||
+        (s->schedule && !aligned(s->schedule, 4)))
         return DF11_E_INVALID_ARG;
     if (h.n_luts < 1 || h.n_luts > DF11_MAX_LUTS || h.max_len < 1 || h.max_len > DF11_MAX_CODE_LEN)
         return DF11_E_BAD_STREAM;
@@ -685,7 +735,7 @@ int resident_per_cu(int dev, size_t lds) {
 
 template <int K, int GPW>
 int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u);  // beyond the static table
+    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u;  // beyond the static table
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
     int cus = 0;
@@ -697,6 +747,9 @@ int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_super, resident));
     (void)hipGetLastError();
     DecodeArgs args = a;
+    // The dynamic schedule pays a few microseconds of ticket and exit
+    // latency; it wins only when each workgroup has many rounds to balance.
+    if (n_super < kDynamicMinRounds * static_cast<uint64_t>(grid)) args.sched = nullptr;
     void *params[] = {&args};
     // hipExtLaunchKernel records start / stop (when given) at the kernel's own
     // start and end, not around the launch.
@@ -727,7 +780,8 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     if (overlaps(out, out_bytes, s->enc, h.enc_bytes) || overlaps(out, out_bytes, s->sm, h.sm_bytes) ||
         overlaps(out, out_bytes, s->gaps, h.gaps_bytes) || overlaps(out, out_bytes, s->out_pos, h.out_pos_bytes) ||
         overlaps(out, out_bytes, s->luts, 256ull * h.n_luts) || overlaps(out, out_bytes, s->code_lengths, 256) ||
-        overlaps(out, out_bytes, s->decode_table, df11_decode_table_bytes(bits)))
+        overlaps(out, out_bytes, s->decode_table, df11_decode_table_bytes(bits)) ||
+        overlaps(out, out_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
         return DF11_E_INVALID_ARG;
 
     DecodeArgs a{};
@@ -749,6 +803,7 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     a.ebuf_cap = static_cast<uint32_t>(round_up(static_cast<uint64_t>(h.max_group_elems) + 8 + kDecodeReach, 16));
     a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
     a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
+    a.sched = s->schedule;
     const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
     switch (bits) {
     case 10: return launch_k<10>(a, gpw, stream, start, stop);

@@ -168,7 +168,16 @@ class DF11Tensor:
             setattr(s, name, t.data_ptr())
         s.decode_table_bits = decode_table_bits
         s.groups_per_workgroup = groups_per_workgroup
+        # The kernel's work counter for dynamic load balancing (zero between
+        # launches).  Launches of one DF11Tensor must not overlap in time.
+        self._schedule = torch.zeros(_lib.SCHEDULE_WORDS, dtype=torch.int32, device=self.device)
+        s.schedule = self._schedule.data_ptr()
         self._stream_struct = s
+
+    def set_dynamic_schedule(self, on: bool) -> None:
+        """Balance work between workgroups at run time (default) or assign it
+        statically."""
+        self._stream_struct.schedule = self._schedule.data_ptr() if on else None
 
     def set_groups_per_workgroup(self, gpw: int) -> None:
         """Launch shape: groups decoded together by one workgroup (0 = default, 1, 2, 4)."""

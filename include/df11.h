@@ -54,6 +54,9 @@ typedef enum df11_status {
 #define DF11_MAX_LUTS 17
 /* Longest code; Gaps hold 5-bit offsets in [0, 31]. */
 #define DF11_MAX_CODE_LEN 32
+/* Size, in uint32 words, of the dynamic-schedule work counters
+ * (df11_device_stream.schedule). */
+#define DF11_SCHEDULE_WORDS 144
 
 /* The codebook shared by all tensors of one stream (host, plain data).
  *   code_lengths[e]: Huffman code length of exponent e, 0 if unused
@@ -120,7 +123,16 @@ typedef struct df11_header {
  *                                        built by df11_build_decode_table
  *   decode_table_bits                    index width of decode_table (10..12)
  *   groups_per_workgroup                 launch shape: groups decoded together by one
- *                                        workgroup (1, 2 or 4); 0 picks the default */
+ *                                        workgroup (1, 2 or 4); 0 picks the default
+ *   schedule     device, DF11_SCHEDULE_WORDS uint32, or NULL
+ *                                        work counters for dynamic load balancing:
+ *                                        zero-filled by the caller once; every
+ *                                        launch leaves them zero again.  Launches
+ *                                        that share one must not overlap in time
+ *                                        (use one per stream of work).  NULL
+ *                                        selects a static schedule, which is
+ *                                        also used for streams too short to
+ *                                        gain from balancing. */
 typedef struct df11_device_stream {
     df11_header h;
     const uint8_t *enc;
@@ -132,6 +144,7 @@ typedef struct df11_device_stream {
     const void *decode_table;
     uint32_t decode_table_bits;
     uint32_t groups_per_workgroup;
+    uint32_t *schedule;
 } df11_device_stream;
 
 /* Accumulate the 256-bin exponent histogram of n BF16 words (host).

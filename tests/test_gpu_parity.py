@@ -157,3 +157,46 @@ def test_empty_and_repeat_and_side_stream(torch_cuda):
     side.synchronize()
     for o in outs:
         assert np.array_equal(_to_u16(o), w)
+
+
+@pytest.mark.parametrize("dynamic", [True, False])
+def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
+    """Dynamic load balancing hands super-groups out from device counters;
+    every launch must leave them zero, and back-to-back launches must all be
+    bit-exact.  The stream (64M weights with ~6-bit exponent codes, ~23K
+    groups) is long enough for the dynamic schedule at two groups per
+    workgroup; one group per workgroup, four, and the static schedule must
+    give the same bytes."""
+    torch = torch_cuda
+    w = _case("uniform_bits", 64 << 20, 11)
+    _note(f"schedule dynamic={dynamic}")
+    t = df11.compress(w, shape=(w.size,), decode_table_bits=11)
+    assert t.header.n_groups >= 2 * 12 * 768
+    t.set_dynamic_schedule(dynamic)
+    for gpw in (2, 1, 4):
+        t.set_groups_per_workgroup(gpw)
+        outs = []
+        for _ in range(3):
+            out = torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            outs.append(t.decompress(out=out))
+        torch.cuda.synchronize()
+        for o in outs:
+            assert np.array_equal(_to_u16(o), w), gpw
+        assert not t._schedule.cpu().numpy().any()
+        del outs
+
+
+@pytest.mark.parametrize("bits", [10, 11, 12])
+def test_timed_entry_point_matches(torch_cuda, bits):
+    """df11_decompress_timed decodes the same bytes and records the kernel's
+    own start and end in the caller's events."""
+    torch = torch_cuda
+    w = _case("normal", 1_500_003, bits)
+    _note(f"timed bits={bits}")
+    t = df11.compress(w, shape=(w.size,), decode_table_bits=bits)
+    out = torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t.decompress(out=out, events=ev)
+    torch.cuda.synchronize()
+    assert np.array_equal(_to_u16(out), w)
+    assert ev[0].elapsed_time(ev[1]) > 0

@@ -272,3 +272,10 @@ def test_decode_table_matches_code_table(workload, bits, case):
         assert a >> 24 == 0
         got = [(int(lo[x]) >> (8 * j)) & 0xFF for j in range(4)] + [(a >> 16) & 0xFF]
         assert got == [rot(s) for s in syms] + [0] * (5 - len(syms))
+
+
+def test_schedule_words_constant_matches_header():
+    import re
+    with open(os.path.join(os.path.dirname(__file__), "..", "include", "df11.h")) as f:
+        m = re.search(r"#define\s+DF11_SCHEDULE_WORDS\s+(\d+)", f.read())
+    assert m and int(m.group(1)) == _lib.SCHEDULE_WORDS
