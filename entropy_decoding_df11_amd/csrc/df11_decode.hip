@@ -443,9 +443,10 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 // which HBM serves markedly faster.  (Neighbouring super-groups thus run on
 // different XCDs, since workgroup i goes to XCD i mod 8; grouping them per
 // XCD instead measured slower, as it splits the window into eight.)
-// Iteration i first merges and stores the super-group decoded in iteration
-// i - 1 (reading and re-zeroing its LDS exponent buffer), then issues the
-// loads of the super-group of iteration i + 1, then decodes its own: phase 1,
+// Iteration i first issues the loads of the super-group of iteration i + 1,
+// then merges and stores the super-group decoded in iteration i - 1 (reading
+// and re-zeroing its LDS exponent buffer) and loads its own sign/mantissa
+// chunks for that merge in the next iteration, then decodes its own: phase 1,
 // the scan (whose barrier also orders the merge's reads before this
 // iteration's phase-2 writes, so one buffer per group suffices), phase 2 and a
 // barrier.  Every wait for loaded data therefore comes a whole decode phase
@@ -538,22 +539,23 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t s_nx =
             (sched && it >= 2u) ? __builtin_amdgcn_readfirstlane(*s_ticket) : min(s_cur + n_wg, n_super);
 
-        // 1. Merge and store the super-group decoded in the previous iteration.
-        if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
-
-        // 2. Loads: the next super-group's thread inputs and output range
+        // 1. Loads of the next super-group's thread inputs and output range
         // (group numbers past the end are clamped inside the loads and never
-        // decoded), and this group's sign/mantissa chunks for the next
-        // iteration's merge.  The output range is clamped so that a corrupt
-        // out_pos stays in bounds.
+        // decoded), issued first so that they are in flight longest.  The
+        // output range is clamped so that a corrupt out_pos stays in bounds.
         const uint32_t end = min(cur_end, a.n_elements);
         const uint32_t base = min(cur_base, end);
         const uint32_t g_nx = min(s_nx * GPW + slot, a.n_groups);
         const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
         const GroupLoad nx = load_group(a, g_nx, ltid);
-        load_sm(a, base, end, ltid, sm);
         uint32_t fetched = 0;
         if (sched && tid == 0) fetched = take_ticket(sched, wg % kPools);  // for round it + 3
+
+        // 2. Merge and store the super-group decoded in the previous
+        // iteration, then load this group's sign/mantissa chunks (into the
+        // registers the merge has just consumed) for the next one.
+        if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+        load_sm(a, base, end, ltid, sm);
 
         // 3. Decode this super-group.
         const uint32_t lead = base & 7u;
