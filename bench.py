@@ -215,18 +215,22 @@ def main() -> int:
     scratch = torch.empty(n, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
-        blk.decompress(scratch=scratch)
+    # Check the decode first: the copy back and the comparison leave the GPU
+    # idle long enough for its clocks to drop, which the warmup then undoes.
+    blk.decompress(scratch=scratch)
     torch.cuda.synchronize()
     got = scratch.view(torch.int16).cpu().numpy().view(np.uint16)
     if not np.array_equal(got, flat):
         print("bench: decoded block differs from the original weights", file=sys.stderr)
         return 1
+    del got
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for e in starts + ends:  # create the events outside the timed region
         e.record(stream)
+    for _ in range(args.warmup):
+        blk.decompress(scratch=scratch)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -234,6 +238,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if not np.array_equal(scratch.view(torch.int16).cpu().numpy().view(np.uint16), flat):
+        print("bench: the timed launches decoded the block wrongly", file=sys.stderr)
+        return 1
     mean_ms = float(np.mean(kern_ms))
     achieved = algo_bytes / (mean_ms * 1e-3) / 1e9
     value = args.steps * algo_bytes / wall / 1e9

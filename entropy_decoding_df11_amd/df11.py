@@ -261,6 +261,7 @@ class DF11Block:
     def __init__(self, tensor: DF11Tensor, views: List[Tuple[str, int, Tuple[int, ...]]]):
         self.tensor = tensor
         self.views = views
+        self._view_cache = (None, None)  # (scratch tensor, its views)
 
     @property
     def n_elements(self) -> int:
@@ -285,8 +286,12 @@ class DF11Block:
             lib = _lib.load()
             _lib.check(lib.df11_decompress_block(ctypes.byref(t.device_stream()), ctypes.c_void_p(scratch.data_ptr()),
                                                  scratch.numel(), t._hip_stream(stream)), "df11_decompress_block")
-        flat = scratch.reshape(-1)
-        return {name: flat[off:off + int(np.prod(shape))].view(shape) for name, off, shape in self.views}
+        cached, views = self._view_cache
+        if cached is not scratch:  # the views of a scratch buffer are built once
+            flat = scratch.reshape(-1)
+            views = {name: flat[off:off + int(np.prod(shape))].view(shape) for name, off, shape in self.views}
+            self._view_cache = (scratch, views)
+        return views
 
 
 def compress_block(weights: Union[Dict[str, ArrayLike], List[Tuple[str, ArrayLike]]], device="cuda",
