@@ -25,6 +25,7 @@ STATUS_NAMES = {
 }
 MAX_LUTS = 17
 SCHEDULE_WORDS = 144  # DF11_SCHEDULE_WORDS
+MAX_BATCH = 16  # DF11_MAX_BATCH
 
 # Every function the header declares; the ABI test checks each is exported.
 EXPORTED = [
@@ -36,6 +37,7 @@ EXPORTED = [
     "df11_build_decode_table",
     "df11_decompress",
     "df11_decompress_block",
+    "df11_decompress_batch",
     "df11_decompress_timed",
     "df11_status_str",
 ]
@@ -131,6 +133,8 @@ def load() -> ctypes.CDLL:
         "df11_decompress": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p]),
         "df11_decompress_block": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint64,
                                                  ctypes.c_void_p]),
+        "df11_decompress_batch": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
         "df11_decompress_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_void_p]),
         "df11_status_str": (ctypes.c_char_p, [ctypes.c_int]),

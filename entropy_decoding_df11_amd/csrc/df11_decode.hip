@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <numeric>
 
 #include <stdint.h>
 #include <string.h>
@@ -79,7 +80,9 @@ struct DecodeArgs {
     uint32_t last_seg_bits;  // payload bits in the last thread's segment (1..64)
     uint32_t sm_chunks;      // 8-byte chunks in the PackedSignMantissa buffer
     uint32_t pad;
-    uint32_t *sched;         // work counter (dynamic schedule) or null
+    uint32_t *sched;         // work counters (dynamic schedule) or null
+    uint32_t pools;          // dynamic schedule: counters in use, dividing the workgroup count
+    uint32_t pad2;
 };
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
@@ -336,17 +339,19 @@ __device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32
 
 // Dynamic schedule.  Workgroups run at different speeds (a CU favours its
 // oldest waves), so after three static rounds (super-groups wg, wg + grid,
-// wg + 2 grid) each workgroup takes its next super-groups from one of eight
-// pools: pool x = wg mod 8 hands out 3 grid + x + 8 v for v = 0, 1, ... from
+// wg + 2 grid) each workgroup takes its next super-groups from one of P <= 8
+// pools: pool x = wg mod P hands out 3 grid + x + P v for v = 0, 1, ... from
 // its own counter, so that the ticket fetches of the whole grid are spread
-// over eight addresses (one address would serialise them).  Thread 0 fetches
+// over P addresses (one address would serialise them).  Thread 0 fetches
 // a ticket every iteration, three iterations before the loads that need it,
 // and hands it to the other waves through LDS.  A workgroup's tickets
 // increase, so it stops at its first ticket past the end having processed
 // every earlier one.  On exit every workgroup counts itself in the done word;
-// the last one zeroes every word for the next launch.
+// the last one zeroes every word for the next launch.  A pool's share of the
+// work is fixed, so P divides the workgroup count (schedule_pools).
 constexpr uint32_t kPools = 8;
 constexpr uint64_t kDynamicMinRounds = 12;
+constexpr uint32_t kMaxPerPool = 96;  // workgroups fetching from one counter
 constexpr uint32_t kPoolStride = DF11_SCHEDULE_WORDS / (kPools + 1);  // words: one cache line per counter
 
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *sched, uint32_t pool) {
@@ -453,7 +458,7 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 // after the last stores were issued.  One buffer per group (rather than two)
 // keeps the LDS of a 512-thread workgroup small enough for four per CU.
 template <int K, int GPW>
-__global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_t wg, const uint32_t n_wg) {
     // Static LDS: the first-level table (lo words | aux words | start masks)
     // at a fixed address, so a lookup's address is its index times 4.
     // Dynamic LDS: LUTs | CodeLengths | GPW exponent buffers | wave sums.
@@ -478,8 +483,6 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     uint32_t *s_ticket = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * (kWaves + 2u);
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
-    const uint32_t n_wg = gridDim.x;
-    const uint32_t wg = blockIdx.x;
     uint32_t *const sched = a.sched;
     if (wg >= n_super) {  // whole workgroup
         finish_schedule(sched, n_wg);
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
-        if (sched && tid == 0) fetched = take_ticket(sched, wg % kPools);  // for round it + 3
+        if (sched && tid == 0) fetched = take_ticket(sched, wg % a.pools);  // for round it + 3
 
         // 2. Merge and store the super-group decoded in the previous
         // iteration, then load this group's sign/mantissa chunks (into the
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
         const uint32_t o_start = min(lead + wave_off + incl - cnt, a.ebuf_cap - kDecodeReach);
         // Round it + 2's ticket (fetched last iteration) for the other waves;
         // they read it after the next barrier, at the top of iteration it + 1.
-        if (sched && tid == 0 && it >= 1u) *s_ticket = 3u * n_wg + wg % kPools + kPools * ticket;
+        if (sched && tid == 0 && it >= 1u) *s_ticket = 3u * n_wg + wg % a.pools + a.pools * ticket;
 
         // Phase 2: OR the (rotated) exponents into the zeroed LDS buffer at
         // their output positions (accumulator x = LDS byte address).  A
@@ -678,6 +681,37 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
     finish_schedule(sched, n_wg);
 }
 
+// One stream over the whole grid.
+template <int K, int GPW>
+__global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
+    decode_stream<K, GPW>(a, blockIdx.x, gridDim.x);
+}
+
+// Several independent streams (each with its own codebook and output) in one
+// launch: the grid is split into ranges of workgroups, one range per stream,
+// sized by the stream's work, so that every workgroup stages one stream's
+// tables once.  The ranges are taken over a permutation of the workgroup ids
+// (id * stride mod grid, stride coprime to the grid), so that each stream
+// gets workgroups of every dispatch position; a CU favours its oldest waves,
+// and a stream made only of late ids would run ~20% slower than the rest.
+// The descriptors travel in the kernel arguments.
+constexpr uint32_t kMaxBatch = DF11_MAX_BATCH;
+
+struct BatchArgs {
+    DecodeArgs s[kMaxBatch];
+    uint32_t wg_begin[kMaxBatch + 1];  // stream i owns permuted ids [wg_begin[i], wg_begin[i + 1])
+    uint32_t n;
+    uint32_t stride;  // coprime to the grid size
+};
+
+template <int K, int GPW>
+__global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_batch_kernel(BatchArgs b) {
+    const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
+    uint32_t i = 0;
+    while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
+    decode_stream<K, GPW>(b.s[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+}
+
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -719,14 +753,15 @@ int validate(const df11_device_stream *s) {
 
 // Workgroups of this kernel instance that fit on one CU, per device (0 until
 // first queried).
-template <int K, int GPW>
+template <int K, int GPW, bool kBatch>
 int resident_per_cu(int dev, size_t lds) {
     static int cache[64] = {};
     static size_t cache_lds[64] = {};
     if (dev >= 0 && dev < 64 && cache[dev] > 0 && cache_lds[dev] == lds) return cache[dev];
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, df11_decode_kernel<K, GPW>, kThreadsPerGroup * GPW,
-                                                     lds) != hipSuccess)
+    const void *fn = kBatch ? reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>)
+                            : reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreadsPerGroup * GPW, lds) != hipSuccess)
         return 0;
     if (dev >= 0 && dev < 64) {
         cache[dev] = per_cu;
@@ -735,23 +770,54 @@ int resident_per_cu(int dev, size_t lds) {
     return per_cu;
 }
 
+// Workgroup count and pool count for the dynamic schedule of a stream with
+// n_super super-groups given `want` workgroups: the pools must divide the
+// workgroup count, and no counter may serve more than kMaxPerPool of them
+// (else the count is rounded down to a multiple of kPools).  Sets a.sched to
+// null when the schedule does not pay (fewer than kDynamicMinRounds rounds).
+uint32_t schedule_pools(DecodeArgs &a, uint64_t n_super, uint64_t want) {
+    uint64_t n_wg = std::max<uint64_t>(1, std::min(want, n_super));
+    uint32_t pools = 1;
+    for (uint32_t p = kPools; p >= 1; --p)
+        if (n_wg % p == 0) {
+            pools = p;
+            break;
+        }
+    if (n_wg / pools > kMaxPerPool) {
+        n_wg -= n_wg % kPools;
+        pools = kPools;
+    }
+    a.pools = pools;
+    if (n_super < kDynamicMinRounds * n_wg) a.sched = nullptr;
+    return static_cast<uint32_t>(n_wg);
+}
+
+// Dynamic LDS of one stream's workgroup (beyond the static decode table).
+template <int GPW>
+size_t dynamic_lds(const DecodeArgs &a) {
+    return a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u;
+}
+
+int device_cus(int &dev, int &cus) {
+    if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return DF11_E_HIP;
+    return DF11_OK;
+}
+
 template <int K, int GPW>
 int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u;  // beyond the static table
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return DF11_E_HIP;
-    const int per_cu = resident_per_cu<K, GPW>(dev, lds);
+    const size_t lds = dynamic_lds<GPW>(a);
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const int per_cu = resident_per_cu<K, GPW, false>(dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
     const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
-    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_super, resident));
     (void)hipGetLastError();
     DecodeArgs args = a;
     // The dynamic schedule pays a few microseconds of ticket and exit
     // latency; it wins only when each workgroup has many rounds to balance.
-    if (n_super < kDynamicMinRounds * static_cast<uint64_t>(grid)) args.sched = nullptr;
+    const uint32_t grid = schedule_pools(args, n_super, resident);
     void *params[] = {&args};
     // hipExtLaunchKernel records start / stop (when given) at the kernel's own
     // start and end, not around the launch.
@@ -770,8 +836,48 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream, hipEvent_t s
     }
 }
 
-int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
-                    hipEvent_t stop) {
+// Split the resident grid between the streams of a batch in proportion to
+// their super-groups (at least one workgroup each, at most one per
+// super-group) and launch once.
+template <int K, int GPW>
+int launch_batch(BatchArgs &b, hipStream_t stream) {
+    size_t lds = 0;
+    uint64_t total_super = 0;
+    for (uint32_t i = 0; i < b.n; ++i) {
+        lds = std::max(lds, dynamic_lds<GPW>(b.s[i]));
+        total_super += (b.s[i].n_groups + GPW - 1) / GPW;
+    }
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const int per_cu = resident_per_cu<K, GPW, true>(dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
+    const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    uint32_t next = 0;
+    for (uint32_t i = 0; i < b.n; ++i) {
+        const uint64_t n_super = (b.s[i].n_groups + GPW - 1) / GPW;
+        const uint32_t share = schedule_pools(b.s[i], n_super, resident * n_super / total_super);
+        b.wg_begin[i] = next;
+        next += share;
+    }
+    b.wg_begin[b.n] = next;
+    // A stride near 0.618 of the grid, coprime to it, spreads each stream's
+    // range over the whole grid.
+    b.stride = 1;
+    for (uint32_t c = std::max<uint32_t>(1, static_cast<uint32_t>(next * 0.618)); c < 2 * next + 2; ++c)
+        if (std::gcd(c, next) == 1) {
+            b.stride = c;
+            break;
+        }
+    (void)hipGetLastError();
+    void *params[] = {&b};
+    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>), dim3(next),
+                           dim3(kThreadsPerGroup * GPW), params, lds, stream, nullptr, nullptr, 0) != hipSuccess)
+        return DF11_E_HIP;
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+}
+
+// Checks s and out (no launch) and fills the kernel arguments of one stream.
+int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
     int rc = validate(s);
     if (rc) return rc;
     const df11_header &h = s->h;
@@ -786,7 +892,7 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
         overlaps(out, out_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
         return DF11_E_INVALID_ARG;
 
-    DecodeArgs a{};
+    a = DecodeArgs{};
     a.enc = s->enc;
     a.sm = s->sm;
     a.gaps = s->gaps;
@@ -806,13 +912,74 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
     a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
     a.sched = s->schedule;
+    return DF11_OK;
+}
+
+int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop) {
+    DecodeArgs a;
+    const int rc = make_args(s, out, a);
+    if (rc || s->h.n_elements == 0) return rc;
     const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
-    switch (bits) {
+    switch (s->decode_table_bits) {
     case 10: return launch_k<10>(a, gpw, stream, start, stop);
     case 11: return launch_k<11>(a, gpw, stream, start, stop);
     case 12: return launch_k<12>(a, gpw, stream, start, stop);
     default: return DF11_E_INVALID_ARG;
     }
+}
+
+int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_t *const *outs,
+                          hipStream_t stream) {
+    if (n > kMaxBatch) return DF11_E_TOO_LARGE;
+    if (n && (!streams || !outs)) return DF11_E_INVALID_ARG;
+    BatchArgs b{};
+    uint32_t bits = 0, gpw = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        DecodeArgs a;
+        const int rc = make_args(&streams[i], outs[i], a);
+        if (rc) return rc;
+        // every output must also stay clear of the other streams' buffers and outputs
+        const uint64_t out_bytes = 2 * streams[i].h.n_elements;
+        for (uint32_t j = 0; j < n; ++j) {
+            if (j == i) continue;
+            const df11_device_stream &o = streams[j];
+            if (overlaps(outs[i], out_bytes, outs[j], 2 * o.h.n_elements) ||
+                overlaps(outs[i], out_bytes, o.enc, o.h.enc_bytes) || overlaps(outs[i], out_bytes, o.sm, o.h.sm_bytes) ||
+                overlaps(outs[i], out_bytes, o.gaps, o.h.gaps_bytes) ||
+                overlaps(outs[i], out_bytes, o.out_pos, o.h.out_pos_bytes) ||
+                overlaps(outs[i], out_bytes, o.luts, 256ull * o.h.n_luts) ||
+                overlaps(outs[i], out_bytes, o.code_lengths, 256) ||
+                overlaps(outs[i], out_bytes, o.decode_table, df11_decode_table_bytes(o.decode_table_bits)) ||
+                overlaps(outs[i], out_bytes, o.schedule, o.schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
+                return DF11_E_INVALID_ARG;
+        }
+        if (streams[i].h.n_elements == 0) continue;
+        const uint32_t g = streams[i].groups_per_workgroup ? streams[i].groups_per_workgroup
+                                                           : kDefaultGroupsPerWorkgroup;
+        if (b.n == 0) {
+            bits = streams[i].decode_table_bits;
+            gpw = g;
+        } else if (streams[i].decode_table_bits != bits || g != gpw) {
+            return DF11_E_INVALID_ARG;
+        }
+        b.s[b.n++] = a;
+    }
+    if (b.n == 0) return DF11_OK;
+#define DF11_BATCH_CASE(KB)                                        \
+    case KB:                                                       \
+        switch (gpw) {                                             \
+        case 1: return launch_batch<KB, 1>(b, stream);             \
+        case 4: return launch_batch<KB, 4>(b, stream);             \
+        default: return launch_batch<KB, 2>(b, stream);            \
+        }
+    switch (bits) {
+        DF11_BATCH_CASE(10)
+        DF11_BATCH_CASE(11)
+        DF11_BATCH_CASE(12)
+    default: return DF11_E_INVALID_ARG;
+    }
+#undef DF11_BATCH_CASE
 }
 
 }  // namespace
@@ -827,6 +994,11 @@ int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64
     if (!s) return DF11_E_INVALID_ARG;
     if (scratch_elems < s->h.n_elements) return DF11_E_BUFFER_TOO_SMALL;
     return decompress_impl(s, scratch, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
+}
+
+int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
+                          void *hip_stream) {
+    return decompress_batch_impl(streams, n_streams, outs, static_cast<hipStream_t>(hip_stream));
 }
 
 int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,

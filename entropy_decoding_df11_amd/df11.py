@@ -294,11 +294,79 @@ class DF11Block:
         return views
 
 
+def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor"], stream=None) -> None:  # noqa: F821
+    """Decode several streams, each with its own codebook, in one launch:
+    outs[i] (a contiguous bf16 tensor of tensors[i].n_elements elements)
+    receives tensors[i].  All streams must use the same decode-table width."""
+    import torch
+    if len(tensors) != len(outs):
+        raise ValueError("one output per stream")
+    for t, o in zip(tensors, outs):
+        if o.dtype != torch.bfloat16 or o.numel() != t.n_elements or not o.is_contiguous():
+            raise ValueError("each out must be a contiguous bfloat16 tensor with its stream's element count")
+    n = len(tensors)
+    arr = (_lib.DeviceStream * max(n, 1))(*[t.device_stream() for t in tensors])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    st = tensors[0]._hip_stream(stream) if n else ctypes.c_void_p(0)
+    lib = _lib.load()
+    _lib.check(lib.df11_decompress_batch(arr, n, ptrs, st), "df11_decompress_batch")
+
+
+class DF11BlockBatch:
+    """Every linear weight of one transformer block as its own DF11 stream
+    (a codebook per weight), decoded in one batched launch into one scratch
+    buffer ("Dekompresi per transformer block")."""
+
+    def __init__(self, tensors: List[DF11Tensor], views: List[Tuple[str, int, Tuple[int, ...]]], n_elements: int):
+        self.tensors = tensors
+        self.views = views
+        self._n = n_elements
+        self._view_cache = (None, None, None)
+
+    @property
+    def n_elements(self) -> int:
+        """Scratch elements needed (each weight starts on a 16-byte boundary)."""
+        return self._n
+
+    def compressed_bytes(self) -> int:
+        return sum(t.compressed_bytes() for t in self.tensors)
+
+    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+        import torch
+        if scratch is None:
+            scratch = torch.empty(self._n, dtype=torch.bfloat16, device=self.tensors[0].device)
+        if scratch.dtype != torch.bfloat16 or not scratch.is_contiguous() or scratch.numel() < self._n:
+            raise ValueError("scratch must be a contiguous bfloat16 tensor of at least n_elements")
+        cached, views, outs = self._view_cache
+        if cached is not scratch:
+            flat = scratch.reshape(-1)
+            outs = [flat[off:off + int(np.prod(shape))] for _, off, shape in self.views]
+            views = {name: o.view(shape) for (name, _, shape), o in zip(self.views, outs)}
+            self._view_cache = (scratch, views, outs)
+        decompress_batch(self.tensors, outs, stream=stream)
+        return views
+
+
 def compress_block(weights: Union[Dict[str, ArrayLike], List[Tuple[str, ArrayLike]]], device="cuda",
-                   decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS) -> DF11Block:
-    """Concatenate the block's weights row-major in the given order, build one
-    codebook from the summed histogram and encode them as one stream."""
+                   decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS,
+                   codebook: str = "shared") -> Union[DF11Block, DF11BlockBatch]:
+    """Encode a block's weights for decompression in one launch.
+
+    codebook="shared": concatenate them row-major in the given order, build
+    one codebook from the summed histogram and encode one stream (DF11Block).
+    codebook="per_weight": one stream and codebook per weight, decoded by a
+    batched launch (DF11BlockBatch, at most 16 weights)."""
     items = list(weights.items()) if isinstance(weights, dict) else list(weights)
+    if codebook == "per_weight":
+        tensors, views, off = [], [], 0
+        for name, w in items:
+            shape = tuple(int(s) for s in w.shape)
+            tensors.append(compress(_u16(w), shape=shape, device=device, decode_table_bits=decode_table_bits))
+            views.append((name, off, shape))
+            off += (int(np.prod(shape)) + 7) // 8 * 8
+        return DF11BlockBatch(tensors, views, off)
+    if codebook != "shared":
+        raise ValueError("codebook must be 'shared' or 'per_weight'")
     parts, views, off = [], [], 0
     for name, w in items:
         shape = tuple(int(s) for s in w.shape)

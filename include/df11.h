@@ -57,6 +57,8 @@ typedef enum df11_status {
 /* Size, in uint32 words, of the dynamic-schedule work counters
  * (df11_device_stream.schedule). */
 #define DF11_SCHEDULE_WORDS 144
+/* Most streams one df11_decompress_batch call decodes. */
+#define DF11_MAX_BATCH 16
 
 /* The codebook shared by all tensors of one stream (host, plain data).
  *   code_lengths[e]: Huffman code length of exponent e, 0 if unused
@@ -216,6 +218,25 @@ int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream
  * offset, shape) are kept by the caller.  Same kernel and errors as
  * df11_decompress, plus DF11_E_BUFFER_TOO_SMALL if scratch_elems < N. */
 int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64_t scratch_elems,
+                          void *hip_stream);
+
+/* Decompress several independent streams -- each with its own codebook,
+ * decode table and output -- in one launch, for instance every linear weight
+ * of a transformer block encoded with a codebook of its own ("Dekompresi per
+ * transformer block" batches a block's matrices into one launch because a
+ * single matrix is too small to fill the GPU).  The grid is divided between
+ * the streams in proportion to their work.
+ *   streams  host array of n_streams device streams (as for df11_decompress);
+ *            all non-empty ones must use the same decode_table_bits and
+ *            groups_per_workgroup
+ *   outs     host array of n_streams device pointers; outs[i] receives
+ *            streams[i].h.n_elements uint16, 16-byte aligned, and may not
+ *            overlap any other output or any stream's buffers
+ * Streams with N = 0 are skipped.  Errors: DF11_E_TOO_LARGE (n_streams >
+ * DF11_MAX_BATCH), DF11_E_INVALID_ARG (mismatched table widths or launch
+ * shapes, overlapping buffers, or as for df11_decompress), DF11_E_BAD_STREAM,
+ * DF11_E_HIP.  Nothing is launched unless every stream is valid. */
+int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
                           void *hip_stream);
 
 /* df11_decompress with the decode kernel timed by the GPU: start_event and

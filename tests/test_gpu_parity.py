@@ -200,3 +200,43 @@ def test_timed_entry_point_matches(torch_cuda, bits):
     torch.cuda.synchronize()
     assert np.array_equal(_to_u16(out), w)
     assert ev[0].elapsed_time(ev[1]) > 0
+
+
+def test_batch_of_independent_streams(torch_cuda):
+    """One launch decodes streams with different codebooks, sizes (empty and
+    single-element ones included) and code-length profiles."""
+    torch = torch_cuda
+    cases = [("normal", 77_777, 1), ("fib_chain", 300_001, 2), ("uniform_bits", 1_000_003, 3), ("normal", 1, 4),
+             ("stress_tuned", 2_000_000, 5), ("student_t", 0, 6), ("stress_literal", 123_457, 7)]
+    _note("batch of independent streams")
+    ws = [_case(k, n, seed) if n else np.zeros(0, np.uint16) for k, n, seed in cases]
+    ts = [df11.compress(w, shape=(w.size,), decode_table_bits=11) for w in ws]
+    outs = [torch.full((max(w.size, 1),), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)[: w.size]
+            for w in ws]
+    df11.decompress_batch(ts, outs)
+    torch.cuda.synchronize()
+    for (kind, n, _), w, o in zip(cases, ws, outs):
+        assert np.array_equal(_to_u16(o), w), kind
+
+
+def test_block_with_per_weight_codebooks(torch_cuda):
+    """The Llama-3-8B-shaped block with a codebook per weight, decoded by one
+    batched launch into one scratch buffer; then the same block with the
+    dynamic schedule off."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block()
+    _note(f"block per-weight codebooks n={flat.size}")
+    blk = df11.compress_block([(name, flat[off:off + r * c].reshape(r, c)) for name, off, (r, c) in views],
+                              codebook="per_weight")
+    assert len(blk.tensors) == len(views)
+    scratch = torch.empty(blk.n_elements, dtype=torch.bfloat16, device="cuda")
+    for dynamic in (True, False):
+        for t in blk.tensors:
+            t.set_dynamic_schedule(dynamic)
+        scratch.view(torch.int16).fill_(0x5A5A)
+        out = blk.decompress(scratch=scratch)
+        torch.cuda.synchronize()
+        for name, off, (r, c) in views:
+            assert np.array_equal(_to_u16(out[name]), flat[off:off + r * c]), (name, dynamic)
+        for t in blk.tensors:
+            assert not t._schedule.cpu().numpy().any()

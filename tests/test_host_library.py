@@ -279,3 +279,34 @@ def test_schedule_words_constant_matches_header():
     with open(os.path.join(os.path.dirname(__file__), "..", "include", "df11.h")) as f:
         m = re.search(r"#define\s+DF11_SCHEDULE_WORDS\s+(\d+)", f.read())
     assert m and int(m.group(1)) == _lib.SCHEDULE_WORDS
+
+
+def test_decompress_batch_validation_runs_before_any_launch():
+    """Every batch error is found before anything is launched (no GPU here)."""
+    lib = _lib_or_skip()
+    host = df11.encode(workloads.gen_single_matrix(rows=64, cols=64))
+    s = _fake_device_stream(host)
+    n = host.header.n_elements
+
+    def call(streams, outs):
+        arr = (_lib.DeviceStream * max(len(streams), 1))(*streams)
+        ptrs = (ctypes.c_void_p * max(len(outs), 1))(*outs)
+        return lib.df11_decompress_batch(arr, len(streams), ptrs, None)
+
+    assert lib.df11_decompress_batch(None, 0, None, None) == 0  # empty batch
+    assert lib.df11_decompress_batch(None, 1, None, None) == -1
+    # more streams than one launch takes
+    assert call([s] * (_lib.MAX_BATCH + 1), [1 << 48] * (_lib.MAX_BATCH + 1)) == -7
+    # a stream whose header is inconsistent
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.enc_bytes += 16
+    assert call([s, bad], [1 << 48, (1 << 48) + (1 << 32)]) == -6
+    # different decode-table widths in one batch
+    other = _lib.DeviceStream.from_buffer_copy(s)
+    other.decode_table_bits = 11
+    assert call([s, other], [1 << 48, (1 << 48) + (1 << 32)]) == -1
+    # outputs that overlap each other, or another stream's input
+    assert call([s, s], [1 << 48, (1 << 48) + 2 * (n // 2) // 16 * 16]) == -1
+    assert call([s, s], [1 << 48, s.enc]) == -1
+    # misaligned output
+    assert call([s], [(1 << 48) + 8]) == -1
