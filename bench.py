@@ -3,7 +3,9 @@
 One step = one batched decompression of the Llama-3-8B-shaped transformer block
 (q, k, v, o, gate, up, down; one DF11 stream, shared codebook, ~218M BF16
 weights) into one scratch buffer, with the compressed stream already resident
-in HBM.  Prints one JSON line.
+in HBM.  Prints one JSON line.  --workload picks another input: the same block
+with a codebook per weight (seven streams, one batched launch), or a single
+stream (LM-head-sized 128256x4096, the 2^28 stress stream, ...).
 
   value     = K * (algorithmic bytes per step) / (timed wall time), GB/s
   algorithmic bytes per step = EncodedExponent + PackedSignMantissa + Gaps
@@ -31,6 +33,9 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "llama3_8b_block"
+WORKLOAD_CHOICES = ["llama3_8b_block", "llama3_8b_block_per_weight", "lm_head_128256x4096", "stress_2p28_zipf",
+                    "mlp_14336x4096_t5", "proj_4096x4096_outliers", "single_1024x1024"]
 METRIC = "DF11 decompress GB/s (compressed in + BF16 out) and % of MI355X HBM peak"
 KERNEL_SRC = os.path.join(REPO, "entropy_decoding_df11_amd", "csrc", "df11_decode.hip")
 PMC_SUMMARY = os.path.join(REPO, "profiles", "df11_decode_kernel_llama3_8b_block_pmc.json")
@@ -172,6 +177,9 @@ def main() -> int:
     # settle; 100 launches (~15 ms) reach the steady state.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-table-bits", type=int, default=11)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=WORKLOAD_CHOICES,
+                    help="the Llama-3-8B block (default), the same with a codebook per weight (one batched "
+                         "launch), or one of the single-stream workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: usable host cores)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -200,46 +208,79 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    flat, views = workloads.gen_block()
-    t_gen = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    blk = df11.compress_block([(n, flat[o:o + r * c].reshape(r, c)) for n, o, (r, c) in views], device=dev,
-                              decode_table_bits=args.decode_table_bits)
-    t_enc = time.perf_counter() - t0
-    t = blk.tensor
-    h = t.header
-    n = int(h.n_elements)
-    comp = t.compressed_bytes()
-    algo_bytes = comp + 2 * n
-    scratch = torch.empty(n, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    wl = args.workload
+    t0 = time.perf_counter()
+    if wl.startswith("llama3_8b_block"):
+        flat, views = workloads.gen_block()
+    else:
+        flat, views = workloads.make(wl), None
+    t_gen = time.perf_counter() - t0
+    n = int(flat.size)
+    t0 = time.perf_counter()
+    config = {"workload": wl}
+    if views is not None:
+        codebook = "per_weight" if wl.endswith("_per_weight") else "shared"
+        blk = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views], device=dev,
+                                  decode_table_bits=args.decode_table_bits, codebook=codebook)
+        scratch = torch.empty(blk.n_elements, dtype=torch.bfloat16, device=dev)
+        config["shapes"] = {name: list(shape) for name, _, shape in views}
+        config["codebook"] = codebook
+        if codebook == "shared":
+            h, comp = blk.tensor.header, blk.tensor.compressed_bytes()
+            decode = lambda ev=None: blk.decompress(scratch=scratch, events=ev)  # noqa: E731
+        else:
+            h, comp = blk.tensors[0].header, blk.compressed_bytes()
+            config["streams"] = len(blk.tensors)
+            config["timing"] = "events recorded around the batched launch"
+
+            def decode(ev=None):
+                # the batched launch has no dispatch-recorded events: record them around it
+                if ev is not None:
+                    ev[0].record(stream)
+                blk.decompress(scratch=scratch)
+                if ev is not None:
+                    ev[1].record(stream)
+
+        def decoded():
+            if codebook == "shared":
+                return scratch[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+            outs = blk.decompress(scratch=scratch)  # cached views; decodes once more
+            torch.cuda.synchronize()
+            return np.concatenate([outs[nm].reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
+                                   for nm, _, _ in views])
+    else:
+        t = df11.compress(flat, shape=(n,), device=dev, decode_table_bits=args.decode_table_bits)
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        h, comp = t.header, t.compressed_bytes()
+        decode = lambda ev=None: t.decompress(out=out, events=ev)  # noqa: E731
+        decoded = lambda: out.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    t_enc = time.perf_counter() - t0
+    algo_bytes = comp + 2 * n
 
     # Check the decode first: the copy back and the comparison leave the GPU
     # idle long enough for its clocks to drop, which the warmup then undoes.
-    blk.decompress(scratch=scratch)
+    decode()
     torch.cuda.synchronize()
-    got = scratch.view(torch.int16).cpu().numpy().view(np.uint16)
-    if not np.array_equal(got, flat):
-        print("bench: decoded block differs from the original weights", file=sys.stderr)
+    if not np.array_equal(decoded(), flat):
+        print(f"bench: decoded {wl} differs from the original weights", file=sys.stderr)
         return 1
-    del got
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for e in starts + ends:  # create the events outside the timed region
         e.record(stream)
     for _ in range(args.warmup):
-        blk.decompress(scratch=scratch)
+        decode()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        blk.decompress(scratch=scratch, events=(starts[i], ends[i]))
+        decode((starts[i], ends[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    if not np.array_equal(scratch.view(torch.int16).cpu().numpy().view(np.uint16), flat):
-        print("bench: the timed launches decoded the block wrongly", file=sys.stderr)
+    if not np.array_equal(decoded(), flat):
+        print(f"bench: the timed launches decoded {wl} wrongly", file=sys.stderr)
         return 1
     mean_ms = float(np.mean(kern_ms))
     achieved = algo_bytes / (mean_ms * 1e-3) / 1e9
@@ -259,7 +300,7 @@ def main() -> int:
     copy_gbps = 10 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    traffic = _traffic_from_profile()
+    traffic = _traffic_from_profile() if wl == DEFAULT_WORKLOAD else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -274,10 +315,8 @@ def main() -> int:
         "dtype": "u32",
         "data": "synthetic",
         "config": {
-            "workload": "llama3_8b_block",
-            "shapes": {name: list(shape) for name, _, shape in views},
+            **config,
             "n_elements": n,
-            "codebook": "shared",
             "bits_per_weight": round(8 * comp / n, 4),
             "compressed_bytes": comp,
             "decode_table_bits": args.decode_table_bits,
@@ -308,7 +347,7 @@ def main() -> int:
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole llama3_8b_block stream ({n} weights), tree-walk decode split by groups "
+            "sample": f"the whole {wl} data as one stream ({n} weights), tree-walk decode split by groups "
                       f"over {threads} threads; {cpu_s:.2f} s wall; output {'matches' if ok else 'DIFFERS FROM'} "
                       f"the original weights",
         }

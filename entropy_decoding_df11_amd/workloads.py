@@ -107,6 +107,23 @@ def gen_block(seed: int = 3, shapes: List[Tuple[str, Tuple[int, int]]] = None
     return np.concatenate(parts), views
 
 
+LM_HEAD_SHAPE = (128256, 4096)
+
+
+def gen_lm_head(seed: int = 5, shape: Tuple[int, int] = LM_HEAD_SHAPE, rows_per_chunk: int = 8192) -> np.ndarray:
+    """LM-head / embedding-sized matrix (128256x4096 for a 128K vocabulary):
+    N(0, 0.02^2) with 1e-4 of the entries replaced by N(0, 1) outliers, drawn
+    row-chunk by row-chunk (rows_per_chunk rows per draw, in order) so that
+    no float64 copy of the whole matrix is held."""
+    rows, cols = shape
+    rng = np.random.default_rng(seed)
+    out = np.empty(rows * cols, dtype=np.uint16)
+    for r0 in range(0, rows, rows_per_chunk):
+        n = (min(rows, r0 + rows_per_chunk) - r0) * cols
+        out[r0 * cols:r0 * cols + n] = f32_to_bf16_bits(_normal_with_replacements(rng, n, 0.02, [(1e-4, 1.0)]))
+    return out
+
+
 STRESS_CENTER = 120
 STRESS_RANKS = 40
 
@@ -176,6 +193,9 @@ WORKLOADS: Dict[str, Workload] = {
     "llama3_8b_block": Workload("llama3_8b_block", sum(r * c for _, (r, c) in LLAMA3_8B_BLOCK),
                                 "Llama-3-8B block q,k,v,o,gate,up,down, N(0,0.02^2) + 1e-4 N(0,1), "
                                 "shared codebook, seed 3", _block_only),
+    "lm_head_128256x4096": Workload("lm_head_128256x4096", LM_HEAD_SHAPE[0] * LM_HEAD_SHAPE[1],
+                                    "128256x4096 N(0,0.02^2) + 1e-4 N(0,1), row chunks of 8192, seed 5",
+                                    gen_lm_head),
     "stress_2p28_zipf": Workload("stress_2p28_zipf", 1 << 28,
                                  "2^28 exponents over 40 ranks (Zipf 1.6 head, 0.6 geometric tail), "
                                  "uniform sign/mantissa, seed 4", gen_stress),

@@ -240,3 +240,13 @@ def test_block_with_per_weight_codebooks(torch_cuda):
             assert np.array_equal(_to_u16(out[name]), flat[off:off + r * c]), (name, dynamic)
         for t in blk.tensors:
             assert not t._schedule.cpu().numpy().any()
+
+
+def test_lm_head_single_stream_full_size(torch_cuda):
+    """An LM-head / embedding-sized matrix (128256x4096, 525M weights) as one
+    stream, decoded unbatched; the original bits are the exact result."""
+    w = workloads.gen_lm_head()
+    _note(f"lm head n={w.size}")
+    got, t = _gpu_decode(torch_cuda, w, bits=11)
+    assert np.array_equal(got, w)
+    assert t.header.n_elements == 128256 * 4096
