@@ -169,6 +169,58 @@ def summarize_profiles(prof_dir: str, commands: dict) -> None:
         f.write("\n")
 
 
+def integration(args, dev) -> int:
+    """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
+    weights, DF11 blocks decoded in line before each block, and DF11 blocks
+    decoded on a side stream (capped grid) while the previous block computes."""
+    import torch
+    from entropy_decoding_df11_amd import df11, runtime, workloads
+    blocks, resident = [], []
+    t0 = time.perf_counter()
+    for b in range(args.blocks):
+        flat, views = workloads.gen_block(seed=1000 + b)
+        parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
+        blocks.append(df11.compress_block(parts, device=dev))
+        resident.append({nm: torch.from_numpy(a.astype(np.int16)).to(dev).view(torch.bfloat16) for nm, a in parts})
+    t_prep = time.perf_counter() - t0
+    overlap = runtime.BlockDecoder(blocks, device=dev, overlap=True, decode_workgroups=args.overlap_workgroups)
+    inline = runtime.BlockDecoder(blocks, device=dev, overlap=False)
+    rows = []
+    for tokens in (16, 256, 4096):
+        rng = np.random.default_rng(tokens)
+        x = workloads.f32_to_bf16_bits(rng.standard_normal(tokens * 4096) * 0.5).reshape(tokens, 4096)
+        x = torch.from_numpy(x.astype(np.int16)).to(dev).view(torch.bfloat16)
+        res = {}
+        ref = None
+        for name, src in (("resident", resident), ("df11_overlap", overlap), ("df11_inline", inline)):
+            for _ in range(3):
+                y = runtime.model_forward(x, src)
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = y
+            elif not torch.equal(y.view(torch.int16), ref.view(torch.int16)):
+                print(f"integration: {name} output differs from resident weights", file=sys.stderr)
+                return 1
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                runtime.model_forward(x, src)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) / 10, 4)
+        rows.append({"tokens": tokens, "ms_per_forward": res,
+                     "df11_overlap_vs_resident": round(res["df11_overlap"] / res["resident"], 3),
+                     "df11_inline_vs_resident": round(res["df11_inline"] / res["resident"], 3)})
+    comp = sum(b.tensor.compressed_bytes() for b in blocks)
+    raw = sum(2 * b.n_elements for b in blocks)
+    print(json.dumps({"integration": "synthetic model forward", "blocks": args.blocks,
+                      "weights_per_block": int(blocks[0].n_elements),
+                      "overlap_decode_workgroups": args.overlap_workgroups, "compressed_over_bf16": round(comp / raw, 4),
+                      "outputs": "bit-identical to the resident-weight forward", "host_prep_s": round(t_prep, 1),
+                      "results": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +234,13 @@ def main() -> int:
                          "launch), or one of the single-stream workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: usable host cores)")
+    ap.add_argument("--integration", action="store_true",
+                    help="instead of the decode line, time a synthetic model forward over full-size blocks with "
+                         "resident BF16 weights, with DF11 blocks decoded on a side stream just before use, and "
+                         "with DF11 blocks decoded in line")
+    ap.add_argument("--blocks", type=int, default=4, help="blocks of the --integration model")
+    ap.add_argument("--overlap-workgroups", type=int, default=512,
+                    help="workgroup cap of the side-stream decode in --integration (0: no cap)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 runs of this script under DIR, then exit")
     args = ap.parse_args()
@@ -209,6 +268,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.integration:
+        return integration(args, dev)
     wl = args.workload
     t0 = time.perf_counter()
     if wl.startswith("llama3_8b_block"):

@@ -97,6 +97,8 @@ class DeviceStream(ctypes.Structure):
         ("decode_table_bits", ctypes.c_uint32),
         ("groups_per_workgroup", ctypes.c_uint32),
         ("schedule", ctypes.c_void_p),
+        ("max_workgroups", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 

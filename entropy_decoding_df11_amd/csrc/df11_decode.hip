@@ -805,14 +805,15 @@ int device_cus(int &dev, int &cus) {
 }
 
 template <int K, int GPW>
-int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const size_t lds = dynamic_lds<GPW>(a);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const int per_cu = resident_per_cu<K, GPW, false>(dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
-    const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, max_wg);
     (void)hipGetLastError();
     DecodeArgs args = a;
     // The dynamic schedule pays a few microseconds of ticket and exit
@@ -828,11 +829,12 @@ int launch(const DecodeArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t
 }
 
 template <int K>
-int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+int launch_k(const DecodeArgs &a, uint32_t gpw, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
+             hipEvent_t stop) {
     switch (gpw) {
-    case 1: return launch<K, 1>(a, stream, start, stop);
-    case 4: return launch<K, 4>(a, stream, start, stop);
-    default: return launch<K, 2>(a, stream, start, stop);
+    case 1: return launch<K, 1>(a, max_wg, stream, start, stop);
+    case 4: return launch<K, 4>(a, max_wg, stream, start, stop);
+    default: return launch<K, 2>(a, max_wg, stream, start, stop);
     }
 }
 
@@ -840,7 +842,7 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, hipStream_t stream, hipEvent_t s
 // their super-groups (at least one workgroup each, at most one per
 // super-group) and launch once.
 template <int K, int GPW>
-int launch_batch(BatchArgs &b, hipStream_t stream) {
+int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
     size_t lds = 0;
     uint64_t total_super = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
@@ -851,7 +853,8 @@ int launch_batch(BatchArgs &b, hipStream_t stream) {
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const int per_cu = resident_per_cu<K, GPW, true>(dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
-    const uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
         const uint64_t n_super = (b.s[i].n_groups + GPW - 1) / GPW;
@@ -922,9 +925,9 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     if (rc || s->h.n_elements == 0) return rc;
     const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
     switch (s->decode_table_bits) {
-    case 10: return launch_k<10>(a, gpw, stream, start, stop);
-    case 11: return launch_k<11>(a, gpw, stream, start, stop);
-    case 12: return launch_k<12>(a, gpw, stream, start, stop);
+    case 10: return launch_k<10>(a, gpw, s->max_workgroups, stream, start, stop);
+    case 11: return launch_k<11>(a, gpw, s->max_workgroups, stream, start, stop);
+    case 12: return launch_k<12>(a, gpw, s->max_workgroups, stream, start, stop);
     default: return DF11_E_INVALID_ARG;
     }
 }
@@ -934,7 +937,7 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
     if (n > kMaxBatch) return DF11_E_TOO_LARGE;
     if (n && (!streams || !outs)) return DF11_E_INVALID_ARG;
     BatchArgs b{};
-    uint32_t bits = 0, gpw = 0;
+    uint32_t bits = 0, gpw = 0, max_wg = 0;
     for (uint32_t i = 0; i < n; ++i) {
         DecodeArgs a;
         const int rc = make_args(&streams[i], outs[i], a);
@@ -957,6 +960,8 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
         if (streams[i].h.n_elements == 0) continue;
         const uint32_t g = streams[i].groups_per_workgroup ? streams[i].groups_per_workgroup
                                                            : kDefaultGroupsPerWorkgroup;
+        if (streams[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, streams[i].max_workgroups)
+                                                       : streams[i].max_workgroups;
         if (b.n == 0) {
             bits = streams[i].decode_table_bits;
             gpw = g;
@@ -969,9 +974,9 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
 #define DF11_BATCH_CASE(KB)                                        \
     case KB:                                                       \
         switch (gpw) {                                             \
-        case 1: return launch_batch<KB, 1>(b, stream);             \
-        case 4: return launch_batch<KB, 4>(b, stream);             \
-        default: return launch_batch<KB, 2>(b, stream);            \
+        case 1: return launch_batch<KB, 1>(b, max_wg, stream);     \
+        case 4: return launch_batch<KB, 4>(b, max_wg, stream);     \
+        default: return launch_batch<KB, 2>(b, max_wg, stream);    \
         }
     switch (bits) {
         DF11_BATCH_CASE(10)

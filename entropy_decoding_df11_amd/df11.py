@@ -179,6 +179,11 @@ class DF11Tensor:
         statically."""
         self._stream_struct.schedule = self._schedule.data_ptr() if on else None
 
+    def set_max_workgroups(self, n: int) -> None:
+        """Launch at most n workgroups (0: fill the GPU), leaving CUs to
+        kernels running concurrently on other streams."""
+        self._stream_struct.max_workgroups = n
+
     def set_groups_per_workgroup(self, gpw: int) -> None:
         """Launch shape: groups decoded together by one workgroup (0 = default, 1, 2, 4)."""
         self._stream_struct.groups_per_workgroup = gpw
@@ -267,6 +272,10 @@ class DF11Block:
     def n_elements(self) -> int:
         return self.tensor.n_elements
 
+    def set_max_workgroups(self, n: int) -> None:
+        """Launch at most n workgroups (0: fill the GPU)."""
+        self.tensor.set_max_workgroups(n)
+
     def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None,
                    events=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
         """Decode the block into scratch (at least n_elements bf16; a new one
@@ -330,6 +339,11 @@ class DF11BlockBatch:
 
     def compressed_bytes(self) -> int:
         return sum(t.compressed_bytes() for t in self.tensors)
+
+    def set_max_workgroups(self, n: int) -> None:
+        """Launch at most n workgroups in total (0: fill the GPU)."""
+        for t in self.tensors:
+            t.set_max_workgroups(n)
 
     def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
         import torch

@@ -1,0 +1,126 @@
+"""Decompress transformer blocks just before use.
+
+GeekNews, "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan LLM
+menjadi 70% ukurannya", sections "Dekompresi yang disesuaikan untuk inferensi
+GPU" and "Dekompresi per transformer block": weights stay compressed in HBM,
+each block is decompressed into a scratch buffer right before its forward
+pass and discarded after it.  BlockDecoder does that on the caller's stream,
+or, with overlap=True, decodes block i + 1 on a side stream into the other of
+two scratch buffers while the caller computes with block i.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Iterator, List, Optional, Sequence, Tuple, Union
+
+from .df11 import DF11Block, DF11BlockBatch
+
+Block = Union[DF11Block, DF11BlockBatch]
+
+
+class BlockDecoder:
+    """Iterate over compressed blocks, yielding (index, {name: bf16 weight})
+    with every weight already decoded in the caller's stream order.
+
+    By default each block is decoded on the caller's stream right before it
+    is yielded.  With overlap=True, block i + 1 is decoded on a side stream
+    while the caller enqueues block i's work; an event recorded on the
+    caller's stream when it asks for the next block marks block i's scratch
+    buffer free again.  Either way the weights of block i are valid until the
+    caller asks for block i + 2 (two scratch buffers alternate), so the caller
+    must finish enqueuing block i's work before advancing.
+
+    Overlap rarely pays on one GPU: the decoder's persistent grid fills every
+    CU and is bound by HBM, and so are the caller's GEMMs at small batch.
+    decode_workgroups caps the workgroups of an overlapped decode (0: fill the
+    GPU) so the caller's kernels find room beside it.
+    """
+
+    def __init__(self, blocks: Sequence[Block], device="cuda", overlap: bool = False, decode_workgroups: int = 0):
+        import torch
+        self.blocks = list(blocks)
+        self.device = torch.device(device)
+        self.overlap = overlap
+        self.decode_workgroups = decode_workgroups
+        n = max((b.n_elements for b in self.blocks), default=0)
+        self._scratch = [torch.empty(max(n, 1), dtype=torch.bfloat16, device=self.device) for _ in range(2)]
+        # Default priority: streams of different priorities are avoided.
+        self._side = torch.cuda.Stream(self.device) if overlap else None
+
+    def __len__(self) -> int:
+        return len(self.blocks)
+
+    def _decode(self, i: int, stream, cap: int = 0) -> Dict:
+        b = self.blocks[i]
+        if cap:
+            b.set_max_workgroups(cap)
+        try:
+            return b.decompress(scratch=self._scratch[i % 2], stream=stream)
+        finally:
+            if cap:
+                b.set_max_workgroups(0)
+
+    def __iter__(self) -> Iterator[Tuple[int, Dict]]:
+        import torch
+        if not self.blocks:
+            return
+        main = torch.cuda.current_stream(self.device)
+        if not self.overlap:
+            for i in range(len(self.blocks)):
+                yield i, self._decode(i, main)
+            return
+        side = self._side
+        free = [None, None]      # event: the caller has finished with scratch[k]
+        ready = [None] * len(self.blocks)
+
+        def launch(i: int):
+            side.wait_stream(main) if free[i % 2] is None else side.wait_event(free[i % 2])
+            views = self._decode(i, side, self.decode_workgroups)
+            ev = torch.cuda.Event()
+            ev.record(side)
+            ready[i] = ev
+            return views
+
+        pending = launch(0)
+        for i in range(len(self.blocks)):
+            views = pending
+            main.wait_event(ready[i])
+            if i + 1 < len(self.blocks):
+                pending = launch(i + 1)
+            yield i, views
+            # the caller has enqueued block i's work on `main`
+            ev = torch.cuda.Event()
+            ev.record(main)
+            free[i % 2] = ev
+
+
+def block_forward(x, w: Dict, eps: float = 1e-5):
+    """A synthetic Llama-style block forward on BF16 weights (no attention
+    mixing, which needs no weights): RMS-normed projections q, k, v and o
+    with a residual, then the gated MLP (gate, up, down) with a residual.
+    Used to show the decompressed weights in use; shapes follow the weights."""
+    import torch
+    import torch.nn.functional as F
+
+    def rms(h):
+        return h * torch.rsqrt(h.float().pow(2).mean(-1, keepdim=True) + eps).to(h.dtype)
+
+    h = rms(x)
+    q = F.linear(h, w["q_proj"])
+    k = F.linear(h, w["k_proj"])
+    v = F.linear(h, w["v_proj"])
+    rep = q.shape[-1] // k.shape[-1]
+    a = q + (k * v).repeat_interleave(rep, dim=-1)
+    x = x + F.linear(a, w["o_proj"])
+    h = rms(x)
+    x = x + F.linear(F.silu(F.linear(h, w["gate_proj"])) * F.linear(h, w["up_proj"]), w["down_proj"])
+    return x
+
+
+def model_forward(x, blocks: Union[BlockDecoder, List[Dict]]):
+    """Run block_forward over every block in order, taking the weights from a
+    BlockDecoder (compressed) or from a list of dicts (resident BF16)."""
+    items = iter(blocks) if isinstance(blocks, BlockDecoder) else enumerate(blocks)
+    for _, w in items:
+        x = block_forward(x, w)
+    return x

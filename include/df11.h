@@ -134,7 +134,11 @@ typedef struct df11_header {
  *                                        (use one per stream of work).  NULL
  *                                        selects a static schedule, which is
  *                                        also used for streams too short to
- *                                        gain from balancing. */
+ *                                        gain from balancing.
+ *   max_workgroups                       launch at most this many workgroups (0: as
+ *                                        many as fit on the GPU at once); a smaller
+ *                                        grid leaves CUs to kernels running
+ *                                        concurrently on other streams */
 typedef struct df11_device_stream {
     df11_header h;
     const uint8_t *enc;
@@ -147,6 +151,8 @@ typedef struct df11_device_stream {
     uint32_t decode_table_bits;
     uint32_t groups_per_workgroup;
     uint32_t *schedule;
+    uint32_t max_workgroups;
+    uint32_t reserved;
 } df11_device_stream;
 
 /* Accumulate the 256-bin exponent histogram of n BF16 words (host).

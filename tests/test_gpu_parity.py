@@ -165,8 +165,8 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
     every launch must leave them zero, and back-to-back launches must all be
     bit-exact.  The stream (64M weights with ~6-bit exponent codes, ~23K
     groups) is long enough for the dynamic schedule at two groups per
-    workgroup; one group per workgroup, four, and the static schedule must
-    give the same bytes."""
+    workgroup; one group per workgroup, four, the static schedule and grids
+    capped below one workgroup per CU must give the same bytes."""
     torch = torch_cuda
     w = _case("uniform_bits", 64 << 20, 11)
     _note(f"schedule dynamic={dynamic}")
@@ -184,6 +184,15 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
             assert np.array_equal(_to_u16(o), w), gpw
         assert not t._schedule.cpu().numpy().any()
         del outs
+    t.set_groups_per_workgroup(2)
+    for cap in (100, 7, 1):
+        t.set_max_workgroups(cap)
+        out = torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        t.decompress(out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(_to_u16(out), w), cap
+        assert not t._schedule.cpu().numpy().any()
+    t.set_max_workgroups(0)
 
 
 @pytest.mark.parametrize("bits", [10, 11, 12])
@@ -250,3 +259,35 @@ def test_lm_head_single_stream_full_size(torch_cuda):
     got, t = _gpu_decode(torch_cuda, w, bits=11)
     assert np.array_equal(got, w)
     assert t.header.n_elements == 128256 * 4096
+
+
+SMALL_BLOCK = [("q_proj", (1024, 1024)), ("k_proj", (256, 1024)), ("v_proj", (256, 1024)),
+               ("o_proj", (1024, 1024)), ("gate_proj", (3584, 1024)), ("up_proj", (3584, 1024)),
+               ("down_proj", (1024, 3584))]
+
+
+@pytest.mark.parametrize("overlap,cap", [(False, 0), (True, 0), (True, 24)])
+@pytest.mark.parametrize("codebook", ["shared", "per_weight"])
+def test_block_decoder_forward_matches_resident_weights(torch_cuda, overlap, cap, codebook):
+    """A synthetic 6-block forward whose weights are decompressed block by
+    block (in line, or block i + 1 on a side stream while block i computes,
+    with the decode's grid capped or not) gives the same bits as the forward
+    on the original BF16 weights."""
+    torch = torch_cuda
+    from entropy_decoding_df11_amd import runtime
+    _note(f"block decoder overlap={overlap} cap={cap} codebook={codebook}")
+    blocks, resident = [], []
+    for b in range(6):
+        flat, views = workloads.gen_block(seed=100 + b, shapes=SMALL_BLOCK)
+        parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
+        blocks.append(df11.compress_block(parts, codebook=codebook))
+        resident.append({nm: torch.from_numpy(a.astype(np.int16)).to("cuda").view(torch.bfloat16)
+                         for nm, a in parts})
+    x = workloads.f32_to_bf16_bits(np.random.default_rng(9).standard_normal(64 * 1024) * 0.5).reshape(64, 1024)
+    x = torch.from_numpy(x.astype(np.int16)).to("cuda").view(torch.bfloat16)
+    ref = runtime.model_forward(x, resident)
+    pf = runtime.BlockDecoder(blocks, overlap=overlap, decode_workgroups=cap)
+    for _ in range(2):  # the scratch buffers are reused across passes
+        got = runtime.model_forward(x, pf)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
