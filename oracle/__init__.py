@@ -226,3 +226,29 @@ def gap_values(s: Dict) -> np.ndarray:
     """Unpack the 5-bit MSB-first gaps (test helper)."""
     bits = np.unpackbits(s["gaps"])[: 5 * s["n_threads"]].reshape(-1, 5).astype(np.uint32)
     return (bits * np.array([16, 8, 4, 2, 1], np.uint32)).sum(axis=1) if s["n_threads"] else np.zeros(0, np.uint32)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Values of BF16 bit patterns: a BF16 is the upper 16 bits of an IEEE
+    binary32 word, so widening it to float32 and then float64 is exact."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def linear(s: Dict, x: np.ndarray, out_features: int) -> np.ndarray:
+    """y = x W^T in float64, W being the stream decoded (tree walk) and viewed
+    as an out_features x in_features row-major matrix, x an n_tokens x
+    in_features matrix of BF16 patterns.
+
+    The page's section "Dekompresi yang disesuaikan untuk inferensi GPU" uses
+    each decompressed weight matrix in a matrix multiplication; the section
+    "Opini Hacker News" suggests decompressing inside the GEMM.  The oracle
+    keeps the two steps apart: decode the whole matrix, then one float64
+    matmul (each BF16 x BF16 product is exact in float64)."""
+    w = decode_treewalk(s)
+    if out_features <= 0 or w.size % out_features:
+        raise ValueError("the stream does not hold out_features whole rows")
+    in_features = w.size // out_features
+    wm = bf16_to_f64(w).reshape(out_features, in_features)
+    xm = bf16_to_f64(np.asarray(x)).reshape(-1, in_features)
+    return xm @ wm.T

@@ -475,3 +475,85 @@ def test_planted_mistakes_are_caught(workload):
     cost_good = int((s["hist"] * s["code_lengths"].astype(np.uint64)).sum())
     cost_bad = int((s["hist"] * lens.astype(np.uint64)).sum())
     assert cost_bad > cost_good
+
+
+# ---------------------------------------------------------------------------
+# The decompressed matrix in a matmul ("Dekompresi yang disesuaikan untuk
+# inferensi GPU"; a GEMM consuming decoded tiles, "Opini Hacker News")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,value", [(0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133), (0x8000, -0.0),
+                                        (0x7F7F, (2 - 2 ** -7) * 2.0 ** 127), (0x3E20, 0.15625)])
+def test_bf16_values(bits, value):
+    got = oracle.bf16_to_f64(np.array([bits], np.uint16))[0]
+    assert got == value and math.copysign(1.0, got) == math.copysign(1.0, value)
+
+
+def _bf16_of_ints(v):
+    """BF16 patterns of small integers (|v| < 256 is exact in 8 significant bits)."""
+    return workloads.f32_to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_linear_one_hot_tokens_pick_columns():
+    """A token that is 1 at column c and 0 elsewhere yields column c of W:
+    y[t, r] = W[r, c_t] exactly.  A transposed W, or rows and columns swapped
+    in the reshape, picks the wrong entries."""
+    rng = np.random.default_rng(0)
+    out_f, in_f = 37, 24
+    w = workloads.f32_to_bf16_bits(rng.standard_normal(out_f * in_f).astype(np.float32) * 0.02)
+    s = oracle.encode(w)
+    cols = [0, 5, 23, 11]
+    x = np.zeros((len(cols), in_f), np.uint16)
+    for t, c in enumerate(cols):
+        x[t, c] = 0x3F80
+    y = oracle.linear(s, x, out_f)
+    assert y.shape == (len(cols), out_f)
+    wv = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(out_f, in_f)
+    for t, c in enumerate(cols):
+        assert np.array_equal(y[t], wv[:, c])
+
+
+def test_linear_small_integers_exact():
+    """Integer weights and tokens: every product and partial sum is an
+    integer far below 2^53, so y equals the integer dot products exactly,
+    computed here with Python integers."""
+    rng = np.random.default_rng(1)
+    out_f, in_f, T = 9, 40, 3
+    wi = rng.integers(-8, 9, (out_f, in_f))
+    xi = rng.integers(-5, 6, (T, in_f))
+    s = oracle.encode(_bf16_of_ints(wi.ravel()))
+    y = oracle.linear(s, _bf16_of_ints(xi), out_f)
+    for t in range(T):
+        for r in range(out_f):
+            assert y[t, r] == sum(int(xi[t, c]) * int(wi[r, c]) for c in range(in_f))
+
+
+def test_linear_matches_exact_rational_sum():
+    """Random BF16 weights and tokens of mixed magnitude: the float64 result
+    lies within the float64 summation bound of the exact rational dot
+    product (each BF16 value is a dyadic rational, so Fraction is exact)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(2)
+    out_f, in_f, T = 6, 64, 2
+    w = workloads.f32_to_bf16_bits((rng.standard_normal(out_f * in_f) * np.exp(rng.uniform(-20, 5, out_f * in_f)))
+                                   .astype(np.float32))
+    x = workloads.f32_to_bf16_bits(rng.standard_normal(T * in_f).astype(np.float32)).reshape(T, in_f)
+    s = oracle.encode(w)
+    y = oracle.linear(s, x, out_f)
+
+    def frac(bits):
+        return Fraction((np.array([bits], np.uint16).astype(np.uint32) << 16).view(np.float32)[0].item())
+
+    wf = [[frac(w[r * in_f + c]) for c in range(in_f)] for r in range(out_f)]
+    xf = [[frac(x[t, c]) for c in range(in_f)] for t in range(T)]
+    for t in range(T):
+        for r in range(out_f):
+            exact = sum(xf[t][c] * wf[r][c] for c in range(in_f))
+            mag = sum(abs(xf[t][c] * wf[r][c]) for c in range(in_f))
+            assert abs(Fraction(y[t, r]) - exact) <= Fraction(in_f) * Fraction(2) ** -53 * mag
+
+
+def test_linear_rejects_partial_rows():
+    s = oracle.encode(_bf16_of_ints(np.arange(10) % 7))
+    with pytest.raises(ValueError):
+        oracle.linear(s, np.zeros((1, 3), np.uint16), 3)
