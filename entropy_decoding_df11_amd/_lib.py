@@ -26,6 +26,8 @@ STATUS_NAMES = {
 MAX_LUTS = 17
 SCHEDULE_WORDS = 144  # DF11_SCHEDULE_WORDS
 MAX_BATCH = 16  # DF11_MAX_BATCH
+LINEAR_MAX_TOKENS = 8  # DF11_LINEAR_MAX_TOKENS
+LINEAR_MIN_IN_FEATURES = 512  # DF11_LINEAR_MIN_IN_FEATURES
 
 # Every function the header declares; the ABI test checks each is exported.
 EXPORTED = [
@@ -39,6 +41,8 @@ EXPORTED = [
     "df11_decompress_block",
     "df11_decompress_batch",
     "df11_decompress_timed",
+    "df11_linear",
+    "df11_linear_timed",
     "df11_status_str",
 ]
 
@@ -139,6 +143,11 @@ def load() -> ctypes.CDLL:
                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
         "df11_decompress_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_linear": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_linear_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                             ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
         "df11_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

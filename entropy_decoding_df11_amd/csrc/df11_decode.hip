@@ -32,7 +32,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
+#include <vector>
 
 #include <stdint.h>
 #include <string.h>
@@ -85,6 +87,18 @@ struct DecodeArgs {
     uint32_t pad2;
 };
 
+// The fused decode + matmul: y = x W^T, W (out_features x in_features,
+// row-major) being the decoded stream.
+struct MatmulArgs {
+    const uint16_t *x;     // n_tokens x in_features BF16, row-major, 16-byte aligned
+    float *y;              // n_tokens x out_features, zero when the kernel starts
+    uint64_t row_magic;    // floor(2^64 / in_features) + 1: row of element i = umulhi64(i, row_magic)
+    uint32_t in_features;  // a multiple of 8, at least 512
+    uint32_t out_features;
+    uint32_t n_tokens;     // 1 .. the kernel's token slots
+    uint32_t yacc_rows;    // rows of W that one group's outputs can touch
+};
+
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
 
 // Continue a code longer than the first-level window through the LUT
@@ -117,6 +131,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
     x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
+}
+
+// Sum of v over the wave, complete in lane 63 (the scan above on floats).
+__device__ __forceinline__ float wave_total(float v) {
+#define DF11_DPP_ADD(ctrl, rows)                                                                           \
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), ctrl, rows, 0xF, false))
+    DF11_DPP_ADD(0x111, 0xF);
+    DF11_DPP_ADD(0x112, 0xF);
+    DF11_DPP_ADD(0x114, 0xF);
+    DF11_DPP_ADD(0x118, 0xF);
+    DF11_DPP_ADD(0x142, 0xA);
+    DF11_DPP_ADD(0x143, 0xC);
+#undef DF11_DPP_ADD
+    return v;
 }
 
 __device__ __forceinline__ uint32_t bitfield_insert(uint32_t mask, uint32_t a, uint32_t b) {
@@ -291,6 +319,121 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
 }
 
+// Fused matmul (y = x W^T) in place of the store.  Chunk k of a group (W's
+// elements 8 (c0 + k) .. + 7, all in one row since in_features is a multiple
+// of 8) times the tokens' matching 8 columns of x gives each lane one partial
+// sum per token.  The wave adds its lanes' sums per row (64 consecutive chunks
+// span at most two rows, as in_features >= 512) and lane 63 adds the wave's
+// into the workgroup's LDS row sums, which flush_rows later adds into y.
+// Chunk k's LDS cell is read and zeroed for the next group when k < n_chunks;
+// only elements in [lo, hi) count.  Every lane of the wave must call this
+// together (k = wave's first chunk + lane).
+template <int TB>
+__device__ __forceinline__ void matmul_chunk(const MatmulArgs &m, uint8_t *ebuf, uint32_t c0, uint32_t k,
+                                             uint32_t n_chunks, uint64_t s8, uint32_t lo, uint32_t hi,
+                                             uint32_t row0, float *yacc) {
+    const uint32_t i0 = 8u * (c0 + k);
+    uint64_t r8 = 0;
+    if (k < n_chunks) {
+        uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
+        r8 = *cell;
+        *cell = 0;
+    }
+    const bool active = k < n_chunks && i0 + 8u > lo && i0 < hi;
+    const uint64_t act = __builtin_amdgcn_ballot_w64(active);
+    if (!act) return;
+    float p[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) p[t] = 0.0f;
+    uint32_t row = 0;
+    if (active) {
+        const uint4 v = merge8(s8, r8);
+        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __uint_as_float(e & 1 ? vw[e >> 1] & 0xFFFF0000u : vw[e >> 1] << 16);
+        if (i0 < lo || i0 + 8u > hi) {
+#pragma unroll
+            for (uint32_t e = 0; e < 8; ++e)
+                if (i0 + e < lo || i0 + e >= hi) w[e] = 0.0f;
+        }
+        row = static_cast<uint32_t>(__umul64hi(i0, m.row_magic));
+        const uint16_t *xc = m.x + (i0 - row * m.in_features);
+        uint4 xv[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            xv[t] = t < static_cast<int>(m.n_tokens)
+                        ? *reinterpret_cast<const uint4 *>(xc + static_cast<size_t>(t) * m.in_features)
+                        : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+            float acc = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc = fmaf(w[e], __uint_as_float(e & 1 ? xw[e >> 1] & 0xFFFF0000u : xw[e >> 1] << 16), acc);
+            p[t] = acc;
+        }
+    }
+    const uint32_t r0 = __builtin_amdgcn_readlane(row, static_cast<uint32_t>(__builtin_ctzll(act)));
+    const bool in_b = active && row != r0;  // then row == r0 + 1
+    const bool two = __builtin_amdgcn_ballot_w64(in_b) != 0;
+    const bool last = (threadIdx.x & (kWaveSize - 1)) == kWaveSize - 1;
+    float *ya = yacc + (r0 - row0) * TB;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        if (t >= static_cast<int>(m.n_tokens)) break;
+        const float sa = wave_total(in_b ? 0.0f : p[t]);
+        if (last) __hip_atomic_fetch_add(ya + t, sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (two) {
+            const float sb = wave_total(in_b ? p[t] : 0.0f);
+            if (last) __hip_atomic_fetch_add(ya + TB + t, sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+}
+
+// merge_group's counterpart for the fused matmul: the group's elements [lo,
+// hi) (the ones merge_group would store) go into the LDS row sums yacc, whose
+// first row is row0 and which cover `rows` rows (both returned for
+// flush_rows).
+template <int TB>
+__device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulArgs &m, uint8_t *ebuf,
+                                             const uint64_t (&sm)[kPrefetchChunks], uint32_t base, uint32_t end,
+                                             uint32_t ltid, bool skip_first, bool whole_last, float *yacc,
+                                             uint32_t &row0, uint32_t &rows) {
+    const uint32_t c0 = base >> 3;
+    const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
+    const uint32_t lo = skip_first ? (base + 7u) & ~7u : base;
+    const uint32_t hi = whole_last ? (end + 7u) & ~7u : end;
+    row0 = static_cast<uint32_t>(__umul64hi(lo, m.row_magic));
+    rows = lo < hi ? min(static_cast<uint32_t>(__umul64hi(hi - 1u, m.row_magic)) - row0 + 1u, m.yacc_rows) : 0u;
+#pragma unroll
+    for (int j = 0; j < kPrefetchChunks; ++j)
+        matmul_chunk<TB>(m, ebuf, c0, ltid + j * kThreadsPerGroup, n_chunks, sm[j], lo, hi, row0, yacc);
+    // Further chunks a wave at a time, so that every lane takes part in the sums.
+    const uint32_t lane = ltid & (kWaveSize - 1);
+    for (uint32_t kb = kPrefetchChunks * kThreadsPerGroup + ltid - lane; kb < n_chunks; kb += kThreadsPerGroup) {
+        const uint32_t c = min(c0 + kb + lane, a.sm_chunks - 1u);
+        const uint64_t s8 = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
+        matmul_chunk<TB>(m, ebuf, c0, kb + lane, n_chunks, s8, lo, hi, row0, yacc);
+    }
+    if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+}
+
+// Add a group's LDS row sums into y (other workgroups add the other parts
+// of rows that cross groups) and zero them for the next group.  Called by
+// the group's threads after a barrier that follows merge_matmul.
+template <int TB>
+__device__ __forceinline__ void flush_rows(const MatmulArgs &m, float *yacc, uint32_t row0, uint32_t rows,
+                                           uint32_t ltid) {
+    for (uint32_t i = ltid; i < rows * TB; i += kThreadsPerGroup) {
+        const float v = yacc[i];
+        yacc[i] = 0.0f;
+        const uint32_t t = i % TB;
+        if (t < m.n_tokens) unsafeAtomicAdd(m.y + static_cast<size_t>(t) * m.out_features + row0 + i / TB, v);
+    }
+}
+
 // Group edges.  When a group's first element is not a multiple of 8, the
 // group shares an 8-element output chunk with the previous group; stored
 // separately, each half of it would be a partial write of one cache line from
@@ -457,11 +600,16 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 // barrier.  Every wait for loaded data therefore comes a whole decode phase
 // after the last stores were issued.  One buffer per group (rather than two)
 // keeps the LDS of a 512-thread workgroup small enough for four per CU.
-template <int K, int GPW>
-__device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_t wg, const uint32_t n_wg) {
+//
+// TB > 0 turns the merge into the fused matmul with up to TB tokens
+// (merge_matmul and flush_rows in place of merge_group).
+template <int K, int GPW, int TB>
+__device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulArgs &m, const uint32_t wg,
+                                              const uint32_t n_wg) {
     // Static LDS: the first-level table (lo words | aux words | start masks)
     // at a fixed address, so a lookup's address is its index times 4.
-    // Dynamic LDS: LUTs | CodeLengths | GPW exponent buffers | wave sums.
+    // Dynamic LDS: LUTs | CodeLengths | GPW exponent buffers | wave sums |
+    // edge flags | ticket | (fused matmul) GPW row-sum arrays.
     __shared__ __align__(16) uint32_t s_tab[(10u << K) / 4u];
     extern __shared__ __align__(16) uint8_t smem[];
     const uint32_t *s_lo = s_tab;
@@ -481,6 +629,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_
     uint32_t *s_edge = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * kWaves + slot * 2u;
     // The next super-group of the dynamic schedule, from thread 0.
     uint32_t *s_ticket = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * (kWaves + 2u);
+    // The fused matmul's row sums (yacc_rows x TB floats per group).
+    float *s_yacc = reinterpret_cast<float *>(s_ticket + 4) + slot * m.yacc_rows * TB;
+    uint32_t y_row0 = 0, y_rows = 0;  // rows of the merged group awaiting flush_rows
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
     uint32_t *const sched = a.sched;
@@ -521,6 +672,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_
         // the merge zeroes every chunk it consumes).
         uint4 *z = reinterpret_cast<uint4 *>(s_clen + 256u);
         for (uint32_t i = tid; i < GPW * a.ebuf_cap / 16u; i += kThreads) z[i] = make_uint4(0, 0, 0, 0);
+        if constexpr (TB > 0) {
+            float *y0 = reinterpret_cast<float *>(s_ticket + 4);
+            for (uint32_t i = tid; i < GPW * m.yacc_rows * TB; i += kThreads) y0[i] = 0.0f;
+        }
         // Unconditional stores (indices clamped like the loads: extra lanes
         // write the last element's value to it again), so the compiler cannot
         // sink each load into a branch next to its store.
@@ -557,7 +712,13 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_
         // 2. Merge and store the super-group decoded in the previous
         // iteration, then load this group's sign/mantissa chunks (into the
         // registers the merge has just consumed) for the next one.
-        if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+        if (it > 0) {
+            if constexpr (TB == 0)
+                merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+            else
+                merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc,
+                                 y_row0, y_rows);
+        }
         load_sm(a, base, end, ltid, sm);
 
         // 3. Decode this super-group.
@@ -613,6 +774,12 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_
         const uint32_t incl = wave_inclusive_scan(cnt);
         if (lane == kWaveSize - 1) s_wsum[wave] = incl;
         __syncthreads();
+        if constexpr (TB > 0) {
+            // The barrier completed the merge's LDS sums; the one at the end
+            // of the iteration orders the zeroing before the next merge.
+            flush_rows<TB>(m, s_yacc, y_row0, y_rows, ltid);
+            y_rows = 0;
+        }
         uint32_t wave_off = 0;
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
@@ -677,14 +844,21 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const uint32_
         ticket = fetched;
         s_cur = s_nx;
     }
-    merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+    if constexpr (TB == 0) {
+        merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+    } else {
+        merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc, y_row0,
+                         y_rows);
+        __syncthreads();
+        flush_rows<TB>(m, s_yacc, y_row0, y_rows, ltid);
+    }
     finish_schedule(sched, n_wg);
 }
 
 // One stream over the whole grid.
 template <int K, int GPW>
 __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
-    decode_stream<K, GPW>(a, blockIdx.x, gridDim.x);
+    decode_stream<K, GPW, 0>(a, MatmulArgs{}, blockIdx.x, gridDim.x);
 }
 
 // Several independent streams (each with its own codebook and output) in one
@@ -709,7 +883,20 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_batch_kerne
     const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
     uint32_t i = 0;
     while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
-    decode_stream<K, GPW>(b.s[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+    decode_stream<K, GPW, 0>(b.s[i], MatmulArgs{}, id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+}
+
+// Decode fused with y = x W^T for up to TB tokens: W's BF16 never leaves the
+// workgroup.  y must be zero at the start (df11_zero_kernel, launched first).
+constexpr int kLinearGPW = 2;
+
+template <int K, int TB>
+__global__ __launch_bounds__(kThreadsPerGroup *kLinearGPW) void df11_linear_kernel(DecodeArgs a, MatmulArgs m) {
+    decode_stream<K, kLinearGPW, TB>(a, m, blockIdx.x, gridDim.x);
+}
+
+__global__ __launch_bounds__(256) void df11_zero_kernel(float *y, uint32_t n) {
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) y[i] = 0.0f;
 }
 
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
@@ -751,22 +938,26 @@ int validate(const df11_device_stream *s) {
     return DF11_OK;
 }
 
-// Workgroups of this kernel instance that fit on one CU, per device (0 until
-// first queried).
-template <int K, int GPW, bool kBatch>
-int resident_per_cu(int dev, size_t lds) {
-    static int cache[64] = {};
-    static size_t cache_lds[64] = {};
-    if (dev >= 0 && dev < 64 && cache[dev] > 0 && cache_lds[dev] == lds) return cache[dev];
-    int per_cu = 0;
-    const void *fn = kBatch ? reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>)
-                            : reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreadsPerGroup * GPW, lds) != hipSuccess)
-        return 0;
-    if (dev >= 0 && dev < 64) {
-        cache[dev] = per_cu;
-        cache_lds[dev] = lds;
+// Workgroups of kernel fn (with `threads` threads and `lds` bytes of dynamic
+// LDS) that fit on one CU of device dev, cached per (kernel, device, LDS).
+int resident_per_cu(const void *fn, uint32_t threads, int dev, size_t lds) {
+    struct Entry {
+        const void *fn;
+        int dev;
+        size_t lds;
+        int per_cu;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (e.fn == fn && e.dev == dev && e.lds == lds) return e.per_cu;
     }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_cu > 0 && cache.size() < 256) cache.push_back({fn, dev, lds, per_cu});
     return per_cu;
 }
 
@@ -809,7 +1000,8 @@ int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t 
     const size_t lds = dynamic_lds<GPW>(a);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
-    const int per_cu = resident_per_cu<K, GPW, false>(dev, lds);
+    const void *fn = reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * GPW, dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
@@ -822,8 +1014,8 @@ int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t 
     void *params[] = {&args};
     // hipExtLaunchKernel records start / stop (when given) at the kernel's own
     // start and end, not around the launch.
-    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>), dim3(grid),
-                           dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) != hipSuccess)
+    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) !=
+        hipSuccess)
         return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
@@ -851,7 +1043,8 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
     }
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
-    const int per_cu = resident_per_cu<K, GPW, true>(dev, lds);
+    const void *fn = reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * GPW, dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
@@ -873,11 +1066,13 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
         }
     (void)hipGetLastError();
     void *params[] = {&b};
-    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>), dim3(next),
-                           dim3(kThreadsPerGroup * GPW), params, lds, stream, nullptr, nullptr, 0) != hipSuccess)
+    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, nullptr, nullptr, 0) !=
+        hipSuccess)
         return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
+
+void fill_args(const df11_device_stream *s, DecodeArgs &a);
 
 // Checks s and out (no launch) and fills the kernel arguments of one stream.
 int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
@@ -894,7 +1089,14 @@ int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
         overlaps(out, out_bytes, s->decode_table, df11_decode_table_bytes(bits)) ||
         overlaps(out, out_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
         return DF11_E_INVALID_ARG;
+    fill_args(s, a);
+    a.out = out;
+    return DF11_OK;
+}
 
+// Kernel arguments of a validated, non-empty stream (no output).
+void fill_args(const df11_device_stream *s, DecodeArgs &a) {
+    const df11_header &h = s->h;
     a = DecodeArgs{};
     a.enc = s->enc;
     a.sm = s->sm;
@@ -903,7 +1105,6 @@ int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
     a.luts = s->luts;
     a.code_lengths = s->code_lengths;
     a.dtab = static_cast<const uint32_t *>(s->decode_table);
-    a.out = out;
     a.total_bits = h.total_bits;
     a.n_elements = static_cast<uint32_t>(h.n_elements);
     a.n_threads = static_cast<uint32_t>(h.n_threads);
@@ -915,7 +1116,6 @@ int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
     a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
     a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
     a.sched = s->schedule;
-    return DF11_OK;
 }
 
 int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
@@ -987,6 +1187,84 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
 #undef DF11_BATCH_CASE
 }
 
+// y = 0 (zero kernel), then the fused kernel over the persistent grid.
+template <int K, int TB>
+int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream,
+                  hipEvent_t start, hipEvent_t stop) {
+    const size_t lds = dynamic_lds<kLinearGPW>(a) + sizeof(float) * kLinearGPW * m.yacc_rows * TB;
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const void *fn = reinterpret_cast<const void *>(&df11_linear_kernel<K, TB>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kLinearGPW, dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
+    const uint64_t n_super = (a.n_groups + kLinearGPW - 1) / kLinearGPW;
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, max_wg);
+    (void)hipGetLastError();
+    DecodeArgs args = a;
+    MatmulArgs margs = m;
+    const uint32_t grid = schedule_pools(args, n_super, resident);
+    const uint32_t n_y = m.n_tokens * m.out_features;
+    float *y = m.y;
+    void *zparams[] = {&y, const_cast<uint32_t *>(&n_y)};
+    const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((n_y + 255) / 256, 1024));
+    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256), zparams, 0,
+                           stream, start, nullptr, 0) != hipSuccess)
+        return DF11_E_HIP;
+    void *params[] = {&args, &margs};
+    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, nullptr, stop,
+                           0) != hipSuccess)
+        return DF11_E_HIP;
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+}
+
+int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    int rc = validate(s);
+    if (rc) return rc;
+    const df11_header &h = s->h;
+    if (n_tokens < 1 || n_tokens > DF11_LINEAR_MAX_TOKENS || in_features < DF11_LINEAR_MIN_IN_FEATURES ||
+        in_features % 8 || static_cast<uint64_t>(in_features) * out_features != h.n_elements)
+        return DF11_E_INVALID_ARG;
+    if (h.n_elements == 0) return DF11_OK;
+    if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return DF11_E_INVALID_ARG;
+    const uint64_t y_bytes = 4ull * n_tokens * out_features, x_bytes = 2ull * n_tokens * in_features;
+    if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, s->enc, h.enc_bytes) ||
+        overlaps(y, y_bytes, s->sm, h.sm_bytes) || overlaps(y, y_bytes, s->gaps, h.gaps_bytes) ||
+        overlaps(y, y_bytes, s->out_pos, h.out_pos_bytes) || overlaps(y, y_bytes, s->luts, 256ull * h.n_luts) ||
+        overlaps(y, y_bytes, s->code_lengths, 256) ||
+        overlaps(y, y_bytes, s->decode_table, df11_decode_table_bytes(s->decode_table_bits)) ||
+        overlaps(y, y_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
+        return DF11_E_INVALID_ARG;
+    if (y_bytes / 4 >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    DecodeArgs a;
+    fill_args(s, a);
+    MatmulArgs m{};
+    m.x = x;
+    m.y = y;
+    m.row_magic = ~0ull / in_features + 1ull;  // umulhi64(i, row_magic) == i / in_features for all i < 2^32
+    m.in_features = in_features;
+    m.out_features = out_features;
+    m.n_tokens = n_tokens;
+    m.yacc_rows = (a.ebuf_cap - 1u) / in_features + 2u;
+    const uint32_t tb = n_tokens <= 1 ? 1 : n_tokens <= 2 ? 2 : n_tokens <= 4 ? 4 : 8;
+#define DF11_LINEAR_CASE(KB)                                                       \
+    case KB:                                                                       \
+        switch (tb) {                                                              \
+        case 1: return launch_linear<KB, 1>(a, m, s->max_workgroups, stream, start, stop); \
+        case 2: return launch_linear<KB, 2>(a, m, s->max_workgroups, stream, start, stop); \
+        case 4: return launch_linear<KB, 4>(a, m, s->max_workgroups, stream, start, stop); \
+        default: return launch_linear<KB, 8>(a, m, s->max_workgroups, stream, start, stop); \
+        }
+    switch (s->decode_table_bits) {
+        DF11_LINEAR_CASE(10)
+        DF11_LINEAR_CASE(11)
+        DF11_LINEAR_CASE(12)
+    default: return DF11_E_INVALID_ARG;
+    }
+#undef DF11_LINEAR_CASE
+}
+
 }  // namespace
 
 extern "C" {
@@ -1010,6 +1288,18 @@ int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_
                           void *stop_event) {
     return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
                            static_cast<hipEvent_t>(stop_event));
+}
+
+int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, void *hip_stream) {
+    return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
+                       nullptr);
+}
+
+int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                      uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event) {
+    return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream),
+                       static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"

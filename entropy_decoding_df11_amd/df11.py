@@ -233,6 +233,44 @@ class DF11Tensor:
                                              ctypes.c_void_p(_event_handle(stop, st))), "df11_decompress_timed")
 
 
+    def linear(self, x: "torch.Tensor", out: Optional["torch.Tensor"] = None, stream=None,  # noqa: F821
+               events=None) -> "torch.Tensor":  # noqa: F821
+        """y = x W^T with the decode fused into the product (df11_linear): W
+        is this tensor as an (out_features, in_features) matrix, x a
+        contiguous bfloat16 (n_tokens, in_features) tensor on the same device
+        with 1 <= n_tokens <= 8.  Returns out, a float32 (n_tokens,
+        out_features) tensor (a new one by default).  events: as for
+        decompress, recorded around the zeroing and fused kernels."""
+        import torch
+        if len(self.shape) != 2:
+            raise ValueError("linear needs a 2-D weight (out_features, in_features)")
+        out_f, in_f = self.shape
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
+            raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
+        dev = torch.device(self.device)
+        if x.device.type != dev.type or x.device.index != (dev.index if dev.index is not None
+                                                          else torch.cuda.current_device()):
+            raise ValueError("x must be on the weight's device")
+        n_tokens = x.shape[0]
+        if out is None:
+            out = torch.empty((n_tokens, out_f), dtype=torch.float32, device=self.device)
+        if out.dtype != torch.float32 or out.shape != (n_tokens, out_f) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 (n_tokens, out_features) tensor")
+        lib = _lib.load()
+        st = self._hip_stream(stream)
+        args = (ctypes.byref(self._stream_struct), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, out_f,
+                ctypes.c_void_p(out.data_ptr()), st)
+        if events is None:
+            _lib.check(lib.df11_linear(*args), "df11_linear")
+        else:
+            start, stop = events
+            _lib.check(lib.df11_linear_timed(*args, ctypes.c_void_p(_event_handle(start, st)),
+                                             ctypes.c_void_p(_event_handle(stop, st))), "df11_linear_timed")
+        return out
+
+
 def _event_handle(ev, stream: ctypes.c_void_p) -> int:
     """The hipEvent_t behind a torch.cuda.Event, created by recording it once
     on the launch stream (the decode launch records it again)."""

@@ -59,6 +59,9 @@ typedef enum df11_status {
 #define DF11_SCHEDULE_WORDS 144
 /* Most streams one df11_decompress_batch call decodes. */
 #define DF11_MAX_BATCH 16
+/* Token rows and smallest row length of df11_linear. */
+#define DF11_LINEAR_MAX_TOKENS 8
+#define DF11_LINEAR_MIN_IN_FEATURES 512
 
 /* The codebook shared by all tensors of one stream (host, plain data).
  *   code_lengths[e]: Huffman code length of exponent e, 0 if unused
@@ -253,6 +256,40 @@ int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams,
  * stream of N = 0 nothing is launched and the events are not recorded. */
 int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,
                           void *stop_event);
+
+/* y = x W^T with the decompression fused into the matrix product: W is the
+ * stream decoded and viewed as an out_features x in_features row-major BF16
+ * matrix, and its BF16 values never reach HBM.  The page's section
+ * "Dekompresi yang disesuaikan untuk inferensi GPU" decompresses each weight
+ * matrix right before its matrix multiplication; the section "Opini Hacker
+ * News" suggests a GEMM that decompresses each tile before the arithmetic,
+ * which this is for small token counts (token-by-token generation), where the
+ * product is bound by reading W.
+ *   w             device stream, h.n_elements == out_features * in_features
+ *   x             device, n_tokens x in_features BF16 (uint16 bit patterns),
+ *                 row-major, 16-byte aligned; read only
+ *   n_tokens      1 .. DF11_LINEAR_MAX_TOKENS
+ *   in_features   a multiple of 8, at least DF11_LINEAR_MIN_IN_FEATURES
+ *   y             device, n_tokens x out_features float, row-major, 4-byte
+ *                 aligned, overlapping neither x nor the stream's buffers;
+ *                 every element is overwritten
+ * y[t][r] is the sum over c of x[t][c] * W[r][c], each product exact in float
+ * and the sums taken in float in an unspecified order (atomic adds), so the
+ * low bits can differ between calls.  Enqueued on hip_stream (a zeroing kernel
+ * for y, then the decode kernel); uses w's schedule counters like
+ * df11_decompress, so calls sharing a stream descriptor must not overlap in
+ * time.  Errors: DF11_E_INVALID_ARG (sizes, alignment, overlap, or as for
+ * df11_decompress), DF11_E_BAD_STREAM, DF11_E_TOO_LARGE (n_tokens *
+ * out_features >= 2^32), DF11_E_HIP.  With N = 0 (out_features = 0) nothing
+ * is launched. */
+int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, void *hip_stream);
+
+/* df11_linear with start_event recorded when the zeroing kernel starts and
+ * stop_event when the fused kernel ends (hipEvent_t, either may be NULL), to
+ * measure the fused product.  Same arguments, output and errors. */
+int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                      uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
 /* Static, human-readable name of a status code. */
 const char *df11_status_str(int status);

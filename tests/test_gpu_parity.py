@@ -291,3 +291,116 @@ def test_block_decoder_forward_matches_resident_weights(torch_cuda, overlap, cap
         got = runtime.model_forward(x, pf)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Decode fused into the matrix product (df11_linear): y = x W^T
+# ---------------------------------------------------------------------------
+
+def _linear_bound(x_bits, w_bits, out_f, in_f):
+    """Largest allowed |y_gpu - y_oracle| per output.  Every BF16 x BF16
+    product is exact in float32, and the kernel adds the in_f products of
+    an output in float32 in some order (lane, wave, LDS and global atomic
+    sums).  With u = 2^-24 the error of any such order is at most
+    gamma_n * sum |x w| with n = in_f additions, and gamma_n = n u / (1 - n u)
+    < 1.01 n u for n u < 0.01."""
+    xa = np.abs(oracle.bf16_to_f64(x_bits).reshape(-1, in_f))
+    wa = np.abs(oracle.bf16_to_f64(w_bits).reshape(out_f, in_f))
+    return 1.01 * in_f * 2.0 ** -24 * (xa @ wa.T)
+
+
+def _tokens(n_tokens, in_f, seed):
+    x = np.random.default_rng(seed).standard_normal(n_tokens * in_f) * 0.5
+    return workloads.f32_to_bf16_bits(x).reshape(n_tokens, in_f)
+
+
+def _check_linear(torch, t, w, x, out_f, in_f, calls=2):
+    ref = oracle.linear(oracle.encode(w), x, out_f)
+    bound = _linear_bound(x, w, out_f, in_f)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    for _ in range(calls):  # y is overwritten on every call
+        y = t.linear(xd)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        assert got.shape == ref.shape
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+
+
+LINEAR_CASES = [  # (weights, out_features, in_features)
+    ("normal", 300, 1024),        # ~50 groups; rows inside groups and across their edges
+    ("student_t", 77, 4104),      # rows not a multiple of 512 long
+    ("normal", 1000, 512),        # the shortest rows: several rows per group
+    ("stress_tuned", 40, 14336),  # codes through the LUT hierarchy; rows longer than a group
+    ("fib_chain", 129, 2048),     # 4 LUT levels
+    ("zeros", 64, 1024),          # one exponent: y is exactly zero
+]
+
+
+@pytest.mark.parametrize("kind,out_f,in_f", LINEAR_CASES)
+@pytest.mark.parametrize("n_tokens", [1, 2, 5, 8])
+def test_linear_matches_oracle(torch_cuda, kind, out_f, in_f, n_tokens):
+    torch = torch_cuda
+    _note(f"linear {kind} {out_f}x{in_f} tokens={n_tokens}")
+    w = _case(kind, out_f * in_f, 21)
+    x = _tokens(n_tokens, in_f, n_tokens)
+    t = df11.compress(w, shape=(out_f, in_f))
+    _check_linear(torch, t, w, x, out_f, in_f)
+
+
+@pytest.mark.parametrize("bits", [10, 12])
+def test_linear_table_widths(torch_cuda, bits):
+    torch = torch_cuda
+    _note(f"linear bits={bits}")
+    w = _case("student_t", 300 * 1024, 5)
+    t = df11.compress(w, shape=(300, 1024), decode_table_bits=bits)
+    _check_linear(torch, t, w, _tokens(4, 1024, 7), 300, 1024)
+
+
+def test_linear_capped_grid_and_dynamic_schedule(torch_cuda):
+    """With a grid of 3 or 7 workgroups the stream (~160 groups) runs on the
+    dynamic schedule; the result must not change and the counters must be
+    left at zero."""
+    torch = torch_cuda
+    w = _case("normal", 1000 * 1024, 8)
+    t = df11.compress(w, shape=(1000, 1024))
+    x = _tokens(3, 1024, 9)
+    for cap in (3, 7):
+        _note(f"linear cap={cap}")
+        t.set_max_workgroups(cap)
+        _check_linear(torch, t, w, x, 1000, 1024, calls=1)
+        assert not t._schedule.cpu().numpy().any()
+    t.set_max_workgroups(0)
+
+
+def test_linear_argument_errors(torch_cuda):
+    torch = torch_cuda
+    w = _case("normal", 64 * 1024, 1)
+    t = df11.compress(w, shape=(64, 1024))
+    x = torch.zeros((9, 1024), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(_lib_error()):
+        t.linear(x)  # more tokens than the fused kernel takes
+    with pytest.raises(ValueError):
+        t.linear(torch.zeros((2, 1000), dtype=torch.bfloat16, device="cuda"))
+
+
+def _lib_error():
+    from entropy_decoding_df11_amd import _lib
+    return _lib.Df11Error
+
+
+@pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
+def test_linear_full_size_block_matrix(torch_cuda, name):
+    """Llama-3-8B-shaped gate_proj (14336 x 4096) and down_proj (4096 x
+    14336), each its own stream, at 4 tokens: every output against the
+    oracle."""
+    torch = torch_cuda
+    shapes = dict(workloads.LLAMA3_8B_BLOCK)
+    out_f, in_f = shapes[name]
+    flat, views = workloads.gen_block(seed=3)
+    off = {nm: o for nm, o, _ in views}[name]
+    w = np.ascontiguousarray(flat[off:off + out_f * in_f])
+    del flat
+    _note(f"linear full size {name} {out_f}x{in_f}")
+    t = df11.compress(w, shape=(out_f, in_f))
+    _check_linear(torch, t, w, _tokens(4, in_f, 11), out_f, in_f, calls=1)

@@ -310,3 +310,45 @@ def test_decompress_batch_validation_runs_before_any_launch():
     assert call([s, s], [1 << 48, s.enc]) == -1
     # misaligned output
     assert call([s], [(1 << 48) + 8]) == -1
+
+
+def test_linear_constants_match_header():
+    import re
+    with open(os.path.join(os.path.dirname(__file__), "..", "include", "df11.h")) as f:
+        text = f.read()
+    assert int(re.search(r"#define\s+DF11_LINEAR_MAX_TOKENS\s+(\d+)", text).group(1)) == _lib.LINEAR_MAX_TOKENS
+    assert int(re.search(r"#define\s+DF11_LINEAR_MIN_IN_FEATURES\s+(\d+)", text).group(1)) == \
+        _lib.LINEAR_MIN_IN_FEATURES
+
+
+def test_linear_validation_runs_before_any_launch():
+    """Every df11_linear argument error is found before anything is launched
+    (no GPU here)."""
+    lib = _lib_or_skip()
+    host = df11.encode(workloads.gen_single_matrix(rows=64, cols=1024))
+    s = _fake_device_stream(host)
+    x, y = ctypes.c_void_p(1 << 48), ctypes.c_void_p((1 << 48) + (1 << 32))
+
+    def call(st, xp, t, i, o, yp):
+        return lib.df11_linear(ctypes.byref(st) if st is not None else None, xp, t, i, o, yp, None)
+
+    assert call(None, x, 1, 1024, 64, y) == -1
+    assert call(s, x, 0, 1024, 64, y) == -1                        # no tokens
+    assert call(s, x, _lib.LINEAR_MAX_TOKENS + 1, 1024, 64, y) == -1
+    assert call(s, x, 1, 1024, 63, y) == -1                        # out * in != N
+    assert call(s, x, 1, 256, 256, y) == -1                        # rows shorter than the minimum
+    big = _fake_device_stream(df11.encode(workloads.gen_single_matrix(rows=64, cols=1028)))
+    assert call(big, x, 1, 1028, 64, y) == -1                      # in_features not a multiple of 8
+    assert call(s, ctypes.c_void_p((1 << 48) + 8), 1, 1024, 64, y) == -1   # x misaligned
+    assert call(s, x, 1, 1024, 64, ctypes.c_void_p((1 << 48) + (1 << 32) + 2)) == -1  # y misaligned
+    assert call(s, x, 2, 1024, 64, ctypes.c_void_p((1 << 48) + 16)) == -1  # y overlaps x
+    assert call(s, x, 1, 1024, 64, ctypes.c_void_p(s.sm)) == -1    # y overlaps the stream
+    assert call(s, None, 1, 1024, 64, y) == -1
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.enc_bytes += 16
+    assert call(bad, x, 1, 1024, 64, y) == -6
+    # an empty stream (no rows) launches nothing
+    empty = df11.encode(np.zeros(0, np.uint16))
+    es = _lib.DeviceStream()
+    es.h = empty.header
+    assert lib.df11_linear(ctypes.byref(es), None, 1, 1024, 0, None, None) == 0
