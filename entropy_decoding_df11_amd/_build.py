@@ -31,6 +31,9 @@ HIP_FLAGS = [
     "-mcode-object-version=5",
     # Packed FP32 instructions are kept out of every HIP build.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Atomics are issued as written (the optimizer would wrap one-lane LDS
+    # adds in a loop over the active lanes).
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -254,19 +254,14 @@ __device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g,
     return r;
 }
 
-// Sign/mantissa chunks ltid + 256 j of the group with outputs [base, end),
-// loaded (clamped like load_group) one iteration before the merge uses them.
+// Sign/mantissa chunks of the group with outputs [base, end) that this
+// thread merges in its first kPrefetchChunks rounds, loaded (clamped like
+// load_group) one iteration before the merge uses them: chunk ltid + 256 j
+// for the store, or round j of the thread's wave run for the fused matmul
+// (run_chunk).
+template <int TB>
 __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
-                                        uint64_t (&sm)[kPrefetchChunks]) {
-    const uint32_t c0 = base >> 3;
-    const uint32_t nch = group_chunks(base, end);
-#pragma unroll
-    for (int j = 0; j < kPrefetchChunks; ++j) {
-        const uint32_t k = ltid + j * kThreadsPerGroup;
-        const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
-        sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
-    }
-}
+                                        uint64_t (&sm)[kPrefetchChunks]);
 
 // Byte offset of the first-level table entry (one uint32 per entry in each
 // array) for the K-bit window at bit p = acc & 63 of the 64-bit pair.
@@ -319,83 +314,100 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
 }
 
-// Fused matmul (y = x W^T) in place of the store.  Chunk k of a group (W's
-// elements 8 (c0 + k) .. + 7, all in one row since in_features is a multiple
-// of 8) times the tokens' matching 8 columns of x gives each lane one partial
-// sum per token.  The wave adds its lanes' sums per row (64 consecutive chunks
-// span at most two rows, as in_features >= 512) and lane 63 adds the wave's
-// into the workgroup's LDS row sums, which flush_rows later adds into y.
-// Chunk k's LDS cell is read and zeroed for the next group when k < n_chunks;
-// only elements in [lo, hi) count.  Every lane of the wave must call this
-// together (k = wave's first chunk + lane).
+// Fused matmul (y = x W^T) in place of the store.  A group's chunks are
+// split into four contiguous runs, one per wave, taken 64 chunks (one per
+// lane) per round; chunk k holds W's elements 8 (c0 + k) .. + 7, all in one
+// row since in_features is a multiple of 8.  Each lane multiplies its chunk
+// by the tokens' matching 8 columns of x (BF16 pairs straight into
+// v_dot2c_f32_bf16, whose products are exact in float) and keeps a running
+// sum per token for the wave's current row.  A round spans 512 elements, so
+// at most two rows (in_features >= 512); when the row changes the wave adds
+// its lanes' sums (DPP) and lane 63 adds them into the workgroup's LDS row
+// sums yacc, which flush_rows later adds into y.  The rows of one wave's run
+// only grow, so a wave reduces about once per row it touches.
+__device__ __forceinline__ uint32_t wave_rounds(uint32_t n_chunks) {
+    return (n_chunks + kThreadsPerGroup - 1u) / kThreadsPerGroup;
+}
+
+// Chunk of lane `lane` of wave `wave` in round j of a group with n_chunks
+// chunks (the runs of merge_matmul; load_sm prefetches the same chunks).
+__device__ __forceinline__ uint32_t run_chunk(uint32_t wave, uint32_t lane, uint32_t j, uint32_t n_chunks) {
+    return (wave * wave_rounds(n_chunks) + j) * kWaveSize + lane;
+}
+
 template <int TB>
-__device__ __forceinline__ void matmul_chunk(const MatmulArgs &m, uint8_t *ebuf, uint32_t c0, uint32_t k,
-                                             uint32_t n_chunks, uint64_t s8, uint32_t lo, uint32_t hi,
-                                             uint32_t row0, float *yacc) {
-    const uint32_t i0 = 8u * (c0 + k);
-    uint64_t r8 = 0;
-    if (k < n_chunks) {
-        uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
-        r8 = *cell;
-        *cell = 0;
+__device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
+                                        uint64_t (&sm)[kPrefetchChunks]) {
+    const uint32_t c0 = base >> 3;
+    const uint32_t nch = min(group_chunks(base, end), a.ebuf_cap / 8u);
+#pragma unroll
+    for (int j = 0; j < kPrefetchChunks; ++j) {
+        const uint32_t k = TB == 0 ? ltid + j * kThreadsPerGroup
+                                   : run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch);
+        const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
+        sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
     }
-    const bool active = k < n_chunks && i0 + 8u > lo && i0 < hi;
-    const uint64_t act = __builtin_amdgcn_ballot_w64(active);
-    if (!act) return;
-    float p[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t) p[t] = 0.0f;
-    uint32_t row = 0;
-    if (active) {
-        const uint4 v = merge8(s8, r8);
-        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-        float w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = __uint_as_float(e & 1 ? vw[e >> 1] & 0xFFFF0000u : vw[e >> 1] << 16);
-        if (i0 < lo || i0 + 8u > hi) {
-#pragma unroll
-            for (uint32_t e = 0; e < 8; ++e)
-                if (i0 + e < lo || i0 + e >= hi) w[e] = 0.0f;
-        }
-        row = static_cast<uint32_t>(__umul64hi(i0, m.row_magic));
-        const uint16_t *xc = m.x + (i0 - row * m.in_features);
-        uint4 xv[TB];
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-            xv[t] = t < static_cast<int>(m.n_tokens)
-                        ? *reinterpret_cast<const uint4 *>(xc + static_cast<size_t>(t) * m.in_features)
-                        : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
-            float acc = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc = fmaf(w[e], __uint_as_float(e & 1 ? xw[e >> 1] & 0xFFFF0000u : xw[e >> 1] << 16), acc);
-            p[t] = acc;
-        }
-    }
-    const uint32_t r0 = __builtin_amdgcn_readlane(row, static_cast<uint32_t>(__builtin_ctzll(act)));
-    const bool in_b = active && row != r0;  // then row == r0 + 1
-    const bool two = __builtin_amdgcn_ballot_w64(in_b) != 0;
+}
+
+template <int TB>
+struct RowSums {
+    float acc[TB];    // this lane's sums for the wave's current row
+    uint32_t row;     // the current row (wave-uniform)
+    bool dirty;       // acc holds something (wave-uniform)
+};
+
+using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Wave sums of the current row into yacc (lane 63), then start over.
+template <int TB>
+__device__ __forceinline__ void flush_wave(const MatmulArgs &m, RowSums<TB> &rs, uint32_t row0, float *yacc) {
+    if (!rs.dirty) return;
     const bool last = (threadIdx.x & (kWaveSize - 1)) == kWaveSize - 1;
-    float *ya = yacc + (r0 - row0) * TB;
+    float *ya = yacc + (rs.row - row0) * TB;
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
         if (t >= static_cast<int>(m.n_tokens)) break;
-        const float sa = wave_total(in_b ? 0.0f : p[t]);
-        if (last) __hip_atomic_fetch_add(ya + t, sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (two) {
-            const float sb = wave_total(in_b ? p[t] : 0.0f);
-            if (last) __hip_atomic_fetch_add(ya + TB + t, sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
+        const float v = wave_total(rs.acc[t]);
+        if (last) __hip_atomic_fetch_add(ya + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        rs.acc[t] = 0.0f;
     }
+    rs.dirty = false;
 }
 
 // merge_group's counterpart for the fused matmul: the group's elements [lo,
 // hi) (the ones merge_group would store) go into the LDS row sums yacc, whose
 // first row is row0 and which cover `rows` rows (both returned for
-// flush_rows).
+// flush_rows).  sm holds the chunks of rounds 0 .. kPrefetchChunks - 1 of
+// this thread's run (load_sm).
+//
+// Wave `wave` takes the run of chunks k0 .. k0 + 64 R - 1 (k0 = 64 R wave,
+// R = wave_rounds), 64 chunks per round; in a round lane l holds W's
+// elements i0 .. i0 + 7, i0 = e0 + 8 l.  The run's elements only grow, so
+// the row bookkeeping is one division per run and one scalar test per round:
+// B is the first element of the row after the wave's current one, and a
+// round spans 512 <= in_features elements, so it crosses at most B.  Lanes at
+// or past B belong to the next row.  x is loaded a round ahead when the
+// tokens' registers allow, with unconditional in-bounds loads (inactive lanes
+// read column 0 and multiply zeros; token slots past n_tokens read token 0
+// and are never flushed), so that each wait for x is an exact count; and the
+// fused kernel runs the merge before issuing the next group's loads, so that
+// those waits do not include them.
+template <int TB>
+__device__ __forceinline__ void load_x(const MatmulArgs &m, uint32_t i0, bool active, uint32_t B,
+                                       uint4 (&xv)[TB]) {
+    // Column of i0 in its row: the row before B, or the one starting at B.
+    const uint32_t col = active ? i0 - (i0 >= B ? B : B - m.in_features) : 0u;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        const uint32_t tt = t < static_cast<int>(m.n_tokens) ? static_cast<uint32_t>(t) : 0u;
+        xv[t] = *reinterpret_cast<const uint4 *>(m.x + static_cast<size_t>(tt) * m.in_features + col);
+    }
+}
+
 template <int TB>
 __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulArgs &m, uint8_t *ebuf,
                                              const uint64_t (&sm)[kPrefetchChunks], uint32_t base, uint32_t end,
@@ -407,17 +419,88 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
     const uint32_t hi = whole_last ? (end + 7u) & ~7u : end;
     row0 = static_cast<uint32_t>(__umul64hi(lo, m.row_magic));
     rows = lo < hi ? min(static_cast<uint32_t>(__umul64hi(hi - 1u, m.row_magic)) - row0 + 1u, m.yacc_rows) : 0u;
-#pragma unroll
-    for (int j = 0; j < kPrefetchChunks; ++j)
-        matmul_chunk<TB>(m, ebuf, c0, ltid + j * kThreadsPerGroup, n_chunks, sm[j], lo, hi, row0, yacc);
-    // Further chunks a wave at a time, so that every lane takes part in the sums.
-    const uint32_t lane = ltid & (kWaveSize - 1);
-    for (uint32_t kb = kPrefetchChunks * kThreadsPerGroup + ltid - lane; kb < n_chunks; kb += kThreadsPerGroup) {
-        const uint32_t c = min(c0 + kb + lane, a.sm_chunks - 1u);
-        const uint64_t s8 = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
-        matmul_chunk<TB>(m, ebuf, c0, kb + lane, n_chunks, s8, lo, hi, row0, yacc);
-    }
+    const uint32_t lane = ltid & (kWaveSize - 1), wave = __builtin_amdgcn_readfirstlane(ltid / kWaveSize);
+    const uint32_t n_rounds = wave_rounds(n_chunks);
+    // Every chunk before n_chunks starts before hi (hi >= end), so
+    // chunk_end bounds the elements that count as well as the LDS cells.
+    const uint32_t chunk_end = 8u * (c0 + n_chunks);
+    const uint32_t hi_eff = min(hi, chunk_end);
+    const uint32_t k0 = run_chunk(wave, 0, 0, n_chunks);
+    uint32_t e0 = 8u * (c0 + k0);
+    const uint32_t run_end = min(e0 + 8u * kWaveSize * n_rounds, hi_eff);
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+    if (e0 >= run_end) return;  // (then no cell of this run is before n_chunks either)
+
+    RowSums<TB> rs;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) rs.acc[t] = 0.0f;
+    rs.row = static_cast<uint32_t>(__umul64hi(max(e0, lo), m.row_magic));
+    rs.dirty = true;
+    uint32_t B = (rs.row + 1u) * m.in_features;
+    constexpr bool kAhead = TB <= 4;
+    uint4 xv[TB], xn[TB];
+    uint8_t *cell = ebuf + 8u * (k0 + lane);
+    uint32_t i0 = e0 + 8u * lane;
+    if (kAhead) load_x<TB>(m, i0, i0 + 8u > lo && i0 < hi_eff, B, xv);
+
+    auto step = [&](uint64_t s8) {
+        const bool in_chunks = i0 < chunk_end;
+        uint64_t r8 = 0;
+        if (in_chunks) {
+            r8 = *reinterpret_cast<uint64_t *>(cell);
+            *reinterpret_cast<uint64_t *>(cell) = 0;
+        }
+        // Does this round reach the next row?  (B only moves forward.)
+        const bool cross = B < min(e0 + 8u * kWaveSize, hi_eff);
+        const uint32_t B_next = cross ? B + m.in_features : B;
+        const uint32_t i1 = i0 + 8u * kWaveSize;
+        if (kAhead) load_x<TB>(m, i1, i1 < hi_eff, B_next, xn);
+        else load_x<TB>(m, i0, i0 + 8u > lo && i0 < hi_eff, B, xv);
+        // Chunks past the group's last one merge as zero.
+        const uint4 v = merge8(in_chunks ? s8 : 0ull, r8);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        // At most two chunks of a group are cut by lo or hi.
+        if (i0 < lo || i0 + 8u > hi) {
+#pragma unroll
+            for (uint32_t e = 0; e < 8; ++e)
+                if (i0 + e < lo || i0 + e >= hi) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+        float p[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            p[t] = dot2_bf16(w[3], xv[t].w,
+                             dot2_bf16(w[2], xv[t].z, dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, 0.0f))));
+        if (!cross) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t) rs.acc[t] += p[t];
+        } else {
+            // Finish the current row with the lanes before B, carry on with the rest.
+            const bool in_b = i0 >= B;
+#pragma unroll
+            for (int t = 0; t < TB; ++t) rs.acc[t] += in_b ? 0.0f : p[t];
+            flush_wave<TB>(m, rs, row0, yacc);
+#pragma unroll
+            for (int t = 0; t < TB; ++t) rs.acc[t] = in_b ? p[t] : 0.0f;
+            rs.row += 1u;
+            rs.dirty = true;
+        }
+        if (kAhead) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t) xv[t] = xn[t];
+        }
+        B = B_next;
+        e0 += 8u * kWaveSize;
+        i0 = i1;
+        cell += 8u * kWaveSize;
+    };
+#pragma unroll
+    for (int j = 0; j < kPrefetchChunks; ++j) {
+        if (e0 >= run_end) break;
+        step(sm[j]);
+    }
+    while (e0 < run_end)
+        step(*reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(i0 >> 3, a.sm_chunks - 1u)));
+    flush_wave<TB>(m, rs, row0, yacc);
 }
 
 // Add a group's LDS row sums into y (other workgroups add the other parts
@@ -705,21 +788,25 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         const uint32_t base = min(cur_base, end);
         const uint32_t g_nx = min(s_nx * GPW + slot, a.n_groups);
         const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
+        if constexpr (TB > 0) {
+            // The fused merge waits for its own loads of x; issued before
+            // the next group's loads, those waits do not include them.
+            if (it > 0)
+                merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc,
+                                 y_row0, y_rows);
+        }
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
         if (sched && tid == 0) fetched = take_ticket(sched, wg % a.pools);  // for round it + 3
 
         // 2. Merge and store the super-group decoded in the previous
-        // iteration, then load this group's sign/mantissa chunks (into the
-        // registers the merge has just consumed) for the next one.
-        if (it > 0) {
-            if constexpr (TB == 0)
-                merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
-            else
-                merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc,
-                                 y_row0, y_rows);
+        // iteration (the fused matmul merged it before step 1's loads), then
+        // load this group's sign/mantissa chunks (into the registers the
+        // merge has just consumed) for the next one.
+        if constexpr (TB == 0) {
+            if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
         }
-        load_sm(a, base, end, ltid, sm);
+        load_sm<TB>(a, base, end, ltid, sm);
 
         // 3. Decode this super-group.
         const uint32_t lead = base & 7u;
