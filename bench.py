@@ -169,6 +169,49 @@ def summarize_profiles(prof_dir: str, commands: dict) -> None:
         f.write("\n")
 
 
+def summarize_linear_profile(prof_dir: str, command: str) -> None:
+    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of
+    bench.py --linear-tokens (prof_dir/lin_trace and prof_dir/lin.json).
+    Every step launches the seven matrices in the same order, so the i-th
+    fused launch of the run is matrix i mod 7; the first 1 + warmup steps
+    are left out of the averages."""
+    with open(os.path.join(prof_dir, "lin.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    names = list(bench["config"]["shapes"])
+    rows = [r for r in _read_csv(os.path.join(prof_dir, "lin_trace", "run_kernel_trace.csv"))
+            if "df11_linear" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    skip = (1 + bench["warmup"]) * len(names)
+    per = {nm: [] for nm in names}
+    for i, r in enumerate(rows):
+        if i >= skip:
+            per[names[i % len(names)]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = _read_csv(os.path.join(prof_dir, "lin_trace", "run_kernel_stats.csv"))
+    T = bench["config"]["tokens"]
+    lines = [f"# df11_linear_kernel on llama3_8b_block_linear ({T} token{'s' if T > 1 else ''}): "
+             "rocprofv3 kernel trace", "",
+             "Command (from the repository root on a one-GPU MI355X box):", "", "    " + command, "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
+    lines += ["", "Fused launches per matrix after the warmup (trace timestamps) against the bench line's "
+              "dispatch events:", "", "| matrix | shape | launches | average us | min us | bench line us |",
+              "|---|---|---|---|---|---|"]
+    total = 0.0
+    for nm in names:
+        v = per[nm]
+        total += float(np.mean(v))
+        lines.append(f"| {nm} | {bench['config']['shapes'][nm]} | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | "
+                     f"{bench['per_matrix_us'][nm]:.2f} |")
+    comp = bench["config"]["compressed_bytes"]
+    lines += ["", f"Sum of the seven averages: {total:.1f} us per step for {comp} compressed bytes "
+              f"({comp / (total * 1e-6) / 1e9:.0f} GB/s of compressed weights).", "",
+              "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+    with open(os.path.join(REPO, "profiles", f"df11_linear_kernel_llama3_8b_block_t{T}_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
     weights, DF11 blocks decoded in line before each block, and DF11 blocks
@@ -221,6 +264,159 @@ def integration(args, dev) -> int:
     return 0
 
 
+def linear_bench(args, dev) -> int:
+    """One step = y = x W^T for each of the seven Llama-3-8B block matrices
+    (each its own DF11 stream) at --linear-tokens tokens, with the decode
+    fused into the product (df11_linear), compressed weights resident in HBM.
+    value = compressed bytes + x + y per step / wall time; the roofline uses
+    the fused kernels' own durations (dispatch events, in a second pass of
+    the same steps).  The same run times resident BF16
+    weights (torch F.linear) and decode-then-F.linear for comparison."""
+    import torch
+    import torch.nn.functional as F
+    from entropy_decoding_df11_amd import df11, workloads
+    T = args.linear_tokens
+    stream = torch.cuda.current_stream(dev)
+    t0 = time.perf_counter()
+    flat, views = workloads.gen_block()
+    mats = []
+    for nm, o, (r, c) in views:
+        w = np.ascontiguousarray(flat[o:o + r * c])
+        t = df11.compress(w, shape=(r, c), device=dev, decode_table_bits=args.decode_table_bits)
+        wd = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16).reshape(r, c)
+        rng = np.random.default_rng(r * 7 + c)
+        xb = workloads.f32_to_bf16_bits(rng.standard_normal(T * c) * 0.5).reshape(T, c)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((T, r), dtype=torch.float32, device=dev)
+        mats.append((nm, r, c, t, wd, x, y))
+    t_prep = time.perf_counter() - t0
+    n = int(flat.size)
+    comp = sum(m[3].compressed_bytes() for m in mats)
+    algo_bytes = comp + sum(2 * T * m[2] + 4 * T * m[1] for m in mats)
+
+    def step(evs=None):
+        for i, (_, _, _, t, _, x, y) in enumerate(mats):
+            t.linear(x, out=y, events=None if evs is None else evs[i])
+
+    # Check every output against a float64 product of the same BF16 values,
+    # within the float32 summation bound (each product exact, in_features
+    # additions): |y - ref| <= 1.01 * in_features * 2^-24 * sum |x w|.
+    step()
+    torch.cuda.synchronize()
+    for nm, r, c, t, wd, x, y in mats:
+        ref = x.double() @ wd.double().T
+        bound = 1.01 * c * 2.0 ** -24 * (x.double().abs() @ wd.double().abs().T)
+        if not bool(((y.double() - ref).abs() <= bound).all()):
+            print(f"bench: fused linear of {nm} is outside the float32 bound", file=sys.stderr)
+            return 1
+    del ref, bound
+
+    # Timed steps (wall clock), then the same steps again with each fused
+    # kernel's own start and end recorded (dispatch events), for the roofline.
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in mats]
+           for _ in range(args.steps)]
+    for e in (ev for row in evs for pair in row for ev in pair):
+        e.record(stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [sum(a.elapsed_time(b) for a, b in row) for row in evs]
+    per_matrix_us = {m[0]: round(float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
+                                                 for i in range(args.steps)])) * 1e3, 2)
+                     for j, m in enumerate(mats)}
+    mean_ms = float(np.mean(kern_ms))
+    achieved = algo_bytes / (mean_ms * 1e-3) / 1e9
+
+    def timed(fn, reps=50):
+        for _ in range(10):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    scratch = torch.empty(max(m[1] * m[2] for m in mats), dtype=torch.bfloat16, device=dev)
+    resident_ms = timed(lambda: [F.linear(m[5], m[4]) for m in mats])
+    decode_gemm_ms = timed(lambda: [F.linear(m[5], m[3].decompress(out=scratch[:m[1] * m[2]].view(m[1], m[2])))
+                                    for m in mats])
+    fused_ms = timed(step)
+    result = {
+        "metric": "DF11 decode fused into y = x W^T: GB/s of compressed weights + x + y per step",
+        "value": round(args.steps * algo_bytes / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_8b_block_linear",
+            "tokens": T,
+            "shapes": {m[0]: [m[1], m[2]] for m in mats},
+            "streams": len(mats),
+            "codebook": "per_weight",
+            "n_elements": n,
+            "compressed_bytes": comp,
+            "decode_table_bits": args.decode_table_bits,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "kernel_ms_mean": round(mean_ms, 5),
+        "per_matrix_us": per_matrix_us,
+        "same_run_ms_per_step": {"fused_df11": round(fused_ms, 4), "resident_bf16_F_linear": round(resident_ms, 4),
+                                 "decode_then_F_linear": round(decode_gemm_ms, 4)},
+        "outputs": "within the float32 summation bound of a float64 product",
+        "host_prep_s": round(t_prep, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle  # test infrastructure: the CPU baseline only
+        nm, r, c, t, wd, x, y = mats[0]
+        w = np.ascontiguousarray(flat[:r * c])
+        s = oracle.encode(w)
+        xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        c0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.linear(s, xb, r)
+            reps += 1
+            if time.perf_counter() - c0 > 10.0:
+                break
+        cpu_s = (time.perf_counter() - c0) / reps
+        sample_bytes = (s["enc"].nbytes + s["sm"].nbytes + s["gaps"].nbytes + s["out_pos"].nbytes
+                        + 2 * T * c + 4 * T * r)
+        result["cpu_baseline"] = {
+            "value": round(sample_bytes / cpu_s / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nm} ({r}x{c}) at {T} tokens: oracle tree-walk decode then a float64 matmul, "
+                      f"{reps} run(s), {cpu_s:.2f} s each",
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +437,9 @@ def main() -> int:
     ap.add_argument("--blocks", type=int, default=4, help="blocks of the --integration model")
     ap.add_argument("--overlap-workgroups", type=int, default=512,
                     help="workgroup cap of the side-stream decode in --integration (0: no cap)")
+    ap.add_argument("--linear-tokens", type=int, default=0,
+                    help="time the decode fused into y = x W^T over the block's seven matrices at this many "
+                         "tokens (1..8) instead of the decompression")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 runs of this script under DIR, then exit")
     args = ap.parse_args()
@@ -255,6 +454,11 @@ def main() -> int:
             "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
                            "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
         })
+        if os.path.isdir(os.path.join(args.summarize_profiles, "lin_trace")):
+            summarize_linear_profile(args.summarize_profiles,
+                                     pre + "rocprofv3 --kernel-trace --stats -d $D/lin_trace -o run --output-format csv "
+                                           "-- python3 $R/bench.py --linear-tokens 1 --steps 50 --warmup 20 "
+                                           "--no-cpu-baseline > $D/lin.json")
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -270,6 +474,8 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.integration:
         return integration(args, dev)
+    if args.linear_tokens:
+        return linear_bench(args, dev)
     wl = args.workload
     t0 = time.perf_counter()
     if wl.startswith("llama3_8b_block"):

@@ -1296,10 +1296,10 @@ int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hip
     void *zparams[] = {&y, const_cast<uint32_t *>(&n_y)};
     const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((n_y + 255) / 256, 1024));
     if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256), zparams, 0,
-                           stream, start, nullptr, 0) != hipSuccess)
+                           stream, nullptr, nullptr, 0) != hipSuccess)
         return DF11_E_HIP;
     void *params[] = {&args, &margs};
-    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, nullptr, stop,
+    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop,
                            0) != hipSuccess)
         return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;

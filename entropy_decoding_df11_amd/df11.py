@@ -240,7 +240,7 @@ class DF11Tensor:
         contiguous bfloat16 (n_tokens, in_features) tensor on the same device
         with 1 <= n_tokens <= 8.  Returns out, a float32 (n_tokens,
         out_features) tensor (a new one by default).  events: as for
-        decompress, recorded around the zeroing and fused kernels."""
+        decompress, recorded at the fused kernel's own start and end."""
         import torch
         if len(self.shape) != 2:
             raise ValueError("linear needs a 2-D weight (out_features, in_features)")

@@ -285,9 +285,10 @@ int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_
 int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                 uint32_t out_features, float *y, void *hip_stream);
 
-/* df11_linear with start_event recorded when the zeroing kernel starts and
- * stop_event when the fused kernel ends (hipEvent_t, either may be NULL), to
- * measure the fused product.  Same arguments, output and errors. */
+/* df11_linear with start_event and stop_event (hipEvent_t, either may be
+ * NULL) recorded when the fused kernel itself starts and ends (the zeroing
+ * kernel before it is not included), to measure the fused product.  Same
+ * arguments, output and errors. */
 int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
