@@ -64,7 +64,8 @@ def load() -> ctypes.CDLL:
         _LIB = ctypes.CDLL(LIB_PATH)
         for fn in ("orc_split", "orc_merge", "orc_histogram", "orc_code_lengths", "orc_canonical_codes",
                    "orc_build_luts", "orc_layout", "orc_encode", "orc_decode_treewalk",
-                   "orc_decode_groups_treewalk", "orc_decode_lut", "orc_check_metadata"):
+                   "orc_decode_groups_treewalk", "orc_decode_lut", "orc_check_metadata", "orc_rans_quantize",
+                   "orc_rans_encode", "orc_rans_decode"):
             getattr(_LIB, fn).restype = ctypes.c_int
         _LIB.orc_total_bits.restype = ctypes.c_uint64
     return _LIB
@@ -252,3 +253,61 @@ def linear(s: Dict, x: np.ndarray, out_features: int) -> np.ndarray:
     wm = bf16_to_f64(w).reshape(out_features, in_features)
     xm = bf16_to_f64(np.asarray(x)).reshape(-1, in_features)
     return xm @ wm.T
+
+
+# rANS exponent coder (see the rANS section of df11_oracle.c for the format):
+# 12-bit probabilities, 64 lanes, 512 steps per segment.
+RANS_PROB_BITS = 12
+RANS_LANES = 64
+RANS_STEPS = 512
+
+
+def rans_quantize(hist: np.ndarray, prob_bits: int = RANS_PROB_BITS) -> np.ndarray:
+    """Frequencies summing to 2^prob_bits for the exponent histogram."""
+    hist = np.ascontiguousarray(hist, dtype=np.uint64)
+    freq = np.zeros(256, np.uint32)
+    _check(load().orc_rans_quantize(_p(hist), ctypes.c_uint32(prob_bits), _p(freq)), "rans_quantize")
+    return freq
+
+
+def rans_encode(w: np.ndarray, prob_bits: int = RANS_PROB_BITS, lanes: int = RANS_LANES, steps: int = RANS_STEPS,
+                freq: Optional[np.ndarray] = None) -> Dict:
+    """rANS-code the exponents of BF16 words w; sign/mantissa bytes as in DF11."""
+    w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
+    if freq is None:
+        freq = rans_quantize(histogram(w), prob_bits)
+    freq = np.ascontiguousarray(freq, dtype=np.uint32)
+    seg = lanes * steps
+    n_seg = (w.size + seg - 1) // seg
+    states = np.zeros(max(n_seg * lanes, 1), np.uint32)
+    offsets = np.zeros(n_seg + 1, np.uint64)
+    words = np.zeros(max(w.size, 1), np.uint16)
+    n_words = ctypes.c_uint64(0)
+    sm = np.zeros(max(w.size, 1), np.uint8)
+    _check(load().orc_rans_encode(_p(w), ctypes.c_uint64(w.size), ctypes.c_uint32(prob_bits), _p(freq),
+                                  ctypes.c_uint32(lanes), ctypes.c_uint32(steps), _p(states), _p(offsets), _p(words),
+                                  ctypes.c_uint64(words.size), ctypes.byref(n_words), _p(sm)), "rans_encode")
+    return {"freq": freq, "prob_bits": prob_bits, "lanes": lanes, "steps": steps, "n_elements": w.size,
+            "states": states[:n_seg * lanes], "word_offsets": offsets, "words": words[:n_words.value].copy(),
+            "sm": sm[:w.size]}
+
+
+def rans_decode(s: Dict) -> np.ndarray:
+    w = np.empty(s["n_elements"], np.uint16)
+    states = np.ascontiguousarray(s["states"], dtype=np.uint32)
+    offsets = np.ascontiguousarray(s["word_offsets"], dtype=np.uint64)
+    words = np.ascontiguousarray(s["words"], dtype=np.uint16)
+    sm = np.ascontiguousarray(s["sm"], dtype=np.uint8)
+    keep = (states if states.size else np.zeros(1, np.uint32), words if words.size else np.zeros(1, np.uint16),
+            sm if sm.size else np.zeros(1, np.uint8))
+    _check(load().orc_rans_decode(_p(np.ascontiguousarray(s["freq"], dtype=np.uint32)), ctypes.c_uint32(s["prob_bits"]),
+                                  ctypes.c_uint32(s["lanes"]), ctypes.c_uint32(s["steps"]), _p(keep[0]), _p(offsets),
+                                  _p(keep[1]), _p(keep[2]), ctypes.c_uint64(s["n_elements"]),
+                                  _p(w if w.size else np.zeros(1, np.uint16))), "rans_decode")
+    return w
+
+
+def rans_compressed_bytes(s: Dict) -> int:
+    """Bytes of the rANS stream: frequencies (2 bytes each), start states,
+    word offsets (4 bytes each), words and sign/mantissa bytes."""
+    return 2 * 256 + 4 * s["states"].size + 4 * s["word_offsets"].size + 2 * s["words"].size + s["sm"].size

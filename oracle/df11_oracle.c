@@ -560,3 +560,187 @@ int orc_check_metadata(const uint8_t lens[256], const uint32_t codes[256], const
     if (out_pos[groups] != n_elements) return ORC_E_BAD_STREAM;
     return ORC_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * rANS exponent coder.  The page's discussion ("Opini Hacker News") names
+ * rANS as an entropy coder that suits SIMD-style instruction sets better than
+ * Huffman; the page gives no format, so the one below is this project's
+ * reading: the plain static rANS of Duda's asymmetric numeral systems with
+ * 16-bit renormalisation, laid out for 64-lane waves.
+ *   - The exponent histogram is quantized to frequencies f[s] summing to
+ *     M = 2^prob_bits (orc_rans_quantize); c[s] = f[0] + ... + f[s - 1].
+ *   - A state x lives in [L, 2^32), L = 2^16.  Encoding s from x first
+ *     emits the low 16 bits of x and shifts them out while x >= f[s] *
+ *     2^(32 - prob_bits), then sets x = floor(x / f[s]) * M + (x mod f[s]) +
+ *     c[s].  Decoding inverts it: slot = x mod M, s is the symbol with
+ *     c[s] <= slot < c[s] + f[s], x = f[s] * floor(x / M) + slot - c[s], and
+ *     if x < L, x = x * 2^16 + the next word (one word at most per symbol).
+ *   - The exponents are cut into segments of lanes x steps symbols; in a
+ *     segment, lane l codes the positions step * lanes + l (step = 0, 1, ...)
+ *     with a state of its own, which starts at L in the encoder.  The
+ *     decoder reads a segment's words in the order step ascending, lane
+ *     ascending, one for each lane whose state fell below L; the encoder
+ *     therefore runs step descending, lane descending, and its words are
+ *     stored reversed.  Per segment the stream keeps the lanes' final encoder
+ *     states (the decoder's start states) and the offset of its words.
+ * Sign and mantissa bytes are stored as in DF11.
+ * ------------------------------------------------------------------------- */
+#define ORC_RANS_L 65536u
+
+/* Frequencies: every used exponent gets max(1, floor(hist * M / N)); if the
+ * sum is below M the difference goes to the most frequent exponent (lowest
+ * value on ties); while it is above M the largest frequency above 1 (lowest
+ * value on ties) drops by one. */
+int orc_rans_quantize(const uint64_t hist[256], uint32_t prob_bits, uint32_t freq[256])
+{
+    if (prob_bits < 1 || prob_bits > 16) return ORC_E_INVALID_ARG;
+    const uint64_t M = 1ull << prob_bits;
+    uint64_t n = 0, used = 0;
+    for (int s = 0; s < 256; s++) {
+        n += hist[s];
+        used += hist[s] > 0;
+        freq[s] = 0;
+    }
+    if (n == 0) return ORC_OK;
+    if (used > M) return ORC_E_INVALID_ARG;
+    uint64_t sum = 0;
+    int top = -1;
+    for (int s = 0; s < 256; s++) {
+        if (!hist[s]) continue;
+        uint64_t f = (uint64_t)(((unsigned __int128)hist[s] * M) / n);
+        freq[s] = (uint32_t)(f ? f : 1);
+        sum += freq[s];
+        if (top < 0 || hist[s] > hist[top]) top = s;
+    }
+    if (sum < M) freq[top] += (uint32_t)(M - sum);
+    while (sum > M) {
+        int big = -1;
+        for (int s = 0; s < 256; s++)
+            if (freq[s] > 1 && (big < 0 || freq[s] > freq[big])) big = s;
+        freq[big]--;
+        sum--;
+    }
+    return ORC_OK;
+}
+
+static void orc_rans_cum(const uint32_t freq[256], uint32_t cum[257])
+{
+    cum[0] = 0;
+    for (int s = 0; s < 256; s++) cum[s + 1] = cum[s] + freq[s];
+}
+
+/* Encode n BF16 words.  states: n_segments * lanes; word_offsets:
+ * n_segments + 1 (word_offsets[g] is segment g's first word); words: room for
+ * words_cap (n suffices: at most one word per symbol); sm: n bytes.  Returns
+ * the number of words in *n_words. */
+int orc_rans_encode(const uint16_t *w, uint64_t n, uint32_t prob_bits, const uint32_t freq[256], uint32_t lanes,
+                    uint32_t steps, uint32_t *states, uint64_t *word_offsets, uint16_t *words, uint64_t words_cap,
+                    uint64_t *n_words, uint8_t *sm)
+{
+    if (prob_bits < 1 || prob_bits > 16 || lanes == 0 || steps == 0) return ORC_E_INVALID_ARG;
+    uint32_t cum[257];
+    orc_rans_cum(freq, cum);
+    if (n && cum[256] != (1u << prob_bits)) return ORC_E_INVALID_ARG;
+    const uint64_t seg = (uint64_t)lanes * steps;
+    const uint64_t n_seg = (n + seg - 1) / seg;
+    uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * lanes);
+    uint16_t *stack = (uint16_t *)malloc(sizeof(uint16_t) * (seg ? seg : 1));
+    if (!x || !stack) {
+        free(x);
+        free(stack);
+        return ORC_E_INVALID_ARG;
+    }
+    uint64_t total = 0;
+    int rc = ORC_OK;
+    for (uint64_t g = 0; g < n_seg && rc == ORC_OK; g++) {
+        const uint64_t base = g * seg;
+        const uint64_t count = n - base < seg ? n - base : seg;
+        uint64_t top = 0;
+        for (uint32_t l = 0; l < lanes; l++) x[l] = ORC_RANS_L;
+        for (uint64_t j = steps; j-- > 0 && rc == ORC_OK;) {
+            for (uint32_t l = lanes; l-- > 0;) {
+                const uint64_t q = j * lanes + l;
+                if (q >= count) continue;
+                const uint32_t s = (w[base + q] >> 7) & 0xFFu;
+                const uint32_t f = freq[s];
+                if (s >= ORC_FIRST_POINTER) { rc = ORC_E_RESERVED_EXPONENT; break; }
+                if (f == 0) { rc = ORC_E_INVALID_ARG; break; }
+                const uint64_t x_max = (uint64_t)f << (32 - prob_bits);
+                while (x[l] >= x_max) {
+                    stack[top++] = (uint16_t)(x[l] & 0xFFFFu);
+                    x[l] >>= 16;
+                }
+                x[l] = (x[l] / f << prob_bits) + x[l] % f + cum[s];
+            }
+        }
+        if (rc != ORC_OK) break;
+        if (total + top > words_cap) { rc = ORC_E_BUFFER_TOO_SMALL; break; }
+        word_offsets[g] = total;
+        for (uint64_t i = 0; i < top; i++) words[total + i] = stack[top - 1 - i];
+        total += top;
+        for (uint32_t l = 0; l < lanes; l++) states[g * lanes + l] = x[l];
+    }
+    free(x);
+    free(stack);
+    if (rc != ORC_OK) return rc;
+    word_offsets[n_seg] = total;
+    *n_words = total;
+    for (uint64_t i = 0; i < n; i++) sm[i] = (uint8_t)(((w[i] >> 8) & 0x80u) | (w[i] & 0x7Fu));
+    return ORC_OK;
+}
+
+/* Decode the stream above into n BF16 words.  Fails with ORC_E_BAD_STREAM if
+ * a segment needs more words than it has, leaves some unread, or does not
+ * return every state to L (the encoder's start). */
+int orc_rans_decode(const uint32_t freq[256], uint32_t prob_bits, uint32_t lanes, uint32_t steps,
+                    const uint32_t *states, const uint64_t *word_offsets, const uint16_t *words, const uint8_t *sm,
+                    uint64_t n, uint16_t *w)
+{
+    if (prob_bits < 1 || prob_bits > 16 || lanes == 0 || steps == 0) return ORC_E_INVALID_ARG;
+    if (n == 0) return ORC_OK;
+    uint32_t cum[257];
+    orc_rans_cum(freq, cum);
+    const uint32_t M = 1u << prob_bits;
+    if (cum[256] != M) return ORC_E_BAD_STREAM;
+    uint8_t *sym = (uint8_t *)malloc(M);
+    uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * lanes);
+    if (!sym || !x) {
+        free(sym);
+        free(x);
+        return ORC_E_INVALID_ARG;
+    }
+    for (int s = 0; s < 256; s++)
+        for (uint32_t k = cum[s]; k < cum[s + 1]; k++) sym[k] = (uint8_t)s;
+    const uint64_t seg = (uint64_t)lanes * steps;
+    const uint64_t n_seg = (n + seg - 1) / seg;
+    int rc = ORC_OK;
+    for (uint64_t g = 0; g < n_seg && rc == ORC_OK; g++) {
+        const uint64_t base = g * seg;
+        const uint64_t count = n - base < seg ? n - base : seg;
+        uint64_t ptr = word_offsets[g];
+        const uint64_t ptr_end = word_offsets[g + 1];
+        for (uint32_t l = 0; l < lanes; l++) x[l] = states[g * lanes + l];
+        for (uint64_t j = 0; j < steps && rc == ORC_OK; j++) {
+            for (uint32_t l = 0; l < lanes; l++) {
+                const uint64_t q = j * lanes + l;
+                if (q >= count) continue;
+                const uint32_t slot = x[l] & (M - 1);
+                const uint32_t s = sym[slot];
+                x[l] = freq[s] * (x[l] >> prob_bits) + slot - cum[s];
+                if (x[l] < ORC_RANS_L) {
+                    if (ptr >= ptr_end) { rc = ORC_E_BAD_STREAM; break; }
+                    x[l] = (x[l] << 16) | words[ptr++];
+                }
+                const uint32_t b = sm[base + q];
+                w[base + q] = (uint16_t)(((b & 0x80u) << 8) | (s << 7) | (b & 0x7Fu));
+            }
+        }
+        if (rc != ORC_OK) break;
+        if (ptr != ptr_end) rc = ORC_E_BAD_STREAM;
+        for (uint32_t l = 0; l < lanes && rc == ORC_OK; l++)
+            if (x[l] != ORC_RANS_L) rc = ORC_E_BAD_STREAM;
+    }
+    free(sym);
+    free(x);
+    return rc;
+}

@@ -557,3 +557,141 @@ def test_linear_rejects_partial_rows():
     s = oracle.encode(_bf16_of_ints(np.arange(10) % 7))
     with pytest.raises(ValueError):
         oracle.linear(s, np.zeros((1, 3), np.uint16), 3)
+
+
+# ---------------------------------------------------------------------------
+# rANS exponent coder ("Opini Hacker News" names rANS as the SIMD-friendlier
+# coder; the format is the plain static rANS of asymmetric numeral systems
+# with 16-bit renormalisation, laid out in 64-lane segments)
+# ---------------------------------------------------------------------------
+
+def _bf16_of_exponents(exps):
+    return (np.asarray(exps, np.uint32) << 7).astype(np.uint16)
+
+
+def _freq_table(pairs):
+    f = np.zeros(256, np.uint32)
+    for s, v in pairs.items():
+        f[s] = v
+    return f
+
+
+def test_rans_hand_example_state_arithmetic():
+    """M = 4 (2 probability bits), f(100) = 3 with c = 0, f(101) = 1 with
+    c = 3; one lane, symbols 100, 101, 100 in decode order, so the encoder
+    codes them last to first from x = L = 65536:
+      100: 65536 = 3 * 21845 + 1   -> 21845 * 4 + 1 + 0 = 87381
+      101: 87381 = 1 * 87381 + 0   -> 87381 * 4 + 0 + 3 = 349527
+      100: 349527 = 3 * 116509 + 0 -> 116509 * 4 + 0 + 0 = 466036
+    No state reaches f * 2^30, so no word is written."""
+    freq = _freq_table({100: 3, 101: 1})
+    w = _bf16_of_exponents([100, 101, 100])
+    s = oracle.rans_encode(w, prob_bits=2, lanes=1, steps=3, freq=freq)
+    assert s["states"].tolist() == [466036]
+    assert s["words"].size == 0
+    assert s["word_offsets"].tolist() == [0, 0]
+    assert np.array_equal(oracle.rans_decode(s), w)
+
+
+def test_rans_hand_example_renormalisation():
+    """M = 4096, f(100) = 4095 (c = 0), f(101) = 1 (c = 4095); symbols 101,
+    101.  The second-coded 101 (first decoded) finds x = 65536 * 4096 + 4095
+    = 0x10000FFF >= 1 * 2^20, so the low 16 bits 0x0FFF = 4095 are written and
+    x becomes 0x1000 = 4096; then x = 4096 * 4096 + 4095 = 16781311."""
+    freq = _freq_table({100: 4095, 101: 1})
+    w = _bf16_of_exponents([101, 101])
+    s = oracle.rans_encode(w, prob_bits=12, lanes=1, steps=2, freq=freq)
+    assert s["states"].tolist() == [16781311]
+    assert s["words"].tolist() == [4095]
+    assert np.array_equal(oracle.rans_decode(s), w)
+
+
+def test_rans_hand_example_lanes_and_word_order():
+    """Two lanes, three steps: lane 0 takes positions 0, 2, 4 and lane 1
+    positions 1, 3, 5.  M = 4096, f(100) = 2048 (c 0), f(101) = 1 (c 2048),
+    f(102) = 2047 (c 2049); positions 0..5 hold 101 101 101 101 100 102.
+      lane 0, coding 100, 101, 101:  131072 -> 536872960 -> writes 2048, 33556480
+      lane 1, coding 102, 101, 101:  133153 -> 545396736 -> writes 6144, 34088960
+    At step 0 both lanes write; the decoder reads lane 0's word first, so the
+    stored words are 2048, 6144."""
+    freq = _freq_table({100: 2048, 101: 1, 102: 2047})
+    w = _bf16_of_exponents([101, 101, 101, 101, 100, 102])
+    s = oracle.rans_encode(w, prob_bits=12, lanes=2, steps=3, freq=freq)
+    assert s["states"].tolist() == [33556480, 34088960]
+    assert s["words"].tolist() == [2048, 6144]
+    assert np.array_equal(oracle.rans_decode(s), w)
+
+
+def test_rans_quantized_frequencies(workload):
+    """Frequencies sum to M, every used exponent gets at least 1 and unused
+    ones 0, and the quantized code costs within 1% of the entropy."""
+    for name in ("single_1024x1024", "proj_4096x4096_outliers"):
+        w = workload(name)
+        hist = oracle.histogram(w)
+        freq = oracle.rans_quantize(hist)
+        assert int(freq.sum()) == 4096
+        assert np.array_equal(freq > 0, hist > 0)
+        used = hist > 0
+        cost = float((hist[used] * np.log2(4096.0 / freq[used])).sum()) / w.size
+        assert cost <= 1.01 * _entropy(hist)
+
+
+@pytest.mark.parametrize("name", ["single_1024x1024", "proj_4096x4096_outliers"])
+def test_rans_roundtrip_and_size_bound(workload, name):
+    """Lossless, and the words hold what the states shed: coding s takes x to
+    within M of x * M / f[s], a word takes 16 bits out of x, and every state
+    starts at 2^16, so 16 * words + sum of (log2 x_final - 16) equals the
+    information sum of log2(M / f[s]) up to each step's rounding, log2(1 +
+    f[s] / x) with x several thousand times f[s] for these streams (the test
+    allows 0.5% of the total, plus 16 bits per state)."""
+    w = workload(name)[:3_000_000]
+    s = oracle.rans_encode(w)
+    assert np.array_equal(oracle.rans_decode(s), w)
+    e = (w >> 7) & 0xFF
+    f = s["freq"][e].astype(np.float64)
+    info = float(np.log2(4096.0 / f).sum())
+    shed = float((np.log2(s["states"].astype(np.float64)) - 16.0).sum())
+    assert abs(16 * s["words"].size + shed - info) <= 0.005 * info + 16 * s["states"].size
+
+
+def test_rans_single_exponent_needs_no_words():
+    """One exponent value: f = M, coding leaves every state at L, no words."""
+    w = _bf16_of_exponents(np.full(70000, 120))
+    s = oracle.rans_encode(w)
+    assert s["words"].size == 0
+    assert np.all(s["states"] == 65536)
+    assert np.array_equal(oracle.rans_decode(s), w)
+
+
+def test_rans_ragged_last_segment_and_empty():
+    rng = np.random.default_rng(3)
+    for n in (0, 1, 63, 64, 65, 32768, 32769, 100_003):
+        w = workloads.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32) * 0.02)
+        s = oracle.rans_encode(w)
+        assert s["word_offsets"].size == (n + 32767) // 32768 + 1
+        assert np.array_equal(oracle.rans_decode(s), w)
+
+
+def test_rans_planted_mistakes_are_caught(workload):
+    w = workload("single_1024x1024")[:200_000]
+    s = oracle.rans_encode(w)
+    # a changed word breaks the decode or its end check
+    bad = dict(s)
+    bad["words"] = s["words"].copy()
+    bad["words"][10] ^= 0x0100
+    try:
+        assert not np.array_equal(oracle.rans_decode(bad), w)
+    except oracle.OracleError:
+        pass
+    # a changed start state is caught by the end check (states must return to L)
+    bad = dict(s)
+    bad["states"] = s["states"].copy()
+    bad["states"][5] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.rans_decode(bad)
+    # swapped word offsets of two segments
+    bad = dict(s)
+    bad["word_offsets"] = s["word_offsets"].copy()
+    bad["word_offsets"][1] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.rans_decode(bad)
