@@ -57,15 +57,18 @@ def build(verbose: bool = False) -> str:
     """Compile every source of the library and return the path of libdf11.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
-    host_obj = os.path.join(BUILD_DIR, "df11_host.o")
+    host_objs = []
+    for src in ("df11_host.cpp", "df11_rans_host.cpp"):
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
+        _run(["g++", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        host_objs.append(obj)
     dev_obj = os.path.join(BUILD_DIR, "df11_decode.o")
-    _run(["g++", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
-          "-c", os.path.join(CSRC, "df11_host.cpp"), "-o", host_obj], verbose)
     _run([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, "df11_decode.hip"),
           "-o", dev_obj], verbose)
     rpaths = [p for p in (_torch_lib_dir(), os.path.join(ROCM, "lib")) if p]
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, host_obj, dev_obj,
+    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, *host_objs, dev_obj,
           *[f"-Wl,-rpath,{p}" for p in rpaths]], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH

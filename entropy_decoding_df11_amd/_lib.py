@@ -28,6 +28,10 @@ SCHEDULE_WORDS = 144  # DF11_SCHEDULE_WORDS
 MAX_BATCH = 16  # DF11_MAX_BATCH
 LINEAR_MAX_TOKENS = 8  # DF11_LINEAR_MAX_TOKENS
 LINEAR_MIN_IN_FEATURES = 512  # DF11_LINEAR_MIN_IN_FEATURES
+RANS_PROB_BITS = 12  # DF11_RANS_PROB_BITS
+RANS_LANES = 64  # DF11_RANS_LANES
+RANS_STEPS = 512  # DF11_RANS_STEPS
+RANS_TABLE_ENTRIES = 4096  # DF11_RANS_TABLE_ENTRIES
 
 # Every function the header declares; the ABI test checks each is exported.
 EXPORTED = [
@@ -43,6 +47,11 @@ EXPORTED = [
     "df11_decompress_timed",
     "df11_linear",
     "df11_linear_timed",
+    "df11_rans_quantize",
+    "df11_rans_encode",
+    "df11_rans_build_table",
+    "df11_rans_decompress",
+    "df11_rans_decompress_timed",
     "df11_status_str",
 ]
 
@@ -106,6 +115,29 @@ class DeviceStream(ctypes.Structure):
     ]
 
 
+class RansHeader(ctypes.Structure):
+    _fields_ = [
+        ("n_elements", ctypes.c_uint64),
+        ("n_segments", ctypes.c_uint64),
+        ("n_words", ctypes.c_uint64),
+        ("prob_bits", ctypes.c_uint32),
+        ("lanes", ctypes.c_uint32),
+        ("steps", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class RansDeviceStream(ctypes.Structure):
+    _fields_ = [
+        ("h", RansHeader),
+        ("table", ctypes.c_void_p),
+        ("states", ctypes.c_void_p),
+        ("word_offsets", ctypes.c_void_p),
+        ("words", ctypes.c_void_p),
+        ("sm", ctypes.c_void_p),
+    ]
+
+
 _LIB = None
 
 
@@ -148,6 +180,13 @@ def load() -> ctypes.CDLL:
         "df11_linear_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_rans_quantize": (ctypes.c_int, [u64p, u32p]),
+        "df11_rans_encode": (ctypes.c_int, [u32p, u16p, ctypes.c_uint64, u32p, u32p, u16p, ctypes.c_uint64, u8p,
+                                            ctypes.POINTER(RansHeader)]),
+        "df11_rans_build_table": (ctypes.c_int, [u32p, u32p]),
+        "df11_rans_decompress": (ctypes.c_int, [ctypes.POINTER(RansDeviceStream), ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_rans_decompress_timed": (ctypes.c_int, [ctypes.POINTER(RansDeviceStream), ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
         "df11_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

@@ -429,3 +429,144 @@ def compress_block(weights: Union[Dict[str, ArrayLike], List[Tuple[str, ArrayLik
     data = np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint16)
     t = compress(data, shape=(data.size,), device=device, decode_table_bits=decode_table_bits)
     return DF11Block(t, views)
+
+
+# ---------------------------------------------------------------------------
+# rANS exponent coder (format in include/df11.h): the alternative entropy
+# coder that the discussion on the page names as the SIMD-friendlier one.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class RansHostStream:
+    """An rANS-coded stream in host memory."""
+
+    header: _lib.RansHeader
+    freq: np.ndarray          # 256 uint32 frequencies summing to 2^12
+    states: np.ndarray        # n_segments * 64 uint32 start states
+    word_offsets: np.ndarray  # n_segments + 1 uint32
+    words: np.ndarray         # n_words uint16
+    sm: np.ndarray            # N sign/mantissa bytes
+
+    @property
+    def n_elements(self) -> int:
+        return int(self.header.n_elements)
+
+    def compressed_bytes(self) -> int:
+        """Frequencies (2 bytes each) + start states + word offsets + words +
+        sign/mantissa bytes."""
+        return int(2 * 256 + 4 * self.states.size + 4 * self.word_offsets.size + 2 * self.words.size
+                   + self.sm.size)
+
+
+def rans_quantize(hist: np.ndarray) -> np.ndarray:
+    hist = np.ascontiguousarray(hist, dtype=np.uint64)
+    freq = np.zeros(256, np.uint32)
+    _lib.check(_lib.load().df11_rans_quantize(_ptr(hist, ctypes.c_uint64), _ptr(freq, ctypes.c_uint32)),
+               "df11_rans_quantize")
+    return freq
+
+
+def rans_encode(bf16: ArrayLike, freq: Optional[np.ndarray] = None) -> RansHostStream:
+    """rANS-encode BF16 data on the host (frequencies from the data's own
+    histogram unless given)."""
+    w = _u16(bf16)
+    lib = _lib.load()
+    if freq is None:
+        freq = rans_quantize(histogram(w))
+    freq = np.ascontiguousarray(freq, dtype=np.uint32)
+    seg = _lib.RANS_LANES * _lib.RANS_STEPS
+    n_seg = (w.size + seg - 1) // seg
+    states = np.empty(max(n_seg * _lib.RANS_LANES, 1), np.uint32)
+    offsets = np.empty(n_seg + 1, np.uint32)
+    words = np.empty(max(w.size, 1), np.uint16)
+    sm = np.empty(max(w.size, 1), np.uint8)
+    h = _lib.RansHeader()
+    _lib.check(lib.df11_rans_encode(_ptr(freq, ctypes.c_uint32), _ptr(w, ctypes.c_uint16), w.size,
+                                    _ptr(states, ctypes.c_uint32), _ptr(offsets, ctypes.c_uint32),
+                                    _ptr(words, ctypes.c_uint16), words.size, _ptr(sm, ctypes.c_uint8),
+                                    ctypes.byref(h)), "df11_rans_encode")
+    return RansHostStream(h, freq, states[:n_seg * _lib.RANS_LANES], offsets, words[:h.n_words].copy(),
+                          sm[:w.size])
+
+
+def rans_table(freq: np.ndarray) -> np.ndarray:
+    table = np.empty(_lib.RANS_TABLE_ENTRIES, np.uint32)
+    _lib.check(_lib.load().df11_rans_build_table(_ptr(np.ascontiguousarray(freq, dtype=np.uint32), ctypes.c_uint32),
+                                                 _ptr(table, ctypes.c_uint32)), "df11_rans_build_table")
+    return table
+
+
+class DF11RansTensor:
+    """An rANS-coded stream resident in GPU memory, decompressed on demand."""
+
+    def __init__(self, host: RansHostStream, shape: Sequence[int], device="cuda"):
+        import torch
+        self.shape = tuple(int(s) for s in shape)
+        self.device = torch.device(device)
+        self.host_header = host.header
+        n = host.n_elements
+
+        def up(a: np.ndarray, size: int) -> "torch.Tensor":
+            b = np.zeros(max(size, 16), dtype=np.uint8)
+            raw = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+            b[:raw.size] = raw
+            return torch.from_numpy(b).to(self.device)
+
+        n_words = int(host.header.n_words)
+        slots = (n_words + 7) // 8 * 8 + 8  # the decoder reads words 8 at a time
+        self._bufs = {
+            # (an empty stream has no frequencies and is never decoded)
+            "table": up(rans_table(host.freq) if n else np.zeros(_lib.RANS_TABLE_ENTRIES, np.uint32),
+                        4 * _lib.RANS_TABLE_ENTRIES),
+            "states": up(host.states, 4 * host.states.size),
+            "word_offsets": up(host.word_offsets, 4 * host.word_offsets.size),
+            "words": up(host.words, 2 * slots),
+            "sm": up(host.sm, (n + 63) // 64 * 64),
+        }
+        self._compressed_bytes = host.compressed_bytes()
+        s = _lib.RansDeviceStream()
+        s.h = host.header
+        for name, t in self._bufs.items():
+            setattr(s, name, t.data_ptr())
+        self._stream_struct = s
+
+    @property
+    def n_elements(self) -> int:
+        return int(self.host_header.n_elements)
+
+    @property
+    def header(self) -> _lib.RansHeader:
+        return self.host_header
+
+    def compressed_bytes(self) -> int:
+        return self._compressed_bytes
+
+    def decompress(self, out: Optional["torch.Tensor"] = None, stream=None, events=None) -> "torch.Tensor":  # noqa: F821
+        """Decode into out (a new bf16 tensor of the original shape by
+        default) on stream (torch's current stream by default); events as
+        for DF11Tensor.decompress."""
+        import torch
+        if out is None:
+            out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
+        if out.dtype != torch.bfloat16 or out.numel() != self.n_elements or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bfloat16 tensor with the stream's element count")
+        lib = _lib.load()
+        st = DF11Tensor._hip_stream(self, stream)
+        if events is None:
+            _lib.check(lib.df11_rans_decompress(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()),
+                                                st), "df11_rans_decompress")
+        else:
+            start, stop = events
+            _lib.check(lib.df11_rans_decompress_timed(ctypes.byref(self._stream_struct),
+                                                      ctypes.c_void_p(out.data_ptr()), st,
+                                                      ctypes.c_void_p(_event_handle(start, st)),
+                                                      ctypes.c_void_p(_event_handle(stop, st))),
+                       "df11_rans_decompress_timed")
+        return out
+
+
+def rans_compress(tensor: ArrayLike, shape: Optional[Sequence[int]] = None, device="cuda") -> DF11RansTensor:
+    """rANS-encode a BF16 tensor on the host and upload the stream."""
+    if shape is None:
+        shape = tuple(tensor.shape)
+    return DF11RansTensor(rans_encode(tensor), shape, device=device)

@@ -292,6 +292,98 @@ int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_token
 int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
+/* ---------------------------------------------------------------------------
+ * rANS exponent coder.  The discussion on the page ("Opini Hacker News")
+ * names rANS as an entropy coder that suits SIMD-style instruction sets better
+ * than Huffman; the page gives no format, so this one is this library's own:
+ * the plain static rANS of asymmetric numeral systems (Duda) with 16-bit
+ * renormalisation, laid out for 64-lane waves.
+ *   - Frequencies f[s] of the exponents sum to M = 2^DF11_RANS_PROB_BITS;
+ *     c[s] = f[0] + ... + f[s - 1].  A state x lies in [2^16, 2^32).
+ *   - Encoding s: while x >= f[s] * 2^(32 - prob_bits), emit x mod 2^16 and
+ *     shift it out; then x = floor(x / f[s]) * M + x mod f[s] + c[s].
+ *     Decoding: slot = x mod M, s with c[s] <= slot < c[s] + f[s],
+ *     x = f[s] * floor(x / M) + slot - c[s], and if x < 2^16,
+ *     x = x * 2^16 + the next word.
+ *   - Segments of DF11_RANS_LANES x DF11_RANS_STEPS exponents: lane l of a
+ *     segment codes its positions step * lanes + l with a state of its own
+ *     (2^16 when encoding starts).  The decoder takes a segment's words step
+ *     by step, and within a step in lane order, one per lane whose state fell
+ *     below 2^16.  Per segment the stream stores the lanes' start states and
+ *     the offset of its words.
+ * Sign/mantissa bytes are stored as for DF11 (PackedSignMantissa).
+ * ------------------------------------------------------------------------- */
+#define DF11_RANS_PROB_BITS 12
+#define DF11_RANS_LANES 64
+#define DF11_RANS_STEPS 512
+/* Entries of the decoder's slot table (M). */
+#define DF11_RANS_TABLE_ENTRIES 4096
+
+typedef struct df11_rans_header {
+    uint64_t n_elements;  /* N */
+    uint64_t n_segments;  /* ceil(N / (lanes * steps)) */
+    uint64_t n_words;     /* 16-bit words in the stream */
+    uint32_t prob_bits;   /* DF11_RANS_PROB_BITS */
+    uint32_t lanes;       /* DF11_RANS_LANES */
+    uint32_t steps;       /* DF11_RANS_STEPS */
+    uint32_t reserved;
+} df11_rans_header;
+
+/* Quantize an exponent histogram to rANS frequencies summing to 2^12 (host):
+ * every used exponent gets max(1, floor(hist * M / N)); a sum below M gives
+ * the difference to the most frequent exponent (lowest value on ties); while
+ * the sum is above M the largest frequency above 1 (lowest value on ties)
+ * drops by one.  An empty histogram gives all zeros.  Errors:
+ * DF11_E_INVALID_ARG (null pointer), DF11_E_RESERVED_EXPONENT (hist[e] > 0 for
+ * e >= 240). */
+int df11_rans_quantize(const uint64_t hist[256], uint32_t freq[256]);
+
+/* rANS-encode n BF16 words (host).  freq: from df11_rans_quantize (or any
+ * table summing to M that covers every exponent present).  Outputs (host,
+ * caller-allocated): states ceil(n / 32768) * 64 uint32; word_offsets
+ * ceil(n / 32768) + 1 uint32 (segment g's words are [word_offsets[g],
+ * word_offsets[g + 1])); words room for words_cap uint16 (n always suffices);
+ * sm n bytes.  h is filled in.  Errors: DF11_E_INVALID_ARG (null pointer, a
+ * table not summing to M, an exponent with frequency 0),
+ * DF11_E_RESERVED_EXPONENT, DF11_E_BUFFER_TOO_SMALL (words_cap), DF11_E_TOO_LARGE
+ * (n >= 2^32). */
+int df11_rans_encode(const uint32_t freq[256], const uint16_t *w, uint64_t n, uint32_t *states,
+                     uint32_t *word_offsets, uint16_t *words, uint64_t words_cap, uint8_t *sm, df11_rans_header *h);
+
+/* The decoder's slot table (host): entry k (0 <= k < 4096) is the rotated
+ * exponent s of slot k (s >> 1 | (s & 1) << 7) in bits 0-7, f[s] - 1 in bits
+ * 8-19 and k - c[s] in bits 20-31.  table: DF11_RANS_TABLE_ENTRIES uint32.
+ * Errors: DF11_E_INVALID_ARG (null pointer, a table not summing to M). */
+int df11_rans_build_table(const uint32_t freq[256], uint32_t *table);
+
+/* A device-resident rANS stream (buffers are device pointers, owned by the
+ * caller).  words holds h.n_words words followed by padding up to a multiple
+ * of 8 words plus 8 more (the decoder reads words 8 at a time), 16-byte
+ * aligned; sm holds the N sign/mantissa bytes padded to a multiple of 64,
+ * 16-byte aligned. */
+typedef struct df11_rans_device_stream {
+    df11_rans_header h;
+    const uint32_t *table;         /* DF11_RANS_TABLE_ENTRIES entries (df11_rans_build_table) */
+    const uint32_t *states;        /* h.n_segments * 64 */
+    const uint32_t *word_offsets;  /* h.n_segments + 1 */
+    const uint16_t *words;
+    const uint8_t *sm;
+} df11_rans_device_stream;
+
+/* Decode a device-resident rANS stream into out (device, N uint16, 16-byte
+ * aligned, not overlapping the stream), enqueued on hip_stream.  Every
+ * element of out is overwritten with the original BF16 bits.  A corrupt
+ * payload cannot make the kernel access memory out of bounds; its output is
+ * unspecified.  Errors: DF11_E_INVALID_ARG (null pointers, alignment, layout
+ * fields other than 12 / 64 / 512, overlap), DF11_E_BAD_STREAM (sizes
+ * inconsistent), DF11_E_TOO_LARGE, DF11_E_HIP. */
+int df11_rans_decompress(const df11_rans_device_stream *s, uint16_t *out, void *hip_stream);
+
+/* df11_rans_decompress with start_event / stop_event (hipEvent_t, either may
+ * be NULL) recorded at the decode kernel's own start and end. */
+int df11_rans_decompress_timed(const df11_rans_device_stream *s, uint16_t *out, void *hip_stream,
+                               void *start_event, void *stop_event);
+
 /* Static, human-readable name of a status code. */
 const char *df11_status_str(int status);
 

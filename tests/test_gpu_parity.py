@@ -404,3 +404,51 @@ def test_linear_full_size_block_matrix(torch_cuda, name):
     _note(f"linear full size {name} {out_f}x{in_f}")
     t = df11.compress(w, shape=(out_f, in_f))
     _check_linear(torch, t, w, _tokens(4, in_f, 11), out_f, in_f, calls=1)
+
+
+# ---------------------------------------------------------------------------
+# rANS exponent coder (df11_rans_decompress): bit-exact against the
+# original weights, whose rANS stream the library encoder writes byte for
+# byte as the oracle does (CPU tests)
+# ---------------------------------------------------------------------------
+
+RANS_SIZES = [1, 63, 64, 65, 511, 512, 513, 4097, 32767, 32768, 32769, 100_003, (1 << 20) + 17]
+
+
+@pytest.mark.parametrize("kind", ["normal", "student_t", "uniform_bits", "zeros", "fib_chain", "stress_tuned",
+                                  "stress_literal"])
+def test_rans_decode_bit_exact(torch_cuda, kind):
+    torch = torch_cuda
+    for n in RANS_SIZES:
+        _note(f"rans {kind} n={n}")
+        w = _case(kind, n, 17)
+        t = df11.rans_compress(w, shape=(n,))
+        out = torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        t.decompress(out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(_to_u16(out), w), n
+
+
+def test_rans_empty_stream(torch_cuda):
+    torch = torch_cuda
+    t = df11.rans_compress(np.zeros(0, np.uint16), shape=(0,))
+    out = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    t.decompress(out=out)
+    torch.cuda.synchronize()
+
+
+def test_rans_full_size_block_repeat_and_timed(torch_cuda):
+    """The Llama-3-8B-shaped block (218M weights) as one rANS stream:
+    bit-exact on back-to-back launches and through the timed entry point."""
+    torch = torch_cuda
+    flat, _ = workloads.gen_block()
+    _note("rans full-size block")
+    t = df11.rans_compress(flat, shape=(flat.size,))
+    out = torch.full((flat.size,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    for _ in range(2):
+        t.decompress(out=out)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t.decompress(out=out, events=ev)
+    torch.cuda.synchronize()
+    assert np.array_equal(_to_u16(out), flat)
+    assert ev[0].elapsed_time(ev[1]) > 0

@@ -59,9 +59,10 @@ def test_header_structs_match_binding_sizes():
 #include <stddef.h>
 #include "df11.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(df11_codebook), sizeof(df11_layout), sizeof(df11_header),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(df11_codebook), sizeof(df11_layout), sizeof(df11_header),
          sizeof(df11_device_stream), offsetof(df11_device_stream, enc), offsetof(df11_device_stream, decode_table_bits),
-         offsetof(df11_header, max_group_elems));
+         offsetof(df11_header, max_group_elems), sizeof(df11_rans_header), sizeof(df11_rans_device_stream),
+         offsetof(df11_rans_device_stream, table), offsetof(df11_rans_header, prob_bits));
   return 0;
 }
 """
@@ -74,7 +75,8 @@ int main(void) {
         got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(_lib.Codebook), ctypes.sizeof(_lib.Layout), ctypes.sizeof(_lib.Header),
             ctypes.sizeof(_lib.DeviceStream), _lib.DeviceStream.enc.offset, _lib.DeviceStream.decode_table_bits.offset,
-            _lib.Header.max_group_elems.offset]
+            _lib.Header.max_group_elems.offset, ctypes.sizeof(_lib.RansHeader), ctypes.sizeof(_lib.RansDeviceStream),
+            _lib.RansDeviceStream.table.offset, _lib.RansHeader.prob_bits.offset]
     assert got == want
 
 
@@ -352,3 +354,127 @@ def test_linear_validation_runs_before_any_launch():
     es = _lib.DeviceStream()
     es.h = empty.header
     assert lib.df11_linear(ctypes.byref(es), None, 1, 1024, 0, None, None) == 0
+
+
+# ---------------------------------------------------------------------------
+# rANS coder: the library's encoder against the oracle's, byte for byte
+# ---------------------------------------------------------------------------
+
+def test_rans_constants_match_header():
+    import re
+    with open(os.path.join(os.path.dirname(__file__), "..", "include", "df11.h")) as f:
+        text = f.read()
+    for name, val in (("PROB_BITS", _lib.RANS_PROB_BITS), ("LANES", _lib.RANS_LANES), ("STEPS", _lib.RANS_STEPS),
+                      ("TABLE_ENTRIES", _lib.RANS_TABLE_ENTRIES)):
+        assert int(re.search(r"#define\s+DF11_RANS_%s\s+(\d+)" % name, text).group(1)) == val
+    assert oracle.RANS_PROB_BITS == _lib.RANS_PROB_BITS and oracle.RANS_LANES == _lib.RANS_LANES
+    assert oracle.RANS_STEPS == _lib.RANS_STEPS
+
+
+def _rans_equal(w):
+    h = df11.rans_encode(w)
+    o = oracle.rans_encode(w)
+    assert np.array_equal(h.freq, o["freq"])
+    assert np.array_equal(h.states, o["states"])
+    assert np.array_equal(h.word_offsets, o["word_offsets"].astype(np.uint32))
+    assert np.array_equal(h.words, o["words"])
+    assert np.array_equal(h.sm, o["sm"])
+    assert h.compressed_bytes() == oracle.rans_compressed_bytes(o)
+    assert int(h.header.n_words) == o["words"].size
+    return h
+
+
+@pytest.mark.parametrize("name", ["single_1024x1024", "proj_4096x4096_outliers"])
+def test_rans_encoder_matches_oracle_bytes(workload, name):
+    w = workload(name)[:5_000_000]
+    h = _rans_equal(w)
+    assert 8 * h.compressed_bytes() / w.size < 10.75  # below DF11's ~10.8 bits per weight here
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 64, 65, 32767, 32768, 32769, 100_003])
+def test_rans_encoder_matches_oracle_ragged(n):
+    rng = np.random.default_rng(n)
+    _rans_equal(workloads.f32_to_bf16_bits(rng.standard_normal(n) * 0.02))
+
+
+def test_rans_encoder_matches_oracle_special_streams():
+    _rans_equal(np.full(70_000, 120 << 7, np.uint16))           # one exponent: no words
+    _rans_equal(workloads.gen_stress(seed=4, n=300_000))        # 29-30-bit Huffman codes
+    _rans_equal(workloads.gen_stress(seed=4, n=300_000, kind="literal"))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rans_quantize_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    hist = np.zeros(256, np.uint64)
+    used = rng.choice(240, size=int(rng.integers(1, 240)), replace=False)
+    hist[used] = rng.integers(1, 10 ** int(rng.integers(1, 9)), used.size)
+    assert np.array_equal(df11.rans_quantize(hist), oracle.rans_quantize(hist))
+
+
+def test_rans_slot_table_matches_definition():
+    """Entry k: rotated exponent of the slot's symbol, f - 1, k - c."""
+    w = workloads.gen_stress(seed=4, n=200_000)
+    freq = df11.rans_quantize(df11.histogram(w))
+    table = df11.rans_table(freq)
+    cum = np.concatenate([[0], np.cumsum(freq)]).astype(np.int64)
+    for k in range(0, 4096, 7):
+        s = int(np.searchsorted(cum, k, side="right") - 1)
+        assert cum[s] <= k < cum[s + 1]
+        e = int(table[k])
+        assert e & 0xFF == ((s >> 1) | ((s & 1) << 7)) & 0xFF
+        assert (e >> 8) & 0xFFF == freq[s] - 1
+        assert e >> 20 == k - cum[s]
+
+
+def test_rans_errors():
+    lib = _lib_or_skip()
+    hist = np.zeros(256, np.uint64)
+    hist[245] = 3
+    freq = np.zeros(256, np.uint32)
+    assert lib.df11_rans_quantize(hist.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                  freq.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))) == -2
+    bad = np.zeros(256, np.uint32)
+    bad[100] = 4095  # does not sum to 4096
+    table = np.zeros(4096, np.uint32)
+    assert lib.df11_rans_build_table(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                     table.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))) == -1
+
+
+def test_rans_decompress_validation_runs_before_any_launch():
+    """Every df11_rans_decompress argument error is found before a launch (no GPU here)."""
+    lib = _lib_or_skip()
+    host = df11.rans_encode(workloads.gen_single_matrix(rows=64, cols=1024))
+    s = _lib.RansDeviceStream()
+    s.h = host.header
+    addr = 1 << 40
+    for name in ("table", "states", "word_offsets", "words", "sm"):
+        setattr(s, name, addr)
+        addr += 1 << 32
+    out = ctypes.c_void_p(1 << 48)
+
+    def call(st, o=out):
+        return lib.df11_rans_decompress(ctypes.byref(st), o, None)
+
+    assert lib.df11_rans_decompress(None, out, None) == -1
+    for field, val, rc in (("prob_bits", 11, -1), ("lanes", 32, -1), ("steps", 256, -1), ("n_segments", 5, -6)):
+        bad = _lib.RansDeviceStream.from_buffer_copy(s)
+        setattr(bad.h, field, val)
+        assert call(bad) == rc, field
+    bad = _lib.RansDeviceStream.from_buffer_copy(s)
+    bad.h.n_words = bad.h.n_elements + 1
+    assert call(bad) == -6
+    bad = _lib.RansDeviceStream.from_buffer_copy(s)
+    bad.h.n_elements = 1 << 32
+    assert call(bad) == -7
+    bad = _lib.RansDeviceStream.from_buffer_copy(s)
+    bad.words = (1 << 40) + 8  # not 16-byte aligned
+    assert call(bad) == -1
+    assert call(s, ctypes.c_void_p((1 << 48) + 8)) == -1       # misaligned output
+    assert call(s, ctypes.c_void_p(s.sm)) == -1                # output over the stream
+    bad = _lib.RansDeviceStream.from_buffer_copy(s)
+    bad.table = None
+    assert call(bad) == -1
+    empty = _lib.RansDeviceStream()
+    empty.h = df11.rans_encode(np.zeros(0, np.uint16)).header
+    assert lib.df11_rans_decompress(ctypes.byref(empty), None, None) == 0
