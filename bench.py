@@ -72,6 +72,17 @@ def _cpu_baseline(flat: np.ndarray, threads: int):
     return algo / dt / 1e9, dt, ok
 
 
+def _cpu_baseline_rans(flat: np.ndarray):
+    """The oracle's rANS decoder (one host thread) on the whole stream."""
+    import oracle
+    s = oracle.rans_encode(flat)
+    t0 = time.perf_counter()
+    out = oracle.rans_decode(s)
+    dt = time.perf_counter() - t0
+    algo = oracle.rans_compressed_bytes(s) + 2 * s["n_elements"]
+    return algo / dt / 1e9, dt, bool(np.array_equal(out, flat))
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -437,6 +448,8 @@ def main() -> int:
     ap.add_argument("--blocks", type=int, default=4, help="blocks of the --integration model")
     ap.add_argument("--overlap-workgroups", type=int, default=512,
                     help="workgroup cap of the side-stream decode in --integration (0: no cap)")
+    ap.add_argument("--coder", choices=["huffman", "rans"], default="huffman",
+                    help="entropy coder of the exponents: the page's Huffman format, or the rANS alternative")
     ap.add_argument("--linear-tokens", type=int, default=0,
                     help="time the decode fused into y = x W^T over the block's seven matrices at this many "
                          "tokens (1..8) instead of the decompression")
@@ -486,7 +499,19 @@ def main() -> int:
     n = int(flat.size)
     t0 = time.perf_counter()
     config = {"workload": wl}
-    if views is not None:
+    if args.coder == "rans":
+        if wl.endswith("_per_weight"):
+            print("bench: the rANS coder takes the block as one stream (llama3_8b_block)", file=sys.stderr)
+            return 2
+        t = df11.rans_compress(flat, shape=(n,), device=dev)
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        h, comp = t.header, t.compressed_bytes()
+        config["coder"] = "rans"
+        config["rans"] = {"prob_bits": int(h.prob_bits), "lanes": int(h.lanes), "steps": int(h.steps),
+                          "segments": int(h.n_segments), "words": int(h.n_words)}
+        decode = lambda ev=None: t.decompress(out=out, events=ev)  # noqa: E731
+        decoded = lambda: out.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    elif views is not None:
         codebook = "per_weight" if wl.endswith("_per_weight") else "shared"
         blk = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views], device=dev,
                                   decode_table_bits=args.decode_table_bits, codebook=codebook)
@@ -567,7 +592,7 @@ def main() -> int:
     copy_gbps = 10 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    traffic = _traffic_from_profile() if wl == DEFAULT_WORKLOAD else None
+    traffic = _traffic_from_profile() if wl == DEFAULT_WORKLOAD and args.coder == "huffman" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -586,9 +611,8 @@ def main() -> int:
             "n_elements": n,
             "bits_per_weight": round(8 * comp / n, 4),
             "compressed_bytes": comp,
-            "decode_table_bits": args.decode_table_bits,
-            "max_code_len": int(h.max_len),
-            "n_luts": int(h.n_luts),
+            **({"decode_table_bits": args.decode_table_bits, "max_code_len": int(h.max_len),
+                "n_luts": int(h.n_luts)} if args.coder == "huffman" else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -608,15 +632,19 @@ def main() -> int:
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or len(os.sched_getaffinity(0))
         threads = min(threads, 16)
-        cpu_gbps, cpu_s, ok = _cpu_baseline(flat, threads)
+        if args.coder == "rans":
+            cpu_gbps, cpu_s, ok = _cpu_baseline_rans(flat)
+            threads, how = 1, "rANS decode on one thread"
+        else:
+            cpu_gbps, cpu_s, ok = _cpu_baseline(flat, threads)
+            how = f"tree-walk decode split by groups over {threads} threads"
         result["cpu_baseline"] = {
             "value": round(cpu_gbps, 3),
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {wl} data as one stream ({n} weights), tree-walk decode split by groups "
-                      f"over {threads} threads; {cpu_s:.2f} s wall; output {'matches' if ok else 'DIFFERS FROM'} "
-                      f"the original weights",
+            "sample": f"the whole {wl} data as one stream ({n} weights), {how}; {cpu_s:.2f} s wall; output "
+                      f"{'matches' if ok else 'DIFFERS FROM'} the original weights",
         }
     print(json.dumps(result), flush=True)
     return 0

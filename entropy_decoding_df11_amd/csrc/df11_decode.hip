@@ -1060,6 +1060,33 @@ __device__ __forceinline__ void rans_merge(const RansArgs &a, const uint8_t *sta
     }
 }
 
+// kRansSub decoding steps of one wave (see df11_rans_decode_kernel); kFull:
+// every lane has a symbol in every step.  The next word is read by every
+// lane whether or not its state needs one (the empty asm keeps the read
+// unconditional, so the step has no branch); lanes that need none discard it.
+template <bool kFull>
+__device__ __forceinline__ void rans_steps(const uint32_t *s_tab, const uint16_t *ring, uint8_t *stage, uint32_t &x,
+                                           uint32_t &ptr, uint32_t q0, uint32_t count, uint32_t lane) {
+#pragma unroll
+    for (uint32_t jj = 0; jj < kRansSub; ++jj) {
+        const bool active = kFull || q0 + jj * kRansLanes + lane < count;
+        const uint32_t e = s_tab[x & (DF11_RANS_TABLE_ENTRIES - 1u)];
+        const uint32_t xs = x >> DF11_RANS_PROB_BITS;
+        const uint32_t xn = ((e >> 8) & 0xFFFu) * xs + xs + (e >> 20);  // f * floor(x / M) + slot - c
+        const bool need = active && xn < kRansStateLow;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+        // ptr + (lanes below this one that need a word)
+        const uint32_t k = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), ptr));
+        uint32_t word = ring[k & (kRansRing - 1u)];
+        asm volatile("" : "+v"(word));
+        const uint32_t xr = (xn << 16) | word;
+        x = need ? xr : (active ? xn : x);
+        stage[jj * kRansLanes + lane] = static_cast<uint8_t>(active ? e : 0u);
+        ptr += static_cast<uint32_t>(__builtin_popcountll(m));
+    }
+}
+
 __global__ __launch_bounds__(kWaveSize *kRansWaves) void df11_rans_decode_kernel(RansArgs a) {
     __shared__ __align__(16) uint32_t s_tab[DF11_RANS_TABLE_ENTRIES];
     __shared__ __align__(16) uint8_t s_stage[kRansWaves][kRansSubElems];
@@ -1100,21 +1127,10 @@ __global__ __launch_bounds__(kWaveSize *kRansWaves) void df11_rans_decode_kernel
             const uint32_t pf_c = ptr / kRansChunk + 2u;
             const uint4 pf = rans_chunk8(a, pf_c, lane);
             const uint64_t smv = rans_sm8(a, (seg0 + q0) / 8u + lane);
-#pragma unroll
-            for (uint32_t jj = 0; jj < kRansSub; ++jj) {
-                const bool active = q0 + jj * kRansLanes + lane < count;
-                const uint32_t e = s_tab[x & (DF11_RANS_TABLE_ENTRIES - 1u)];
-                const uint32_t xs = x >> DF11_RANS_PROB_BITS;
-                const uint32_t xn = ((e >> 8) & 0xFFFu) * xs + xs + (e >> 20);  // f * floor(x / M) + slot - c
-                const bool need = active && xn < kRansStateLow;
-                const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-                const uint32_t k = ptr + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-                const uint32_t word = ring[k & (kRansRing - 1u)];
-                x = need ? (xn << 16) | word : (active ? xn : x);
-                stage[jj * kRansLanes + lane] = static_cast<uint8_t>(active ? e : 0u);
-                ptr += static_cast<uint32_t>(__builtin_popcountll(m));
-            }
+            if (q0 + kRansSubElems <= count)
+                rans_steps<true>(s_tab, ring, stage, x, ptr, q0, count, lane);
+            else
+                rans_steps<false>(s_tab, ring, stage, x, ptr, q0, count, lane);
             rans_ring_put(ring, pf_c, lane, pf);
             rans_merge(a, stage, smv, seg0 + q0, min(kRansSubElems, count - q0), lane);
         }
