@@ -223,6 +223,34 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
         f.write("\n".join(lines))
 
 
+def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, command: str, out_name: str) -> None:
+    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of this
+    script (prof_dir/sub, its bench line in prof_dir/sub.json): the stats
+    table and the kernel's average over the run's timed launches (the last
+    `steps` launches of `kernel`) against the bench line's event timing."""
+    with open(os.path.join(prof_dir, sub + ".json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    stats = _read_csv(os.path.join(prof_dir, sub, "run_kernel_stats.csv"))
+    rows = [r for r in _read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv")) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-bench["steps"]:]]
+    algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
+    avg = float(np.mean(timed_us))
+    lines = [f"# {title}: rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box):",
+             "", "    " + command, "", "| kernel | calls | average us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in stats[:6]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
+    lines += ["", f"Over the {len(timed_us)} timed launches (the last ones in the trace) the kernel averages "
+              f"{avg:.2f} us (min {min(timed_us):.2f}, max {max(timed_us):.2f}) for {algo} algorithmic bytes: "
+              f"{algo / (avg * 1e-6) / 1e9:.1f} GB/s, {algo / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s.  "
+              f"The bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with the events that "
+              f"the kernel dispatch records.", "", "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+    with open(os.path.join(REPO, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines))
+
+
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
     weights, DF11 blocks decoded in line before each block, and DF11 blocks
@@ -472,6 +500,13 @@ def main() -> int:
                                      pre + "rocprofv3 --kernel-trace --stats -d $D/lin_trace -o run --output-format csv "
                                            "-- python3 $R/bench.py --linear-tokens 1 --steps 50 --warmup 20 "
                                            "--no-cpu-baseline > $D/lin.json")
+        if os.path.isdir(os.path.join(args.summarize_profiles, "rans_trace")):
+            summarize_kernel_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
+                                   "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
+                                   pre + "rocprofv3 --kernel-trace --stats -d $D/rans_trace -o run --output-format csv "
+                                         "-- python3 $R/bench.py --coder rans --steps 100 --warmup 100 "
+                                         "--no-cpu-baseline > $D/rans_trace.json",
+                                   "df11_rans_decode_kernel_llama3_8b_block_trace.md")
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
