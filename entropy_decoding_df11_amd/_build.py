@@ -63,12 +63,14 @@ def build(verbose: bool = False) -> str:
         _run(["g++", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         host_objs.append(obj)
-    dev_obj = os.path.join(BUILD_DIR, "df11_decode.o")
-    _run([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, "df11_decode.hip"),
-          "-o", dev_obj], verbose)
+    dev_objs = []
+    for src in ("df11_decode.hip", "df11_rans_decode.hip"):
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        _run([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        dev_objs.append(obj)
     rpaths = [p for p in (_torch_lib_dir(), os.path.join(ROCM, "lib")) if p]
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, *host_objs, dev_obj,
+    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, *host_objs, *dev_objs,
           *[f"-Wl,-rpath,{p}" for p in rpaths]], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
