@@ -390,6 +390,17 @@ def linear_bench(args, dev) -> int:
     decode_gemm_ms = timed(lambda: [F.linear(m[5], m[3].decompress(out=scratch[:m[1] * m[2]].view(m[1], m[2])))
                                     for m in mats])
     fused_ms = timed(step)
+    # As a forward issues them: q, k, v on one x in one launch, o, gate and
+    # up on one x in one launch, down (df11_linear_batch).
+    by = {m[0]: m for m in mats}
+
+    def step_batched():
+        df11.linear_batch([by[n][3] for n in ("q_proj", "k_proj", "v_proj")], by["q_proj"][5])
+        by["o_proj"][3].linear(by["o_proj"][5], out=by["o_proj"][6])
+        df11.linear_batch([by[n][3] for n in ("gate_proj", "up_proj")], by["gate_proj"][5])
+        by["down_proj"][3].linear(by["down_proj"][5], out=by["down_proj"][6])
+
+    batched_ms = timed(step_batched)
     result = {
         "metric": "DF11 decode fused into y = x W^T: GB/s of compressed weights + x + y per step",
         "value": round(args.steps * algo_bytes / wall / 1e9, 2),
@@ -423,7 +434,9 @@ def linear_bench(args, dev) -> int:
         },
         "kernel_ms_mean": round(mean_ms, 5),
         "per_matrix_us": per_matrix_us,
-        "same_run_ms_per_step": {"fused_df11": round(fused_ms, 4), "resident_bf16_F_linear": round(resident_ms, 4),
+        "same_run_ms_per_step": {"fused_df11": round(fused_ms, 4),
+                                 "fused_df11_qkv_and_gate_up_batched": round(batched_ms, 4),
+                                 "resident_bf16_F_linear": round(resident_ms, 4),
                                  "decode_then_F_linear": round(decode_gemm_ms, 4)},
         "outputs": "within the float32 summation bound of a float64 product",
         "host_prep_s": round(t_prep, 1),

@@ -47,6 +47,7 @@ EXPORTED = [
     "df11_decompress_timed",
     "df11_linear",
     "df11_linear_timed",
+    "df11_linear_batch",
     "df11_rans_quantize",
     "df11_rans_encode",
     "df11_rans_build_table",
@@ -180,6 +181,10 @@ def load() -> ctypes.CDLL:
         "df11_linear_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_linear_batch": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32, ctypes.c_void_p,
+                                             ctypes.c_uint32, ctypes.c_uint32, u32p,
+                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
         "df11_rans_quantize": (ctypes.c_int, [u64p, u32p]),
         "df11_rans_encode": (ctypes.c_int, [u32p, u16p, ctypes.c_uint64, u32p, u32p, u16p, ctypes.c_uint64, u8p,
                                             ctypes.POINTER(RansHeader)]),

@@ -942,6 +942,41 @@ __global__ __launch_bounds__(256) void df11_zero_kernel(float *y, uint32_t n) {
     for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) y[i] = 0.0f;
 }
 
+// Several weight matrices multiplying the same x in one launch (a block's q,
+// k and v, or gate and up): the grid is split between them as for
+// df11_decode_batch_kernel.
+struct LinearBatchArgs {
+    DecodeArgs s[kMaxBatch];
+    MatmulArgs m[kMaxBatch];
+    uint32_t wg_begin[kMaxBatch + 1];  // stream i owns permuted ids [wg_begin[i], wg_begin[i + 1])
+    uint32_t n;
+    uint32_t stride;  // coprime to the grid size
+};
+
+template <int K, int TB>
+__global__ __launch_bounds__(kThreadsPerGroup *kLinearGPW) void df11_linear_batch_kernel(LinearBatchArgs b) {
+    const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
+    uint32_t i = 0;
+    while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
+    decode_stream<K, kLinearGPW, TB>(b.s[i], b.m[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+}
+
+// Zero several outputs: y[i] has end[i] - end[i - 1] floats (end[-1] = 0).
+struct ZeroArgs {
+    float *y[kMaxBatch];
+    uint32_t end[kMaxBatch];
+    uint32_t n;
+};
+
+__global__ __launch_bounds__(256) void df11_zero_batch_kernel(ZeroArgs z) {
+    const uint32_t total = z.end[z.n - 1];
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+        uint32_t k = 0;
+        while (i >= z.end[k]) ++k;
+        z.y[k][i - (k ? z.end[k - 1] : 0u)] = 0.0f;
+    }
+}
+
 
 int validate(const df11_device_stream *s) {
     if (!s) return DF11_E_INVALID_ARG;
@@ -1224,15 +1259,18 @@ int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hip
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
 
-int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
-                uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+// Checks one product's arguments (no launch) and fills its kernel arguments;
+// *empty is set for a stream with no rows (nothing to launch).
+int linear_args(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, DecodeArgs &a, MatmulArgs &m, bool &empty) {
     int rc = validate(s);
     if (rc) return rc;
     const df11_header &h = s->h;
     if (n_tokens < 1 || n_tokens > DF11_LINEAR_MAX_TOKENS || in_features < DF11_LINEAR_MIN_IN_FEATURES ||
         in_features % 8 || static_cast<uint64_t>(in_features) * out_features != h.n_elements)
         return DF11_E_INVALID_ARG;
-    if (h.n_elements == 0) return DF11_OK;
+    empty = h.n_elements == 0;
+    if (empty) return DF11_OK;
     if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return DF11_E_INVALID_ARG;
     const uint64_t y_bytes = 4ull * n_tokens * out_features, x_bytes = 2ull * n_tokens * in_features;
     if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, s->enc, h.enc_bytes) ||
@@ -1243,9 +1281,8 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
         overlaps(y, y_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
         return DF11_E_INVALID_ARG;
     if (y_bytes / 4 >= (1ull << 32)) return DF11_E_TOO_LARGE;
-    DecodeArgs a;
     fill_args(s, a);
-    MatmulArgs m{};
+    m = MatmulArgs{};
     m.x = x;
     m.y = y;
     m.row_magic = ~0ull / in_features + 1ull;  // umulhi64(i, row_magic) == i / in_features for all i < 2^32
@@ -1253,10 +1290,21 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
     m.out_features = out_features;
     m.n_tokens = n_tokens;
     m.yacc_rows = (a.ebuf_cap - 1u) / in_features + 2u;
-    const uint32_t tb = n_tokens <= 1 ? 1 : n_tokens <= 2 ? 2 : n_tokens <= 4 ? 4 : 8;
+    return DF11_OK;
+}
+
+uint32_t token_slots(uint32_t n_tokens) { return n_tokens <= 1 ? 1 : n_tokens <= 2 ? 2 : n_tokens <= 4 ? 4 : 8; }
+
+int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    DecodeArgs a;
+    MatmulArgs m;
+    bool empty = false;
+    const int rc = linear_args(s, x, n_tokens, in_features, out_features, y, a, m, empty);
+    if (rc || empty) return rc;
 #define DF11_LINEAR_CASE(KB)                                                       \
     case KB:                                                                       \
-        switch (tb) {                                                              \
+        switch (token_slots(n_tokens)) {                                           \
         case 1: return launch_linear<KB, 1>(a, m, s->max_workgroups, stream, start, stop); \
         case 2: return launch_linear<KB, 2>(a, m, s->max_workgroups, stream, start, stop); \
         case 4: return launch_linear<KB, 4>(a, m, s->max_workgroups, stream, start, stop); \
@@ -1269,6 +1317,113 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
     default: return DF11_E_INVALID_ARG;
     }
 #undef DF11_LINEAR_CASE
+}
+
+// Zero every output, then the batched fused kernel over the persistent grid
+// split between the streams in proportion to their super-groups.
+template <int K, int TB>
+int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
+    size_t lds = 0;
+    uint64_t total_super = 0;
+    for (uint32_t i = 0; i < b.n; ++i) {
+        lds = std::max(lds, dynamic_lds<kLinearGPW>(b.s[i]) + sizeof(float) * kLinearGPW * b.m[i].yacc_rows * TB);
+        total_super += (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
+    }
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const void *fn = reinterpret_cast<const void *>(&df11_linear_batch_kernel<K, TB>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kLinearGPW, dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
+    uint32_t next = 0;
+    for (uint32_t i = 0; i < b.n; ++i) {
+        const uint64_t n_super = (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
+        const uint32_t share = schedule_pools(b.s[i], n_super, resident * n_super / total_super);
+        b.wg_begin[i] = next;
+        next += share;
+    }
+    b.wg_begin[b.n] = next;
+    b.stride = 1;
+    for (uint32_t c = std::max<uint32_t>(1, static_cast<uint32_t>(next * 0.618)); c < 2 * next + 2; ++c)
+        if (std::gcd(c, next) == 1) {
+            b.stride = c;
+            break;
+        }
+    (void)hipGetLastError();
+    const uint32_t total = z.end[z.n - 1];
+    void *zparams[] = {&z};
+    const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((total + 255) / 256, 1024));
+    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256), zparams, 0,
+                           stream, nullptr, nullptr, 0) != hipSuccess)
+        return DF11_E_HIP;
+    void *params[] = {&b};
+    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop, 0) !=
+        hipSuccess)
+        return DF11_E_HIP;
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+}
+
+int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *x, uint32_t n_tokens,
+                      uint32_t in_features, const uint32_t *out_features, float *const *ys, hipStream_t stream,
+                      hipEvent_t start, hipEvent_t stop) {
+    if (n > kMaxBatch) return DF11_E_TOO_LARGE;
+    if (n && (!ws || !out_features || !ys)) return DF11_E_INVALID_ARG;
+    LinearBatchArgs b{};
+    ZeroArgs z{};
+    uint32_t bits = 0, max_wg = 0, total = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        DecodeArgs a;
+        MatmulArgs m;
+        bool empty = false;
+        const int rc = linear_args(&ws[i], x, n_tokens, in_features, out_features[i], ys[i], a, m, empty);
+        if (rc) return rc;
+        // every output must also stay clear of the other outputs and the other streams' buffers
+        const uint64_t y_bytes = 4ull * n_tokens * out_features[i];
+        for (uint32_t j = 0; j < n && !empty; ++j) {
+            if (j == i) continue;
+            const df11_device_stream &o = ws[j];
+            if (overlaps(ys[i], y_bytes, ys[j], 4ull * n_tokens * out_features[j]) ||
+                overlaps(ys[i], y_bytes, o.enc, o.h.enc_bytes) || overlaps(ys[i], y_bytes, o.sm, o.h.sm_bytes) ||
+                overlaps(ys[i], y_bytes, o.gaps, o.h.gaps_bytes) ||
+                overlaps(ys[i], y_bytes, o.out_pos, o.h.out_pos_bytes) ||
+                overlaps(ys[i], y_bytes, o.luts, 256ull * o.h.n_luts) ||
+                overlaps(ys[i], y_bytes, o.code_lengths, 256) ||
+                overlaps(ys[i], y_bytes, o.decode_table, df11_decode_table_bytes(o.decode_table_bits)) ||
+                overlaps(ys[i], y_bytes, o.schedule, o.schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
+                return DF11_E_INVALID_ARG;
+        }
+        if (empty) continue;
+        if (b.n && ws[i].decode_table_bits != bits) return DF11_E_INVALID_ARG;
+        bits = ws[i].decode_table_bits;
+        if (ws[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, ws[i].max_workgroups) : ws[i].max_workgroups;
+        if (static_cast<uint64_t>(total) + static_cast<uint64_t>(n_tokens) * out_features[i] >= (1ull << 32))
+            return DF11_E_TOO_LARGE;
+        total += n_tokens * out_features[i];
+        z.y[b.n] = ys[i];
+        z.end[b.n] = total;
+        b.s[b.n] = a;
+        b.m[b.n] = m;
+        ++b.n;
+    }
+    if (b.n == 0) return DF11_OK;
+    z.n = b.n;
+#define DF11_LINEAR_BATCH_CASE(KB)                                                              \
+    case KB:                                                                                    \
+        switch (token_slots(n_tokens)) {                                                        \
+        case 1: return launch_linear_batch<KB, 1>(b, z, max_wg, stream, start, stop);           \
+        case 2: return launch_linear_batch<KB, 2>(b, z, max_wg, stream, start, stop);           \
+        case 4: return launch_linear_batch<KB, 4>(b, z, max_wg, stream, start, stop);           \
+        default: return launch_linear_batch<KB, 8>(b, z, max_wg, stream, start, stop);          \
+        }
+    switch (bits) {
+        DF11_LINEAR_BATCH_CASE(10)
+        DF11_LINEAR_BATCH_CASE(11)
+        DF11_LINEAR_BATCH_CASE(12)
+    default: return DF11_E_INVALID_ARG;
+    }
+#undef DF11_LINEAR_BATCH_CASE
 }
 
 }  // namespace
@@ -1306,6 +1461,14 @@ int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event) {
     return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream),
                        static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+}
+
+int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
+                      uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
+                      void *start_event, void *stop_event) {
+    return linear_batch_impl(ws, n_streams, x, n_tokens, in_features, out_features, ys,
+                             static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
+                             static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"

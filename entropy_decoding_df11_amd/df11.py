@@ -271,6 +271,43 @@ class DF11Tensor:
         return out
 
 
+def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, stream=None,  # noqa: F821
+                 events=None) -> List["torch.Tensor"]:  # noqa: F821
+    """[x W_i^T for each W_i in tensors] in one launch (df11_linear_batch):
+    every W_i is (out_features_i, in_features) with the same in_features, x
+    a contiguous bfloat16 (n_tokens, in_features) tensor, 1 <= n_tokens <= 8
+    (a block's q, k and v, or gate and up).  Returns the float32 outputs
+    (new tensors by default); events as for DF11Tensor.linear."""
+    import torch
+    if not tensors:
+        return []
+    if len(tensors) > _lib.MAX_BATCH:
+        raise ValueError(f"at most {_lib.MAX_BATCH} matrices per launch")
+    in_f = tensors[0].shape[1] if len(tensors[0].shape) == 2 else -1
+    if any(len(t.shape) != 2 or t.shape[1] != in_f for t in tensors):
+        raise ValueError("every weight must be 2-D with the same in_features")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
+    n_tokens = x.shape[0]
+    if outs is None:
+        outs = [torch.empty((n_tokens, t.shape[0]), dtype=torch.float32, device=x.device) for t in tensors]
+    for t, y in zip(tensors, outs):
+        if y.dtype != torch.float32 or y.shape != (n_tokens, t.shape[0]) or not y.is_contiguous():
+            raise ValueError("each output must be a contiguous float32 (n_tokens, out_features) tensor")
+    lib = _lib.load()
+    st = tensors[0]._hip_stream(stream)
+    arr = (_lib.DeviceStream * len(tensors))(*[t._stream_struct for t in tensors])
+    out_f = np.array([t.shape[0] for t in tensors], np.uint32)
+    ptrs = (ctypes.c_void_p * len(tensors))(*[y.data_ptr() for y in outs])
+    ev = (None, None) if events is None else (ctypes.c_void_p(_event_handle(events[0], st)),
+                                              ctypes.c_void_p(_event_handle(events[1], st)))
+    _lib.check(lib.df11_linear_batch(arr, len(tensors), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f,
+                                     _ptr(out_f, ctypes.c_uint32), ptrs, st, *ev), "df11_linear_batch")
+    return outs
+
+
 def _event_handle(ev, stream: ctypes.c_void_p) -> int:
     """The hipEvent_t behind a torch.cuda.Event, created by recording it once
     on the launch stream (the decode launch records it again)."""

@@ -292,6 +292,28 @@ int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_token
 int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
+/* df11_linear for several weight matrices that multiply the same x -- a
+ * transformer block's q, k and v projections, or its gate and up projections
+ * -- in one launch, the grid split between them in proportion to their work
+ * (small matrices alone cannot fill the GPU).
+ *   ws            host array of n_streams device streams (as for df11_linear);
+ *                 the non-empty ones must share decode_table_bits
+ *   x, n_tokens, in_features   shared by all, as for df11_linear
+ *   out_features  host array: rows of each matrix
+ *   ys            host array of device outputs, n_tokens x out_features[i]
+ *                 floats each, overlapping neither each other, x nor any
+ *                 stream's buffers; overwritten
+ *   start_event, stop_event   hipEvent_t or NULL, recorded at the fused
+ *                 kernel's own start and end
+ * One kernel zeroes every output, then one fused kernel runs.  Errors:
+ * DF11_E_TOO_LARGE (n_streams > DF11_MAX_BATCH, or the outputs' total
+ * >= 2^32 floats), DF11_E_INVALID_ARG (as for df11_linear, mismatched table
+ * widths, overlaps), DF11_E_BAD_STREAM, DF11_E_HIP.  Nothing is launched
+ * unless every stream is valid. */
+int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
+                      uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
+                      void *start_event, void *stop_event);
+
 /* ---------------------------------------------------------------------------
  * rANS exponent coder.  The discussion on the page ("Opini Hacker News")
  * names rANS as an entropy coder that suits SIMD-style instruction sets better

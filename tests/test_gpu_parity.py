@@ -452,3 +452,48 @@ def test_rans_full_size_block_repeat_and_timed(torch_cuda):
     torch.cuda.synchronize()
     assert np.array_equal(_to_u16(out), flat)
     assert ev[0].elapsed_time(ev[1]) > 0
+
+
+@pytest.mark.parametrize("n_tokens", [1, 3, 8])
+def test_linear_batch_matches_oracle(torch_cuda, n_tokens):
+    """q, k and v shaped matrices (different row counts, each its own
+    stream) multiplying one x in one launch, each output within the float32
+    bound of the oracle; an empty matrix in the batch is skipped."""
+    torch = torch_cuda
+    _note(f"linear batch tokens={n_tokens}")
+    in_f = 1024
+    shapes = [(300, in_f), (77, in_f), (128, in_f), (0, in_f)]
+    ws = [_case("normal" if i % 2 == 0 else "student_t", r * c, 40 + i) for i, (r, c) in enumerate(shapes)]
+    ts = [df11.compress(w, shape=s) for w, s in zip(ws, shapes)]
+    x = _tokens(n_tokens, in_f, 5)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    for _ in range(2):
+        ys = df11.linear_batch(ts, xd)
+        torch.cuda.synchronize()
+        for w, (r, c), y in zip(ws, shapes, ys):
+            if r == 0:
+                assert y.numel() == 0
+                continue
+            ref = oracle.linear(oracle.encode(w), x, r)
+            err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+            assert np.all(err <= _linear_bound(x, w, r, c))
+
+
+def test_linear_batch_full_size_qkv(torch_cuda):
+    """The Llama-3-8B q, k and v projections (4096, 1024 and 1024 rows of
+    4096) in one launch at one token, against the oracle."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block(seed=3)
+    ws, shapes = [], []
+    for nm, o, (r, c) in views[:3]:
+        ws.append(np.ascontiguousarray(flat[o:o + r * c]))
+        shapes.append((r, c))
+    del flat
+    _note("linear batch full-size qkv")
+    ts = [df11.compress(w, shape=s) for w, s in zip(ws, shapes)]
+    x = _tokens(1, 4096, 12)
+    ys = df11.linear_batch(ts, torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16))
+    torch.cuda.synchronize()
+    for w, (r, c), y in zip(ws, shapes, ys):
+        ref = oracle.linear(oracle.encode(w), x, r)
+        assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= _linear_bound(x, w, r, c))

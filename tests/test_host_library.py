@@ -478,3 +478,29 @@ def test_rans_decompress_validation_runs_before_any_launch():
     empty = _lib.RansDeviceStream()
     empty.h = df11.rans_encode(np.zeros(0, np.uint16)).header
     assert lib.df11_rans_decompress(ctypes.byref(empty), None, None) == 0
+
+
+def test_linear_batch_validation_runs_before_any_launch():
+    lib = _lib_or_skip()
+    host = df11.encode(workloads.gen_single_matrix(rows=64, cols=1024))
+    s = _fake_device_stream(host)
+    x = ctypes.c_void_p(1 << 48)
+
+    def call(streams, out_f, outs, t=1, in_f=1024):
+        arr = (_lib.DeviceStream * max(len(streams), 1))(*streams)
+        of = np.array(out_f if out_f else [0], np.uint32)
+        ptrs = (ctypes.c_void_p * max(len(outs), 1))(*outs)
+        return lib.df11_linear_batch(arr, len(streams), x, t, in_f, of.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                     ptrs, None, None, None)
+
+    y0, y1 = (1 << 48) + (1 << 32), (1 << 48) + (2 << 32)
+    assert lib.df11_linear_batch(None, 0, x, 1, 1024, None, None, None, None, None) == 0  # empty batch
+    assert lib.df11_linear_batch(None, 1, x, 1, 1024, None, None, None, None, None) == -1
+    assert call([s] * (_lib.MAX_BATCH + 1), [64] * (_lib.MAX_BATCH + 1), [y0] * (_lib.MAX_BATCH + 1)) == -7
+    assert call([s, s], [64, 63], [y0, y1]) == -1               # rows that do not match a stream
+    assert call([s, s], [64, 64], [y0, y0 + 64]) == -1          # outputs overlap each other
+    assert call([s, s], [64, 64], [y0, s.enc]) == -1            # an output over another stream
+    other = _lib.DeviceStream.from_buffer_copy(s)
+    other.decode_table_bits = 11
+    assert call([s, other], [64, 64], [y0, y1]) == -1           # different table widths
+    assert call([s], [64], [y0], t=9) == -1                     # too many tokens
