@@ -253,22 +253,31 @@ def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, com
 
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
-    weights, DF11 blocks decoded in line before each block, and DF11 blocks
-    decoded on a side stream (capped grid) while the previous block computes."""
+    weights, DF11 blocks decoded in line before each block, DF11 blocks
+    decoded on a side stream (capped grid) while the previous block computes,
+    and, at 1..8 tokens, DF11 blocks (a stream per weight) whose projections
+    decode inside their products (runtime.fused_block_forward)."""
     import torch
     from entropy_decoding_df11_amd import df11, runtime, workloads
-    blocks, resident = [], []
+    blocks, resident, per_weight = [], [], []
     t0 = time.perf_counter()
     for b in range(args.blocks):
         flat, views = workloads.gen_block(seed=1000 + b)
         parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
         blocks.append(df11.compress_block(parts, device=dev))
+        per_weight.append(df11.compress_block(parts, device=dev, codebook="per_weight"))
         resident.append({nm: torch.from_numpy(a.astype(np.int16)).to(dev).view(torch.bfloat16) for nm, a in parts})
     t_prep = time.perf_counter() - t0
     overlap = runtime.BlockDecoder(blocks, device=dev, overlap=True, decode_workgroups=args.overlap_workgroups)
     inline = runtime.BlockDecoder(blocks, device=dev, overlap=False)
     rows = []
-    for tokens in (16, 256, 4096):
+
+    def fused_forward(x):
+        for blk in per_weight:
+            x = runtime.fused_block_forward(x, blk)
+        return x
+
+    for tokens in (1, 8, 16, 256, 4096):
         rng = np.random.default_rng(tokens)
         x = workloads.f32_to_bf16_bits(rng.standard_normal(tokens * 4096) * 0.5).reshape(tokens, 4096)
         x = torch.from_numpy(x.astype(np.int16)).to(dev).view(torch.bfloat16)
@@ -290,15 +299,36 @@ def integration(args, dev) -> int:
             e1.record()
             torch.cuda.synchronize()
             res[name] = round(e0.elapsed_time(e1) / 10, 4)
-        rows.append({"tokens": tokens, "ms_per_forward": res,
-                     "df11_overlap_vs_resident": round(res["df11_overlap"] / res["resident"], 3),
-                     "df11_inline_vs_resident": round(res["df11_inline"] / res["resident"], 3)})
+        row = {"tokens": tokens, "ms_per_forward": res,
+               "df11_overlap_vs_resident": round(res["df11_overlap"] / res["resident"], 3),
+               "df11_inline_vs_resident": round(res["df11_inline"] / res["resident"], 3)}
+        if tokens <= 8:
+            for _ in range(3):
+                y = fused_forward(x)
+            torch.cuda.synchronize()
+            # float32 sums in another order: close to, not equal to, the resident forward
+            dev_max = float((y.float() - ref.float()).abs().max())
+            if dev_max > 0.05 * float(ref.float().abs().max()):
+                print("integration: the fused forward is far from the resident-weight forward", file=sys.stderr)
+                return 1
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fused_forward(x)
+            e1.record()
+            torch.cuda.synchronize()
+            res["df11_fused"] = round(e0.elapsed_time(e1) / 10, 4)
+            row["df11_fused_vs_resident"] = round(res["df11_fused"] / res["resident"], 3)
+            row["df11_fused_max_abs_diff_over_max_abs"] = round(dev_max / float(ref.float().abs().max()), 5)
+        rows.append(row)
     comp = sum(b.tensor.compressed_bytes() for b in blocks)
     raw = sum(2 * b.n_elements for b in blocks)
     print(json.dumps({"integration": "synthetic model forward", "blocks": args.blocks,
                       "weights_per_block": int(blocks[0].n_elements),
                       "overlap_decode_workgroups": args.overlap_workgroups, "compressed_over_bf16": round(comp / raw, 4),
-                      "outputs": "bit-identical to the resident-weight forward", "host_prep_s": round(t_prep, 1),
+                      "outputs": "in line and overlapped: bit-identical to the resident-weight forward; fused: "
+                                 "float32 sums in another order",
+                      "host_prep_s": round(t_prep, 1),
                       "results": rows}), flush=True)
     return 0
 

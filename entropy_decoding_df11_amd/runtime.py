@@ -1,4 +1,5 @@
-"""Decompress transformer blocks just before use.
+"""Decompress transformer blocks just before use, or fuse the decode into
+each projection.
 
 GeekNews, "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan LLM
 menjadi 70% ukurannya", sections "Dekompresi yang disesuaikan untuk inferensi
@@ -114,6 +115,33 @@ def block_forward(x, w: Dict, eps: float = 1e-5):
     x = x + F.linear(a, w["o_proj"])
     h = rms(x)
     x = x + F.linear(F.silu(F.linear(h, w["gate_proj"])) * F.linear(h, w["up_proj"]), w["down_proj"])
+    return x
+
+
+def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
+    """block_forward with each projection's decode fused into its product
+    (df11_linear_batch for q, k, v and for gate, up; df11_linear for o and
+    down), for 1..8 tokens: blk holds one DF11 stream per weight, and no
+    weight is ever decompressed to HBM.  The products accumulate in float32
+    and are rounded to x's dtype, like the resident path's outputs, but in
+    another order, so the last bits can differ from block_forward's."""
+    import torch.nn.functional as F
+    from .df11 import linear_batch
+
+    w = {nm: t for (nm, _, _), t in zip(blk.views, blk.tensors)}
+
+    def rms(h):
+        import torch
+        return h * torch.rsqrt(h.float().pow(2).mean(-1, keepdim=True) + eps).to(h.dtype)
+
+    h = rms(x).contiguous()
+    q, k, v = (y.to(x.dtype) for y in linear_batch([w["q_proj"], w["k_proj"], w["v_proj"]], h))
+    rep = q.shape[-1] // k.shape[-1]
+    a = q + (k * v).repeat_interleave(rep, dim=-1)
+    x = x + w["o_proj"].linear(a.contiguous()).to(x.dtype)
+    h = rms(x).contiguous()
+    g, u = (y.to(x.dtype) for y in linear_batch([w["gate_proj"], w["up_proj"]], h))
+    x = x + w["down_proj"].linear((F.silu(g) * u).contiguous()).to(x.dtype)
     return x
 
 

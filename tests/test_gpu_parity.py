@@ -497,3 +497,25 @@ def test_linear_batch_full_size_qkv(torch_cuda):
     for w, (r, c), y in zip(ws, shapes, ys):
         ref = oracle.linear(oracle.encode(w), x, r)
         assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= _linear_bound(x, w, r, c))
+
+
+@pytest.mark.parametrize("n_tokens", [1, 4, 8])
+def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens):
+    """A block forward whose projections decode inside their products gives
+    what the forward on the original BF16 weights gives, up to the order of
+    the float32 sums (outputs rounded to bf16 either way): within 2% of the
+    output's largest magnitude after one block."""
+    torch = torch_cuda
+    from entropy_decoding_df11_amd import runtime
+    _note(f"fused block forward tokens={n_tokens}")
+    flat, views = workloads.gen_block(seed=7, shapes=SMALL_BLOCK)
+    parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
+    blk = df11.compress_block(parts, codebook="per_weight")
+    resident = {nm: torch.from_numpy(a.astype(np.int16)).to("cuda").view(torch.bfloat16) for nm, a in parts}
+    x = workloads.f32_to_bf16_bits(np.random.default_rng(n_tokens).standard_normal(n_tokens * 1024) * 0.5)
+    x = torch.from_numpy(x.astype(np.int16).reshape(n_tokens, 1024)).to("cuda").view(torch.bfloat16)
+    ref = runtime.block_forward(x, resident).float()
+    got = runtime.fused_block_forward(x, blk).float()
+    torch.cuda.synchronize()
+    assert got.shape == ref.shape
+    assert float((got - ref).abs().max()) <= 0.02 * float(ref.abs().max())
