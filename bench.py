@@ -190,7 +190,7 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
         bench = json.loads(f.read().strip().splitlines()[-1])
     names = list(bench["config"]["shapes"])
     rows = [r for r in _read_csv(os.path.join(prof_dir, "lin_trace", "run_kernel_trace.csv"))
-            if "df11_linear" in r["Kernel_Name"]]
+            if "df11_linear_kernel" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     skip = (1 + bench["warmup"]) * len(names)
     per = {nm: [] for nm in names}
