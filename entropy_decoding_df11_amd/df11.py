@@ -290,6 +290,11 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
         x = x.unsqueeze(0)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
         raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
+    for t in tensors:
+        dev = torch.device(t.device)
+        if x.device.type != dev.type or x.device.index != (dev.index if dev.index is not None
+                                                          else torch.cuda.current_device()):
+            raise ValueError("x and every weight must be on the same device")
     n_tokens = x.shape[0]
     if outs is None:
         outs = [torch.empty((n_tokens, t.shape[0]), dtype=torch.float32, device=x.device) for t in tensors]
