@@ -519,3 +519,24 @@ def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens):
     torch.cuda.synchronize()
     assert got.shape == ref.shape
     assert float((got - ref).abs().max()) <= 0.02 * float(ref.abs().max())
+
+
+def test_linear_lm_head_full_size(torch_cuda):
+    """The LM-head-sized matrix (128256 x 4096, 525M weights, one stream) at
+    two tokens: long enough for the dynamic schedule, and every one of the
+    256,512 outputs against the oracle."""
+    torch = torch_cuda
+    w = workloads.gen_lm_head()
+    out_f, in_f = workloads.LM_HEAD_SHAPE
+    _note("linear lm head full size")
+    t = df11.compress(w, shape=(out_f, in_f))
+    assert t.header.n_groups >= 2 * 12 * 768  # many rounds per workgroup: the dynamic schedule runs
+    x = _tokens(2, in_f, 13)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    y = t.linear(xd)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    del t, y
+    ref = oracle.linear(oracle.encode(w), x, out_f)
+    assert np.all(np.abs(got - ref) <= _linear_bound(x, w, out_f, in_f))
+    assert not np.array_equal(got[0], got[1])
