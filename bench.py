@@ -253,6 +253,65 @@ def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, com
         f.write("\n".join(lines))
 
 
+# The two rocprofv3 --pmc passes of the instruction-mix summary.  Each stays
+# within one pass's hardware limits (8 SQ counters, counting those that the
+# derived metrics VALUBusy, LDSBankConflict and VALUUtilization read, and one
+# GRBM counter).
+COUNTER_PASSES = {
+    "sq_a": "VALUBusy LDSBankConflict SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_LDS_IDX_ACTIVE "
+            "SQ_LDS_BANK_CONFLICT",
+    "sq_b": "VALUUtilization SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INSTS_VMEM_RD "
+            "SQ_INSTS_VMEM_WR",
+}
+
+
+def summarize_counters(prof_dir: str, kernel: str, title: str, bench_args: str, source: str, out_name: str) -> None:
+    """profiles/ summary of the COUNTER_PASSES runs of `bench.py bench_args`
+    (prof_dir/<kernel>_sq_a and _sq_b): every counter of the kernel's
+    dispatches (median over them; rocprofv3 has already reduced each over the
+    chip), rocprofv3's derived VALUBusy, LDSBankConflict and VALUUtilization,
+    and per-wave instruction counts."""
+    med = {}
+    for sub in COUNTER_PASSES:
+        per = {}
+        for r in _read_csv(os.path.join(prof_dir, f"{kernel}_{sub}", "run_counter_collection.csv")):
+            if kernel in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"summarize: no {kernel} dispatches in the {sub} counter run")
+        for name, by_dispatch in per.items():
+            med[name] = float(np.median(list(by_dispatch.values())))
+    waves = med["SQ_WAVES"]
+    with open(os.path.join(REPO, source), "rb") as f:
+        src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+    pre = "cd /tmp && export TMPDIR=/tmp && "
+    lines = [f"# {title}: rocprofv3 counters", "",
+             f"Kernel source `{source}`, sha256 prefix {src_hash}.  Commands (from the repository root on a "
+             "one-GPU MI355X box; R = repository root, D = R/gpurun_out/prof):", ""]
+    for sub, counters in COUNTER_PASSES.items():
+        lines.append(f"    {pre}rocprofv3 --pmc {counters} -d $D/{kernel}_{sub} -o run --output-format csv "
+                     f"-- python3 $R/bench.py {bench_args}")
+    lines += ["", "Each value is the median over the kernel's dispatches in the run.", "",
+              "| counter | value | per wave |", "|---|---|---|"]
+    for name in sorted(med):
+        per_wave = f"{med[name] / waves:.1f}" if name.startswith("SQ_INSTS") else ""
+        lines.append(f"| {name} | {med[name]:.6g} | {per_wave} |")
+    lines += ["",
+              f"- VALUBusy {med['VALUBusy']:.1f}%: the share of the kernel's time that the vector ALUs issue "
+              "(rocprofv3's derived metric, SQ_ACTIVE_INST_VALU over CUs and GRBM_GUI_ACTIVE).",
+              f"- VALUUtilization {med['VALUUtilization']:.1f}%: lanes active per VALU instruction.",
+              f"- LDSBankConflict {med['LDSBankConflict']:.1f}%: the share of the kernel's time the LDS stalls on "
+              f"bank conflicts; conflict cycles are {100 * med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.0f}% "
+              "of the cycles the LDS spends on indexed operations (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE).",
+              f"- Instructions per wave: {med['SQ_INSTS_VALU'] / waves:.0f} VALU, {med['SQ_INSTS_SALU'] / waves:.0f} "
+              f"SALU, {med['SQ_INSTS_LDS'] / waves:.0f} LDS, {med['SQ_INSTS_VMEM_RD'] / waves:.0f} vector-memory "
+              f"reads, {med['SQ_INSTS_VMEM_WR'] / waves:.0f} vector-memory writes.",
+              f"- Waves wait on something {100 * med['SQ_WAIT_ANY'] / med['SQ_WAVE_CYCLES']:.0f}% of their "
+              f"resident cycles, on LDS issue {100 * med['SQ_WAIT_INST_LDS'] / med['SQ_WAVE_CYCLES']:.1f}%.", ""]
+    with open(os.path.join(REPO, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines))
+
+
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
     weights, DF11 blocks decoded in line before each block, DF11 blocks
@@ -532,26 +591,38 @@ def main() -> int:
 
     if args.summarize_profiles:
         pre = "cd /tmp && export TMPDIR=/tmp && "   # R = repository root, D = R/gpurun_out/prof
-        summarize_profiles(args.summarize_profiles, {
-            "trace": pre + "rocprofv3 --kernel-trace --stats -d $D/trace -o run --output-format csv "
-                           "-- python3 $R/bench.py --steps 100 --warmup 100 --no-cpu-baseline > $D/bench.json",
-            "fetch": pre + "rocprofv3 --pmc FETCH_SIZE -d $D/fetch -o run --output-format csv "
-                           "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-            "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
-                           "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-        })
-        if os.path.isdir(os.path.join(args.summarize_profiles, "lin_trace")):
+        have = lambda sub: os.path.isdir(os.path.join(args.summarize_profiles, sub))
+        if have("trace"):
+            summarize_profiles(args.summarize_profiles, {
+                "trace": pre + "rocprofv3 --kernel-trace --stats -d $D/trace -o run --output-format csv "
+                               "-- python3 $R/bench.py --steps 100 --warmup 100 --no-cpu-baseline > $D/bench.json",
+                "fetch": pre + "rocprofv3 --pmc FETCH_SIZE -d $D/fetch -o run --output-format csv "
+                               "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+                "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
+                               "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+            })
+        if have("lin_trace"):
             summarize_linear_profile(args.summarize_profiles,
                                      pre + "rocprofv3 --kernel-trace --stats -d $D/lin_trace -o run --output-format csv "
                                            "-- python3 $R/bench.py --linear-tokens 1 --steps 50 --warmup 20 "
                                            "--no-cpu-baseline > $D/lin.json")
-        if os.path.isdir(os.path.join(args.summarize_profiles, "rans_trace")):
+        if have("rans_trace"):
             summarize_kernel_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
                                    "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
                                    pre + "rocprofv3 --kernel-trace --stats -d $D/rans_trace -o run --output-format csv "
                                          "-- python3 $R/bench.py --coder rans --steps 100 --warmup 100 "
                                          "--no-cpu-baseline > $D/rans_trace.json",
                                    "df11_rans_decode_kernel_llama3_8b_block_trace.md")
+        counter_runs = [("df11_decode_kernel", "df11_decode_kernel on llama3_8b_block",
+                         "--steps 3 --warmup 2 --no-cpu-baseline", "entropy_decoding_df11_amd/csrc/df11_decode.hip",
+                         "df11_decode_kernel_llama3_8b_block_counters.md"),
+                        ("df11_rans_decode_kernel", "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
+                         "--coder rans --steps 3 --warmup 2 --no-cpu-baseline",
+                         "entropy_decoding_df11_amd/csrc/df11_rans_decode.hip",
+                         "df11_rans_decode_kernel_llama3_8b_block_counters.md")]
+        for kernel, title, bench_args, source, out_name in counter_runs:
+            if all(have(f"{kernel}_{sub}") for sub in COUNTER_PASSES):
+                summarize_counters(args.summarize_profiles, kernel, title, bench_args, source, out_name)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
