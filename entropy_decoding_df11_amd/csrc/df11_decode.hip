@@ -1115,6 +1115,19 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
 
 void fill_args(const df11_device_stream *s, DecodeArgs &a);
 
+// Whether stream i of a batch uses work counters that an earlier stream of
+// the same launch also uses (the same tensor twice, say).  Its workgroups
+// would take tickets from the other stream's counters, so it runs the static
+// schedule instead.
+bool shares_schedule(const df11_device_stream *streams, uint32_t i) {
+    const uint32_t *sc = streams[i].schedule;
+    if (!sc) return false;
+    for (uint32_t j = 0; j < i; ++j)
+        if (overlaps(sc, 4 * DF11_SCHEDULE_WORDS, streams[j].schedule, streams[j].schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
+            return true;
+    return false;
+}
+
 // Checks s and out (no launch) and fills the kernel arguments of one stream.
 int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
     int rc = validate(s);
@@ -1199,6 +1212,7 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
                 return DF11_E_INVALID_ARG;
         }
         if (streams[i].h.n_elements == 0) continue;
+        if (shares_schedule(streams, i)) a.sched = nullptr;
         const uint32_t g = streams[i].groups_per_workgroup ? streams[i].groups_per_workgroup
                                                            : kDefaultGroupsPerWorkgroup;
         if (streams[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, streams[i].max_workgroups)
@@ -1395,6 +1409,7 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
                 return DF11_E_INVALID_ARG;
         }
         if (empty) continue;
+        if (shares_schedule(ws, i)) a.sched = nullptr;
         if (b.n && ws[i].decode_table_bits != bits) return DF11_E_INVALID_ARG;
         bits = ws[i].decode_table_bits;
         if (ws[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, ws[i].max_workgroups) : ws[i].max_workgroups;

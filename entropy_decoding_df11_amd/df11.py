@@ -211,12 +211,16 @@ class DF11Tensor:
         """Decode into out (a new bf16 tensor of the original shape by default),
         enqueued on stream (torch's current stream by default).  events, a pair
         of torch.cuda.Event(enable_timing=True), are recorded at the decode
-        kernel's own start and end."""
+        kernel's own start and end.  Launches of one DF11Tensor share its
+        work counters and must not overlap in time: decode one tensor on one
+        stream at a time."""
         import torch
         if out is None:
             out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
         if out.dtype != torch.bfloat16 or out.numel() != self.n_elements or not out.is_contiguous():
             raise ValueError("out must be a contiguous bfloat16 tensor with the stream's element count")
+        if not _on_device(out, self.device):
+            raise ValueError("out must be on the stream's device")
         self._launch(out, stream, events)
         return out
 
@@ -249,15 +253,15 @@ class DF11Tensor:
             x = x.unsqueeze(0)
         if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
             raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
-        dev = torch.device(self.device)
-        if x.device.type != dev.type or x.device.index != (dev.index if dev.index is not None
-                                                          else torch.cuda.current_device()):
+        if not _on_device(x, self.device):
             raise ValueError("x must be on the weight's device")
         n_tokens = x.shape[0]
         if out is None:
             out = torch.empty((n_tokens, out_f), dtype=torch.float32, device=self.device)
         if out.dtype != torch.float32 or out.shape != (n_tokens, out_f) or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 (n_tokens, out_features) tensor")
+        if not _on_device(out, self.device):
+            raise ValueError("out must be on the weight's device")
         lib = _lib.load()
         st = self._hip_stream(stream)
         args = (ctypes.byref(self._stream_struct), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, out_f,
@@ -290,17 +294,16 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
         x = x.unsqueeze(0)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
         raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
-    for t in tensors:
-        dev = torch.device(t.device)
-        if x.device.type != dev.type or x.device.index != (dev.index if dev.index is not None
-                                                          else torch.cuda.current_device()):
-            raise ValueError("x and every weight must be on the same device")
+    if not all(_on_device(x, t.device) for t in tensors):
+        raise ValueError("x and every weight must be on the same device")
     n_tokens = x.shape[0]
     if outs is None:
         outs = [torch.empty((n_tokens, t.shape[0]), dtype=torch.float32, device=x.device) for t in tensors]
     for t, y in zip(tensors, outs):
         if y.dtype != torch.float32 or y.shape != (n_tokens, t.shape[0]) or not y.is_contiguous():
             raise ValueError("each output must be a contiguous float32 (n_tokens, out_features) tensor")
+        if not _on_device(y, x.device):
+            raise ValueError("every output must be on the weights' device")
     lib = _lib.load()
     st = tensors[0]._hip_stream(stream)
     arr = (_lib.DeviceStream * len(tensors))(*[t._stream_struct for t in tensors])
@@ -311,6 +314,19 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
     _lib.check(lib.df11_linear_batch(arr, len(tensors), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f,
                                      _ptr(out_f, ctypes.c_uint32), ptrs, st, *ev), "df11_linear_batch")
     return outs
+
+
+def _on_device(t: "torch.Tensor", device) -> bool:  # noqa: F821
+    """Whether tensor t lives on device (an index-less CUDA device means the
+    current one)."""
+    import torch
+    dev = torch.device(device)
+    if t.device.type != dev.type:
+        return False
+    if dev.type != "cuda":
+        return True
+    here = lambda d: d.index if d.index is not None else torch.cuda.current_device()  # noqa: E731
+    return here(t.device) == here(dev)
 
 
 def _event_handle(ev, stream: ctypes.c_void_p) -> int:
@@ -367,6 +383,8 @@ class DF11Block:
             scratch = torch.empty(t.n_elements, dtype=torch.bfloat16, device=t.device)
         if scratch.dtype != torch.bfloat16 or not scratch.is_contiguous():
             raise ValueError("scratch must be a contiguous bfloat16 tensor")
+        if not _on_device(scratch, t.device):
+            raise ValueError("scratch must be on the stream's device")
         if events is not None:
             if scratch.numel() < t.n_elements:
                 raise _lib.Df11Error(-5, "df11_decompress_timed")
@@ -393,6 +411,8 @@ def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor
     for t, o in zip(tensors, outs):
         if o.dtype != torch.bfloat16 or o.numel() != t.n_elements or not o.is_contiguous():
             raise ValueError("each out must be a contiguous bfloat16 tensor with its stream's element count")
+        if not (_on_device(o, tensors[0].device) and _on_device(o, t.device)):
+            raise ValueError("every stream and output must be on one device")
     n = len(tensors)
     arr = (_lib.DeviceStream * max(n, 1))(*[t.device_stream() for t in tensors])
     ptrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
@@ -431,6 +451,8 @@ class DF11BlockBatch:
             scratch = torch.empty(self._n, dtype=torch.bfloat16, device=self.tensors[0].device)
         if scratch.dtype != torch.bfloat16 or not scratch.is_contiguous() or scratch.numel() < self._n:
             raise ValueError("scratch must be a contiguous bfloat16 tensor of at least n_elements")
+        if not _on_device(scratch, self.tensors[0].device):
+            raise ValueError("scratch must be on the streams' device")
         cached, views, outs = self._view_cache
         if cached is not scratch:
             flat = scratch.reshape(-1)
@@ -592,6 +614,8 @@ class DF11RansTensor:
             out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
         if out.dtype != torch.bfloat16 or out.numel() != self.n_elements or not out.is_contiguous():
             raise ValueError("out must be a contiguous bfloat16 tensor with the stream's element count")
+        if not _on_device(out, self.device):
+            raise ValueError("out must be on the stream's device")
         lib = _lib.load()
         st = DF11Tensor._hip_stream(self, stream)
         if events is None:

@@ -134,7 +134,10 @@ typedef struct df11_header {
  *                                        zero-filled by the caller once; every
  *                                        launch leaves them zero again.  Launches
  *                                        that share one must not overlap in time
- *                                        (use one per stream of work).  NULL
+ *                                        (use one per stream of work); within one
+ *                                        batched launch, a stream whose counters
+ *                                        an earlier stream of the batch also uses
+ *                                        runs the static schedule.  NULL
  *                                        selects a static schedule, which is
  *                                        also used for streams too short to
  *                                        gain from balancing.

@@ -384,6 +384,61 @@ def test_linear_argument_errors(torch_cuda):
         t.linear(torch.zeros((2, 1000), dtype=torch.bfloat16, device="cuda"))
 
 
+def test_same_stream_twice_in_one_batch(torch_cuda):
+    """A batch that holds one tensor twice: both entries would use the same
+    work counters, so the second runs the static schedule.  The grid is capped
+    so that the first entry takes the dynamic schedule; both outputs must be
+    exact (decode) or within the float32 bound (product), on two calls in a
+    row, and the counters must be zero afterwards."""
+    torch = torch_cuda
+    out_f, in_f = 1024, 4096
+    w = _case("normal", out_f * in_f, 17)
+    t = df11.compress(w, shape=(out_f, in_f))
+    t.set_max_workgroups(32)
+    _note("same stream twice in one batch")
+    x = _tokens(2, in_f, 9)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ref = oracle.linear(oracle.encode(w), x, out_f)
+    bound = _linear_bound(x, w, out_f, in_f)
+    for _ in range(2):
+        outs = [torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+                for _ in range(2)]
+        df11.decompress_batch([t, t], outs)
+        ys = df11.linear_batch([t, t], xd)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert np.array_equal(_to_u16(o), w)
+        for y in ys:
+            assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= bound)
+        assert not t._schedule.cpu().numpy().any()
+    t.set_max_workgroups(0)
+
+
+def test_outputs_on_another_device_are_rejected(torch_cuda):
+    """Every entry point refuses an output (or x, or scratch) that is not on
+    the weights' device before anything is launched."""
+    torch = torch_cuda
+    w = _case("normal", 64 * 1024, 1)
+    t = df11.compress(w, shape=(64, 1024))
+    x = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        t.decompress(out=torch.empty((64, 1024), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        t.linear(x, out=torch.empty((1, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        t.linear(x.cpu())
+    with pytest.raises(ValueError):
+        df11.linear_batch([t, t], x, outs=[torch.empty((1, 64), dtype=torch.float32, device="cuda"),
+                                           torch.empty((1, 64), dtype=torch.float32)])
+    with pytest.raises(ValueError):
+        df11.decompress_batch([t], [torch.empty(64 * 1024, dtype=torch.bfloat16)])
+    r = df11.rans_compress(w, shape=(64, 1024))
+    with pytest.raises(ValueError):
+        r.decompress(out=torch.empty((64, 1024), dtype=torch.bfloat16))
+    # Nothing was launched: a normal call still decodes exactly.
+    assert np.array_equal(t.decompress().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1), w)
+
+
 def _lib_error():
     from entropy_decoding_df11_amd import _lib
     return _lib.Df11Error

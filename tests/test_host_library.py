@@ -504,3 +504,13 @@ def test_linear_batch_validation_runs_before_any_launch():
     other.decode_table_bits = 11
     assert call([s, other], [64, 64], [y0, y1]) == -1           # different table widths
     assert call([s], [64], [y0], t=9) == -1                     # too many tokens
+
+
+def test_device_check_of_the_binding():
+    """The binding's device check: a host tensor is never on a CUDA device
+    (decided without a GPU), and tensors match a device of their own type."""
+    import torch
+    from entropy_decoding_df11_amd.df11 import _on_device
+    assert not _on_device(torch.zeros(1), "cuda")
+    assert not _on_device(torch.zeros(1), "cuda:0")
+    assert _on_device(torch.zeros(1), "cpu")
