@@ -346,21 +346,21 @@ __device__ __forceinline__ void flush_wave(const MatmulArgs &m, RowSums<TB> &rs,
 // the row bookkeeping is one division per run and one scalar test per round:
 // B is the first element of the row after the wave's current one, and a
 // round spans 512 <= in_features elements, so it crosses at most B.  Lanes at
-// or past B belong to the next row.  x is loaded a round ahead when the
-// tokens' registers allow, with unconditional in-bounds loads (inactive lanes
-// read column 0 and multiply zeros; token slots past n_tokens read token 0
-// and are never flushed), so that each wait for x is an exact count; and the
-// fused kernel runs the merge before issuing the next group's loads, so that
-// those waits do not include them.
+// or past B belong to the next row.  Each lane tracks the byte offset in x's
+// rows of its element's column (one add and one min per round: a lane's next
+// element is 512 further, at most one row on).  x is loaded a round ahead
+// when the tokens' registers allow, with unconditional loads that the
+// columns keep in bounds (lanes without weights multiply zeros; token slots
+// past n_tokens read token 0 and are never flushed), so that each wait for x
+// is an exact count; and the fused kernel runs the merge before issuing the
+// next group's loads, so that those waits do not include them.
 template <int TB>
-__device__ __forceinline__ void load_x(const MatmulArgs &m, uint32_t i0, bool active, uint32_t B,
-                                       uint4 (&xv)[TB]) {
-    // Column of i0 in its row: the row before B, or the one starting at B.
-    const uint32_t col = active ? i0 - (i0 >= B ? B : B - m.in_features) : 0u;
+__device__ __forceinline__ void load_x(const MatmulArgs &m, uint32_t colb, uint4 (&xv)[TB]) {
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(m.x);
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
         const uint32_t tt = t < static_cast<int>(m.n_tokens) ? static_cast<uint32_t>(t) : 0u;
-        xv[t] = *reinterpret_cast<const uint4 *>(m.x + static_cast<size_t>(tt) * m.in_features + col);
+        xv[t] = *reinterpret_cast<const uint4 *>(xb + static_cast<size_t>(tt) * m.in_features * 2u + colb);
     }
 }
 
@@ -394,10 +394,16 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
     rs.dirty = true;
     uint32_t B = (rs.row + 1u) * m.in_features;
     constexpr bool kAhead = TB <= 4;
+    constexpr uint32_t kRound = 8u * kWaveSize;  // elements per round
     uint4 xv[TB], xn[TB];
     uint8_t *cell = ebuf + 8u * (k0 + lane);
     uint32_t i0 = e0 + 8u * lane;
-    if (kAhead) load_x<TB>(m, i0, i0 + 8u > lo && i0 < hi_eff, B, xv);
+    // Byte offset of i0's column, from i0's own row: a lane before lo can
+    // lie two rows before B (lo is then the first element of the row before
+    // B), so B alone does not place every lane.
+    uint32_t colb = 2u * (i0 - static_cast<uint32_t>(__umul64hi(i0, m.row_magic)) * m.in_features);
+    const uint32_t wrapb = 2u * kRound - 2u * m.in_features;  // modulo 2^32
+    if (kAhead) load_x<TB>(m, colb, xv);
 
     auto step = [&](uint64_t s8) {
         const bool in_chunks = i0 < chunk_end;
@@ -406,31 +412,38 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
             r8 = *reinterpret_cast<uint64_t *>(cell);
             *reinterpret_cast<uint64_t *>(cell) = 0;
         }
-        // Does this round reach the next row?  (B only moves forward.)
-        const bool cross = B < min(e0 + 8u * kWaveSize, hi_eff);
-        const uint32_t B_next = cross ? B + m.in_features : B;
-        const uint32_t i1 = i0 + 8u * kWaveSize;
-        if (kAhead) load_x<TB>(m, i1, i1 < hi_eff, B_next, xn);
-        else load_x<TB>(m, i0, i0 + 8u > lo && i0 < hi_eff, B, xv);
+        // Does this round reach the next row?  (B only moves forward and
+        // stays past e0.)
+        const bool cross = B < hi_eff && B - e0 < kRound;
+        // The lane's next column: 512 on, less a row when that passes its end.
+        const uint32_t colb_nx = min(colb + 2u * kRound, colb + wrapb);
+        if (kAhead) load_x<TB>(m, colb_nx, xn);
+        else load_x<TB>(m, colb, xv);
         // Chunks past the group's last one merge as zero.
         const uint4 v = merge8(in_chunks ? s8 : 0ull, r8);
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        // At most two chunks of a group are cut by lo or hi.
-        if (i0 < lo || i0 + 8u > hi) {
+        // Only the rounds that hold the group's first or last output can be
+        // cut by lo or hi (e0 < run_end <= hi).
+        if (e0 < lo || hi - e0 < kRound) {
+            if (i0 < lo || i0 + 8u > hi) {
 #pragma unroll
-            for (uint32_t e = 0; e < 8; ++e)
-                if (i0 + e < lo || i0 + e >= hi) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                for (uint32_t e = 0; e < 8; ++e)
+                    if (i0 + e < lo || i0 + e >= hi) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            }
         }
-        float p[TB];
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-            p[t] = dot2_bf16(w[3], xv[t].w,
-                             dot2_bf16(w[2], xv[t].z, dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, 0.0f))));
         if (!cross) {
 #pragma unroll
-            for (int t = 0; t < TB; ++t) rs.acc[t] += p[t];
+            for (int t = 0; t < TB; ++t)
+                rs.acc[t] = dot2_bf16(w[3], xv[t].w,
+                                      dot2_bf16(w[2], xv[t].z,
+                                                dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, rs.acc[t]))));
         } else {
             // Finish the current row with the lanes before B, carry on with the rest.
+            float p[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                p[t] = dot2_bf16(w[3], xv[t].w,
+                                 dot2_bf16(w[2], xv[t].z, dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, 0.0f))));
             const bool in_b = i0 >= B;
 #pragma unroll
             for (int t = 0; t < TB; ++t) rs.acc[t] += in_b ? 0.0f : p[t];
@@ -439,15 +452,16 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
             for (int t = 0; t < TB; ++t) rs.acc[t] = in_b ? p[t] : 0.0f;
             rs.row += 1u;
             rs.dirty = true;
+            B += m.in_features;
         }
         if (kAhead) {
 #pragma unroll
             for (int t = 0; t < TB; ++t) xv[t] = xn[t];
         }
-        B = B_next;
-        e0 += 8u * kWaveSize;
-        i0 = i1;
-        cell += 8u * kWaveSize;
+        colb = colb_nx;
+        e0 += kRound;
+        i0 += kRound;
+        cell += kRound;
     };
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
