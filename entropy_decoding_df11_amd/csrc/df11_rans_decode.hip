@@ -45,12 +45,11 @@ namespace {
 constexpr uint32_t kRansLanes = DF11_RANS_LANES;
 static_assert(kRansLanes == kWaveSize, "a segment's lanes are a wave's lanes");
 constexpr uint32_t kRansSegment = DF11_RANS_LANES * DF11_RANS_STEPS;
-// Steps per sub-block.  8 leaves 4.5 KB of LDS per wave (three workgroups,
-// 24 segments per CU); 4 would fit four workgroups but measured 18% slower
-// (the per-pass loads, waits and merge come twice as often).
+// Steps per sub-block.  8 leaves 4.5 KB of LDS per wave (plus the 16 KB
+// table per workgroup); 4 would fit more segments per CU but measured 18%
+// slower (the per-pass loads, waits and merge come twice as often).
 constexpr uint32_t kRansSub = 8;
 constexpr uint32_t kRansSubElems = kRansSub * kRansLanes;    // exponents (and most words) per sub-block
-constexpr uint32_t kRansWaves = 8;                           // segments in flight per workgroup
 constexpr uint32_t kRansChunk = kRansSubElems;               // words per ring chunk (8 per lane)
 constexpr uint32_t kRansRing = 4 * kRansChunk;               // staged words per wave
 static_assert(kRansChunk >= kRansSubElems, "a sub-block spans at most two chunks");
@@ -122,7 +121,11 @@ __device__ __forceinline__ void rans_steps(const uint32_t *s_tab, const uint16_t
     }
 }
 
-__global__ __launch_bounds__(kWaveSize *kRansWaves) void df11_rans_decode_kernel(RansArgs a) {
+// W waves (segments in flight) per workgroup; the host picks W per stream
+// (rans_waves).
+template <uint32_t W>
+__global__ __launch_bounds__(kWaveSize *W) void df11_rans_decode_kernel(RansArgs a) {
+    constexpr uint32_t kRansWaves = W;
     __shared__ __align__(16) uint32_t s_tab[DF11_RANS_TABLE_ENTRIES];
     __shared__ __align__(16) uint8_t s_stage[kRansWaves][kRansSubElems];
     __shared__ __align__(16) uint16_t s_ring[kRansWaves][kRansRing];
@@ -130,15 +133,17 @@ __global__ __launch_bounds__(kWaveSize *kRansWaves) void df11_rans_decode_kernel
     const uint32_t lane = tid & (kWaveSize - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
     {
+        // Every load first, then every store; indices clamped (extra lanes
+        // copy the last vector again).
         constexpr uint32_t kThreads = kWaveSize * kRansWaves;
-        constexpr uint32_t kPer = DF11_RANS_TABLE_ENTRIES / 4 / kThreads;
-        static_assert(kPer * 4 * kThreads == DF11_RANS_TABLE_ENTRIES, "the table splits evenly");
+        constexpr uint32_t kVecs = DF11_RANS_TABLE_ENTRIES / 4;
+        constexpr uint32_t kPer = (kVecs + kThreads - 1) / kThreads;
         const uint4 *src = reinterpret_cast<const uint4 *>(a.table);
         uint4 v[kPer];
 #pragma unroll
-        for (uint32_t j = 0; j < kPer; ++j) v[j] = src[tid + j * kThreads];
+        for (uint32_t j = 0; j < kPer; ++j) v[j] = src[min(tid + j * kThreads, kVecs - 1u)];
 #pragma unroll
-        for (uint32_t j = 0; j < kPer; ++j) reinterpret_cast<uint4 *>(s_tab)[tid + j * kThreads] = v[j];
+        for (uint32_t j = 0; j < kPer; ++j) reinterpret_cast<uint4 *>(s_tab)[min(tid + j * kThreads, kVecs - 1u)] = v[j];
     }
     __syncthreads();
     const uint32_t stride = gridDim.x * kRansWaves;
@@ -170,6 +175,52 @@ __global__ __launch_bounds__(kWaveSize *kRansWaves) void df11_rans_decode_kernel
             rans_merge(a, stage, smv, seg0 + q0, min(kRansSubElems, count - q0), lane);
         }
     }
+}
+
+// Launch shape.  A CU decodes its resident segments at a throughput of
+// about one per 6.5 us (block workload), but no round of segments takes less
+// than the ~50 us that one segment's chain of steps needs alone: a round with
+// fewer than ~8 segments per CU costs as much as one with 8.  The cost of
+// W-wave workgroups, in units of one segment's CU time, is therefore the sum
+// over rounds of max(8, segments on the busiest CU).  LDS bounds the
+// workgroups per CU: three of 8 waves, two of 10 to 14 (24 to 28 segments
+// per CU); the cheapest shape wins, the one with more waves on a tie.
+struct RansShape {
+    const void *fn;
+    uint32_t waves;
+    uint32_t grid;
+};
+
+template <uint32_t W>
+void consider_shape(uint64_t n_seg, int dev, int cus, RansShape &best, uint64_t &best_cost) {
+    const void *fn = reinterpret_cast<const void *>(&df11_rans_decode_kernel<W>);
+    const int per_cu = resident_per_cu(fn, kWaveSize * W, dev, 0);
+    if (per_cu < 1) return;
+    const uint64_t grid = std::min<uint64_t>((n_seg + W - 1) / W, static_cast<uint64_t>(per_cu) * cus);
+    const uint64_t slots = grid * W;
+    uint64_t cost = 0;
+    for (uint64_t done = 0; done < n_seg; done += slots) {
+        const uint64_t in_round = std::min(slots, n_seg - done);
+        const uint64_t wgs = (in_round + W - 1) / W;
+        const uint64_t busiest = std::min<uint64_t>((wgs + cus - 1) / cus * W, in_round);
+        cost += std::max<uint64_t>(8, busiest);
+    }
+    if (!best.fn || cost <= best_cost) {
+        best = RansShape{fn, W, static_cast<uint32_t>(grid)};
+        best_cost = cost;
+    }
+}
+
+RansShape rans_shape(uint64_t n_seg, int dev, int cus) {
+    RansShape best{nullptr, 0, 0};
+    uint64_t cost = 0;
+    consider_shape<8>(n_seg, dev, cus, best, cost);
+    consider_shape<10>(n_seg, dev, cus, best, cost);
+    consider_shape<11>(n_seg, dev, cus, best, cost);
+    consider_shape<12>(n_seg, dev, cus, best, cost);
+    consider_shape<13>(n_seg, dev, cus, best, cost);
+    consider_shape<14>(n_seg, dev, cus, best, cost);
+    return best;
 }
 
 int rans_impl(const df11_rans_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
@@ -206,15 +257,12 @@ int rans_impl(const df11_rans_device_stream *s, uint16_t *out, hipStream_t strea
     a.sm_chunks = static_cast<uint32_t>(sm_bytes / 8);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
-    const void *fn = reinterpret_cast<const void *>(&df11_rans_decode_kernel);
-    const int per_cu = resident_per_cu(fn, kWaveSize * kRansWaves, dev, 0);
-    if (per_cu < 1) return DF11_E_HIP;
-    const uint64_t grid = std::min<uint64_t>((h.n_segments + kRansWaves - 1) / kRansWaves,
-                                             static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus));
+    const RansShape shape = rans_shape(h.n_segments, dev, cus);
+    if (!shape.fn) return DF11_E_HIP;
     (void)hipGetLastError();
     void *params[] = {&a};
-    if (hipExtLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(kWaveSize * kRansWaves), params, 0, stream,
-                           start, stop, 0) != hipSuccess)
+    if (hipExtLaunchKernel(shape.fn, dim3(shape.grid), dim3(kWaveSize * shape.waves), params, 0, stream, start, stop,
+                           0) != hipSuccess)
         return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }

@@ -509,6 +509,31 @@ def test_rans_full_size_block_repeat_and_timed(torch_cuda):
     assert ev[0].elapsed_time(ev[1]) > 0
 
 
+# Segment counts at which the launch picks each workgroup shape on a 256-CU
+# MI355X (14, 8, 10, 11, 12 and 13 waves); on another GPU they still check
+# whatever shapes it picks.
+RANS_SHAPE_SEGMENTS = [1, 9, 2049, 2561, 2817, 3073]
+
+
+def test_rans_every_launch_shape(torch_cuda):
+    """Streams sized to select every workgroup shape of the rANS decoder,
+    each with a ragged last segment: bit-exact."""
+    torch = torch_cuda
+    seg = 64 * 512
+    base = _case("normal", 1 << 22, 23)
+    for n_seg in RANS_SHAPE_SEGMENTS:
+        n = (n_seg - 1) * seg + 1000
+        w = np.resize(base, n)
+        _note(f"rans shape, {n_seg} segments")
+        t = df11.rans_compress(w, shape=(n,))
+        assert t.header.n_segments == n_seg
+        out = torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        t.decompress(out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(_to_u16(out), w)
+        del t, out
+
+
 @pytest.mark.parametrize("n_tokens", [1, 3, 8])
 def test_linear_batch_matches_oracle(torch_cuda, n_tokens):
     """q, k and v shaped matrices (different row counts, each its own
