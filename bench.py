@@ -35,6 +35,7 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 HBM_PEAK_GBPS = 8000.0
+COLD_LAUNCHES = 20  # cold-cache launches after the timed ones
 DEFAULT_WORKLOAD = "llama3_8b_block"
 WORKLOAD_CHOICES = ["llama3_8b_block", "llama3_8b_block_per_weight", "lm_head_128256x4096", "stress_2p28_zipf",
                     "mlp_14336x4096_t5", "proj_4096x4096_outliers", "single_1024x1024"]
@@ -118,7 +119,7 @@ def summarize_profiles(prof_dir: str, commands: dict) -> None:
     trace = [r for r in _read_csv(os.path.join(prof_dir, "trace", "run_kernel_trace.csv"))
              if "df11_decode" in r["Kernel_Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    timed = trace[-bench["steps"]:]
+    timed = trace[-(bench["steps"] + COLD_LAUNCHES):-COLD_LAUNCHES]
     timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
     algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
     copy_bytes = algo // 2
@@ -150,7 +151,8 @@ def summarize_profiles(prof_dir: str, commands: dict) -> None:
     avg_all = float(dec_row[0]["AverageNs"]) / 1e3
     avg_us = float(np.mean(timed_us))
     lines += ["", f"The table averages every decode launch of the run, warmup included ({avg_all:.2f} us).  "
-              f"Over the {len(timed_us)} timed launches (the last ones in the trace) the decode kernel averages "
+              f"Over the {len(timed_us)} timed launches (those before the last {COLD_LAUNCHES}, which run after a "
+              f"cache flush) the decode kernel averages "
               f"{avg_us:.2f} us (min {min(timed_us):.2f}, max {max(timed_us):.2f}) for {algo} algorithmic bytes: "
               f"{algo / (avg_us * 1e-6) / 1e9:.1f} GB/s, {algo / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s.  "
               f"The same run's bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with the events "
@@ -228,14 +230,16 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
 def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, command: str, out_name: str) -> None:
     """profiles/ summary of a rocprofv3 --kernel-trace --stats run of this
     script (prof_dir/sub, its bench line in prof_dir/sub.json): the stats
-    table and the kernel's average over the run's timed launches (the last
-    `steps` launches of `kernel`) against the bench line's event timing."""
+    table and the kernel's average over the run's timed launches (the
+    `steps` launches of `kernel` before the cold-cache ones) against the
+    bench line's event timing."""
     with open(os.path.join(prof_dir, sub + ".json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     stats = _read_csv(os.path.join(prof_dir, sub, "run_kernel_stats.csv"))
     rows = [r for r in _read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv")) if kernel in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-bench["steps"]:]]
+    timed = rows[-(bench["steps"] + COLD_LAUNCHES):-COLD_LAUNCHES]
+    timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
     algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
     avg = float(np.mean(timed_us))
     lines = [f"# {title}: rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box):",
@@ -244,7 +248,8 @@ def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, com
     for r in stats[:6]:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
-    lines += ["", f"Over the {len(timed_us)} timed launches (the last ones in the trace) the kernel averages "
+    lines += ["", f"Over the {len(timed_us)} timed launches (those before the last {COLD_LAUNCHES}, which run "
+              f"after a cache flush) the kernel averages "
               f"{avg:.2f} us (min {min(timed_us):.2f}, max {max(timed_us):.2f}) for {algo} algorithmic bytes: "
               f"{algo / (avg * 1e-6) / 1e9:.1f} GB/s, {algo / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s.  "
               f"The bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with the events that "
@@ -735,13 +740,14 @@ def main() -> int:
     achieved = algo_bytes / (mean_ms * 1e-3) / 1e9
     value = args.steps * algo_bytes / wall / 1e9
 
-    # Cold caches: 20 more launches, each after reading 1 GiB so that neither
+    # Cold caches: COLD_LAUNCHES more launches, each after reading 1 GiB so that neither
     # the L2 nor the 256 MB MALL holds the stream (outside the timed launch;
     # the hot numbers above come from back-to-back launches).  The flush reads
     # rather than writes: written lines would be dirty, and the timed launch
     # would pay for writing them back.
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(COLD_LAUNCHES)]
     sink = torch.empty((), dtype=torch.float32, device=dev)
     for ev in cold_ev:
         torch.sum(flush, dim=0, out=sink)
