@@ -686,15 +686,7 @@ def main() -> int:
         else:
             h, comp = blk.tensors[0].header, blk.compressed_bytes()
             config["streams"] = len(blk.tensors)
-            config["timing"] = "events recorded around the batched launch"
-
-            def decode(ev=None):
-                # the batched launch has no dispatch-recorded events: record them around it
-                if ev is not None:
-                    ev[0].record(stream)
-                blk.decompress(scratch=scratch)
-                if ev is not None:
-                    ev[1].record(stream)
+            decode = lambda ev=None: blk.decompress(scratch=scratch, events=ev)  # noqa: E731
 
         def decoded():
             if codebook == "shared":

@@ -45,6 +45,7 @@ EXPORTED = [
     "df11_decompress_block",
     "df11_decompress_batch",
     "df11_decompress_timed",
+    "df11_decompress_batch_timed",
     "df11_linear",
     "df11_linear_timed",
     "df11_linear_batch",
@@ -176,6 +177,9 @@ def load() -> ctypes.CDLL:
                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
         "df11_decompress_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_decompress_batch_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32,
+                                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                       ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,

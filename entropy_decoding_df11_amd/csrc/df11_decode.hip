@@ -1089,7 +1089,7 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, uint32_t max_wg, hipStream_t str
 // their super-groups (at least one workgroup each, at most one per
 // super-group) and launch once.
 template <int K, int GPW>
-int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
+int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     size_t lds = 0;
     uint64_t total_super = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
@@ -1121,7 +1121,7 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream) {
         }
     (void)hipGetLastError();
     void *params[] = {&b};
-    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, nullptr, nullptr, 0) !=
+    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) !=
         hipSuccess)
         return DF11_E_HIP;
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
@@ -1201,7 +1201,7 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
 }
 
 int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_t *const *outs,
-                          hipStream_t stream) {
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     if (n > kMaxBatch) return DF11_E_TOO_LARGE;
     if (n && (!streams || !outs)) return DF11_E_INVALID_ARG;
     BatchArgs b{};
@@ -1240,12 +1240,12 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
         b.s[b.n++] = a;
     }
     if (b.n == 0) return DF11_OK;
-#define DF11_BATCH_CASE(KB)                                        \
-    case KB:                                                       \
-        switch (gpw) {                                             \
-        case 1: return launch_batch<KB, 1>(b, max_wg, stream);     \
-        case 4: return launch_batch<KB, 4>(b, max_wg, stream);     \
-        default: return launch_batch<KB, 2>(b, max_wg, stream);    \
+#define DF11_BATCH_CASE(KB)                                                  \
+    case KB:                                                                 \
+        switch (gpw) {                                                       \
+        case 1: return launch_batch<KB, 1>(b, max_wg, stream, start, stop);  \
+        case 4: return launch_batch<KB, 4>(b, max_wg, stream, start, stop);  \
+        default: return launch_batch<KB, 2>(b, max_wg, stream, start, stop); \
         }
     switch (bits) {
         DF11_BATCH_CASE(10)
@@ -1471,7 +1471,13 @@ int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64
 
 int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
                           void *hip_stream) {
-    return decompress_batch_impl(streams, n_streams, outs, static_cast<hipStream_t>(hip_stream));
+    return decompress_batch_impl(streams, n_streams, outs, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
+}
+
+int df11_decompress_batch_timed(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
+                                void *hip_stream, void *start_event, void *stop_event) {
+    return decompress_batch_impl(streams, n_streams, outs, static_cast<hipStream_t>(hip_stream),
+                                 static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
 int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,

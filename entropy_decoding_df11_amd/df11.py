@@ -401,10 +401,13 @@ class DF11Block:
         return views
 
 
-def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor"], stream=None) -> None:  # noqa: F821
+def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor"], stream=None,  # noqa: F821
+                     events=None) -> None:
     """Decode several streams, each with its own codebook, in one launch:
     outs[i] (a contiguous bf16 tensor of tensors[i].n_elements elements)
-    receives tensors[i].  All streams must use the same decode-table width."""
+    receives tensors[i].  All streams must use the same decode-table width.
+    events: as for DF11Tensor.decompress, recorded at the batched kernel's
+    own start and end (df11_decompress_batch_timed)."""
     import torch
     if len(tensors) != len(outs):
         raise ValueError("one output per stream")
@@ -418,7 +421,12 @@ def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor
     ptrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
     st = tensors[0]._hip_stream(stream) if n else ctypes.c_void_p(0)
     lib = _lib.load()
-    _lib.check(lib.df11_decompress_batch(arr, n, ptrs, st), "df11_decompress_batch")
+    if events is None:
+        _lib.check(lib.df11_decompress_batch(arr, n, ptrs, st), "df11_decompress_batch")
+        return
+    _lib.check(lib.df11_decompress_batch_timed(arr, n, ptrs, st, ctypes.c_void_p(_event_handle(events[0], st)),
+                                               ctypes.c_void_p(_event_handle(events[1], st))),
+               "df11_decompress_batch_timed")
 
 
 class DF11BlockBatch:
@@ -445,7 +453,11 @@ class DF11BlockBatch:
         for t in self.tensors:
             t.set_max_workgroups(n)
 
-    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+    def decompress(self, scratch: Optional["torch.Tensor"] = None, stream=None,
+                   events=None) -> Dict[str, "torch.Tensor"]:  # noqa: F821
+        """Decode every weight into scratch (at least n_elements bf16; a new
+        one by default) in one launch and return a view per weight.  events:
+        as for decompress_batch."""
         import torch
         if scratch is None:
             scratch = torch.empty(self._n, dtype=torch.bfloat16, device=self.tensors[0].device)
@@ -459,7 +471,7 @@ class DF11BlockBatch:
             outs = [flat[off:off + int(np.prod(shape))] for _, off, shape in self.views]
             views = {name: o.view(shape) for (name, _, shape), o in zip(self.views, outs)}
             self._view_cache = (scratch, views, outs)
-        decompress_batch(self.tensors, outs, stream=stream)
+        decompress_batch(self.tensors, outs, stream=stream, events=events)
         return views
 
 

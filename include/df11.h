@@ -260,6 +260,14 @@ int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams,
 int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_stream, void *start_event,
                           void *stop_event);
 
+/* df11_decompress_batch with the batched kernel timed like
+ * df11_decompress_timed: start_event and stop_event (either may be NULL) are
+ * recorded when the kernel itself starts and ends.  Same arguments, output
+ * and errors as df11_decompress_batch; when every stream is empty nothing is
+ * launched and the events are not recorded. */
+int df11_decompress_batch_timed(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
+                                void *hip_stream, void *start_event, void *stop_event);
+
 /* y = x W^T with the decompression fused into the matrix product: W is the
  * stream decoded and viewed as an out_features x in_features row-major BF16
  * matrix, and its BF16 values never reach HBM.  The page's section

@@ -249,6 +249,15 @@ def test_block_with_per_weight_codebooks(torch_cuda):
             assert np.array_equal(_to_u16(out[name]), flat[off:off + r * c]), (name, dynamic)
         for t in blk.tensors:
             assert not t._schedule.cpu().numpy().any()
+    # The timed batch entry point decodes the same bytes and records the
+    # batched kernel's own start and end.
+    scratch.view(torch.int16).fill_(0x5A5A)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    out = blk.decompress(scratch=scratch, events=ev)
+    torch.cuda.synchronize()
+    for name, off, (r, c) in views:
+        assert np.array_equal(_to_u16(out[name]), flat[off:off + r * c]), name
+    assert ev[0].elapsed_time(ev[1]) > 0
 
 
 def test_lm_head_single_stream_full_size(torch_cuda):

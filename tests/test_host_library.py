@@ -312,6 +312,12 @@ def test_decompress_batch_validation_runs_before_any_launch():
     assert call([s, s], [1 << 48, s.enc]) == -1
     # misaligned output
     assert call([s], [(1 << 48) + 8]) == -1
+    # the timed entry point validates the same way
+    assert lib.df11_decompress_batch_timed(None, 0, None, None, None, None) == 0
+    assert lib.df11_decompress_batch_timed(None, 1, None, None, None, None) == -1
+    arr = (_lib.DeviceStream * 2)(s, bad)
+    ptrs = (ctypes.c_void_p * 2)(1 << 48, (1 << 48) + (1 << 32))
+    assert lib.df11_decompress_batch_timed(arr, 2, ptrs, None, None, None) == -6
 
 
 def test_linear_constants_match_header():
