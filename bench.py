@@ -322,7 +322,9 @@ def integration(args, dev) -> int:
     weights, DF11 blocks decoded in line before each block, DF11 blocks
     decoded on a side stream (capped grid) while the previous block computes,
     and, at 1..8 tokens, DF11 blocks (a stream per weight) whose projections
-    decode inside their products (runtime.fused_block_forward)."""
+    decode inside their products (runtime.fused_block_forward); at up to 16
+    tokens also the resident, in-line and fused forwards captured into HIP
+    graphs and replayed."""
     import torch
     from entropy_decoding_df11_amd import df11, runtime, workloads
     blocks, resident, per_weight = [], [], []
@@ -386,6 +388,35 @@ def integration(args, dev) -> int:
             res["df11_fused"] = round(e0.elapsed_time(e1) / 10, 4)
             row["df11_fused_vs_resident"] = round(res["df11_fused"] / res["resident"], 3)
             row["df11_fused_max_abs_diff_over_max_abs"] = round(dev_max / float(ref.float().abs().max()), 5)
+        if tokens <= 16:
+            # The same forwards captured into HIP graphs (runtime.CapturedForward):
+            # at a few tokens a forward is many small launches.
+            graphs = {"resident_graph": lambda x: runtime.model_forward(x, resident),
+                      "df11_inline_graph": lambda x: runtime.model_forward(x, inline)}
+            if tokens <= 8:
+                graphs["df11_fused_graph"] = fused_forward
+            for name, fwd in graphs.items():
+                g = runtime.CapturedForward(fwd, x)
+                y = g(x)
+                torch.cuda.synchronize()
+                if name == "df11_fused_graph":
+                    ok = float((y.float() - ref.float()).abs().max()) <= 0.05 * float(ref.float().abs().max())
+                else:
+                    ok = torch.equal(y.view(torch.int16), ref.view(torch.int16))
+                if not ok:
+                    print(f"integration: the {name} replay differs from the resident-weight forward", file=sys.stderr)
+                    return 1
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    g(x)
+                e1.record()
+                torch.cuda.synchronize()
+                res[name] = round(e0.elapsed_time(e1) / 10, 4)
+                del g
+            row["df11_inline_graph_vs_resident_graph"] = round(res["df11_inline_graph"] / res["resident_graph"], 3)
+            if tokens <= 8:
+                row["df11_fused_graph_vs_resident_graph"] = round(res["df11_fused_graph"] / res["resident_graph"], 3)
         rows.append(row)
     comp = sum(b.tensor.compressed_bytes() for b in blocks)
     raw = sum(2 * b.n_elements for b in blocks)

@@ -1067,12 +1067,9 @@ int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t 
     // latency; it wins only when each workgroup has many rounds to balance.
     const uint32_t grid = schedule_pools(args, n_super, resident);
     void *params[] = {&args};
-    // hipExtLaunchKernel records start / stop (when given) at the kernel's own
-    // start and end, not around the launch.
-    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) !=
-        hipSuccess)
-        return DF11_E_HIP;
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    // start / stop (when given) are recorded at the kernel's own start and
+    // end, not around the launch.
+    return launch_kernel(fn, dim3(grid), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop);
 }
 
 template <int K>
@@ -1121,10 +1118,7 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t s
         }
     (void)hipGetLastError();
     void *params[] = {&b};
-    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop, 0) !=
-        hipSuccess)
-        return DF11_E_HIP;
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return launch_kernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop);
 }
 
 void fill_args(const df11_device_stream *s, DecodeArgs &a);
@@ -1277,14 +1271,11 @@ int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hip
     float *y = m.y;
     void *zparams[] = {&y, const_cast<uint32_t *>(&n_y)};
     const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((n_y + 255) / 256, 1024));
-    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256), zparams, 0,
-                           stream, nullptr, nullptr, 0) != hipSuccess)
-        return DF11_E_HIP;
+    const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256), zparams,
+                                 0, stream, nullptr, nullptr);
+    if (rc) return rc;
     void *params[] = {&args, &margs};
-    if (hipExtLaunchKernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop,
-                           0) != hipSuccess)
-        return DF11_E_HIP;
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return launch_kernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop);
 }
 
 // Checks one product's arguments (no launch) and fills its kernel arguments;
@@ -1383,14 +1374,11 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
     const uint32_t total = z.end[z.n - 1];
     void *zparams[] = {&z};
     const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((total + 255) / 256, 1024));
-    if (hipExtLaunchKernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256), zparams, 0,
-                           stream, nullptr, nullptr, 0) != hipSuccess)
-        return DF11_E_HIP;
+    const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256),
+                                 zparams, 0, stream, nullptr, nullptr);
+    if (rc) return rc;
     void *params[] = {&b};
-    if (hipExtLaunchKernel(fn, dim3(next), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop, 0) !=
-        hipSuccess)
-        return DF11_E_HIP;
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return launch_kernel(fn, dim3(next), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop);
 }
 
 int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *x, uint32_t n_tokens,

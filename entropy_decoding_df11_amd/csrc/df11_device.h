@@ -3,6 +3,7 @@
 // df11_rans_decode.hip).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -93,6 +94,18 @@ int resident_per_cu(const void *fn, uint32_t threads, int dev, size_t lds) {
     std::lock_guard<std::mutex> lock(mu);
     if (per_cu > 0 && cache.size() < 256) cache.push_back({fn, dev, lds, per_cu});
     return per_cu;
+}
+
+// Launch fn.  With both events null this is a plain hipLaunchKernel, which a
+// caller may capture into a HIP graph; with either event given,
+// hipExtLaunchKernel records it at the kernel's own start or end.
+int launch_kernel(const void *fn, dim3 grid, dim3 block, void **params, size_t lds, hipStream_t stream,
+                  hipEvent_t start, hipEvent_t stop) {
+    const hipError_t e = (start || stop)
+                             ? hipExtLaunchKernel(fn, grid, block, params, lds, stream, start, stop, 0)
+                             : hipLaunchKernel(fn, grid, block, params, lds, stream);
+    if (e != hipSuccess) return DF11_E_HIP;
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
 
 int device_cus(int &dev, int &cus) {

@@ -261,10 +261,7 @@ int rans_impl(const df11_rans_device_stream *s, uint16_t *out, hipStream_t strea
     if (!shape.fn) return DF11_E_HIP;
     (void)hipGetLastError();
     void *params[] = {&a};
-    if (hipExtLaunchKernel(shape.fn, dim3(shape.grid), dim3(kWaveSize * shape.waves), params, 0, stream, start, stop,
-                           0) != hipSuccess)
-        return DF11_E_HIP;
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return launch_kernel(shape.fn, dim3(shape.grid), dim3(kWaveSize * shape.waves), params, 0, stream, start, stop);
 }
 
 }  // namespace

@@ -145,6 +145,51 @@ def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
     return x
 
 
+def fused_model_forward(x, blocks: Sequence[DF11BlockBatch]):
+    """fused_block_forward over every block in order (1..8 tokens)."""
+    for blk in blocks:
+        x = fused_block_forward(x, blk)
+    return x
+
+
+class CapturedForward:
+    """A forward captured once into a HIP graph and replayed.
+
+    At a few tokens a forward is many small launches (per block: the
+    products, or decodes and products, plus norms, activations and residual
+    adds); a graph replay issues all of them at once.  forward(x) must run on
+    the current stream and keep its shapes: this wrapper runs it `warmup`
+    times on a side stream (so that launch-time queries, torch's allocations
+    and the decode tables' caches are settled), then captures one call into a
+    graph that reads a static copy of x and writes a static output.
+    __call__(x) copies x in, replays, and returns that output, which the next
+    call overwrites.  Every DF11 kernel launches without memsets or host
+    synchronisation and leaves its work counters zero, so replays are
+    independent.  The forward's own buffers (weights, BlockDecoder scratch)
+    must stay alive as long as this object."""
+
+    def __init__(self, forward, example_x, warmup: int = 2):
+        import torch
+        self._forward = forward
+        self.x = example_x.clone()
+        side = torch.cuda.Stream(self.x.device)
+        side.wait_stream(torch.cuda.current_stream(self.x.device))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                forward(self.x)
+        torch.cuda.current_stream(self.x.device).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.y = forward(self.x)
+
+    def __call__(self, x):
+        if x.shape != self.x.shape or x.dtype != self.x.dtype:
+            raise ValueError("a captured forward takes inputs of the captured shape and dtype")
+        self.x.copy_(x)
+        self.graph.replay()
+        return self.y
+
+
 def model_forward(x, blocks: Union[BlockDecoder, List[Dict]]):
     """Run block_forward over every block in order, taking the weights from a
     BlockDecoder (compressed) or from a list of dicts (resident BF16)."""

@@ -610,6 +610,52 @@ def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens):
     assert float((got - ref).abs().max()) <= 0.02 * float(ref.abs().max())
 
 
+@pytest.mark.parametrize("path", ["resident", "inline", "fused"])
+def test_captured_forward_replays_match_eager(torch_cuda, path):
+    """A 3-block forward captured into a HIP graph (runtime.CapturedForward)
+    and replayed on five inputs, with eager forwards and synchronisations
+    between the replays: every replay gives the eager resident-weight
+    forward's output, bit for bit on the resident and in-line decode paths,
+    and within 5% of the output's largest magnitude on the fused path (its
+    float32 sums run in another order)."""
+    torch = torch_cuda
+    from entropy_decoding_df11_amd import runtime
+    _note(f"captured forward path={path}")
+    resident, shared, per_weight = [], [], []
+    for b in range(3):
+        flat, views = workloads.gen_block(seed=200 + b, shapes=SMALL_BLOCK)
+        parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
+        resident.append({nm: torch.from_numpy(a.astype(np.int16)).to("cuda").view(torch.bfloat16)
+                         for nm, a in parts})
+        if path == "inline":
+            shared.append(df11.compress_block(parts, codebook="shared"))
+        if path == "fused":
+            per_weight.append(df11.compress_block(parts, codebook="per_weight"))
+    xs = []
+    for i in range(5):
+        xb = workloads.f32_to_bf16_bits(np.random.default_rng(30 + i).standard_normal(4 * 1024) * 0.5)
+        xs.append(torch.from_numpy(xb.astype(np.int16).reshape(4, 1024)).to("cuda").view(torch.bfloat16))
+    refs = [runtime.model_forward(x, resident).clone() for x in xs]
+    if path == "resident":
+        fwd = lambda x: runtime.model_forward(x, resident)  # noqa: E731
+    elif path == "inline":
+        decoder = runtime.BlockDecoder(shared)
+        fwd = lambda x: runtime.model_forward(x, decoder)  # noqa: E731
+    else:
+        fwd = lambda x: runtime.fused_model_forward(x, per_weight)  # noqa: E731
+    g = runtime.CapturedForward(fwd, xs[0])
+    for i, x in enumerate(xs):
+        got = g(x).clone()
+        torch.cuda.synchronize()
+        if path == "fused":
+            err = float((got.float() - refs[i].float()).abs().max())
+            assert err <= 0.05 * float(refs[i].float().abs().max()), (i, err)
+        else:
+            assert torch.equal(got.view(torch.int16), refs[i].view(torch.int16)), i
+        fwd(xs[(i + 2) % len(xs)])  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_linear_lm_head_full_size(torch_cuda):
     """The LM-head-sized matrix (128256 x 4096, 525M weights, one stream) at
     two tokens: long enough for the dynamic schedule, and every one of the
