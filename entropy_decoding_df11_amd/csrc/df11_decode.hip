@@ -393,6 +393,10 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
     rs.row = static_cast<uint32_t>(__umul64hi(max(e0, lo), m.row_magic));
     rs.dirty = true;
     uint32_t B = (rs.row + 1u) * m.in_features;
+    // x of the first kPrefetchChunks rounds is loaded all at once (1-2
+    // tokens: the decode's registers are free during the merge), one round
+    // ahead (4 tokens), or in its round (8 tokens).
+    constexpr bool kAll = TB <= 2;
     constexpr bool kAhead = TB <= 4;
     constexpr uint32_t kRound = 8u * kWaveSize;  // elements per round
     uint4 xv[TB], xn[TB];
@@ -403,9 +407,23 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
     // B), so B alone does not place every lane.
     uint32_t colb = 2u * (i0 - static_cast<uint32_t>(__umul64hi(i0, m.row_magic)) * m.in_features);
     const uint32_t wrapb = 2u * kRound - 2u * m.in_features;  // modulo 2^32
-    if (kAhead) load_x<TB>(m, colb, xv);
+    // The lane's column one round on: 512 further, less a row when that
+    // passes the row's end.
+    auto next_col = [wrapb](uint32_t c) { return min(c + 2u * kRound, c + wrapb); };
+    uint4 xr[kAll ? kPrefetchChunks : 1][TB];
+    if constexpr (kAll) {
+        uint32_t c = colb;
+#pragma unroll
+        for (int j = 0; j < kPrefetchChunks; ++j) {
+            load_x<TB>(m, c, xr[j]);
+            c = next_col(c);
+        }
+    } else if constexpr (kAhead) {
+        load_x<TB>(m, colb, xv);
+    }
 
-    auto step = [&](uint64_t s8) {
+    // One round, with xc this round's x columns.
+    auto step = [&](uint64_t s8, const uint4 (&xc)[TB]) {
         const bool in_chunks = i0 < chunk_end;
         uint64_t r8 = 0;
         if (in_chunks) {
@@ -415,10 +433,6 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
         // Does this round reach the next row?  (B only moves forward and
         // stays past e0.)
         const bool cross = B < hi_eff && B - e0 < kRound;
-        // The lane's next column: 512 on, less a row when that passes its end.
-        const uint32_t colb_nx = min(colb + 2u * kRound, colb + wrapb);
-        if (kAhead) load_x<TB>(m, colb_nx, xn);
-        else load_x<TB>(m, colb, xv);
         // Chunks past the group's last one merge as zero.
         const uint4 v = merge8(in_chunks ? s8 : 0ull, r8);
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -434,16 +448,16 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
         if (!cross) {
 #pragma unroll
             for (int t = 0; t < TB; ++t)
-                rs.acc[t] = dot2_bf16(w[3], xv[t].w,
-                                      dot2_bf16(w[2], xv[t].z,
-                                                dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, rs.acc[t]))));
+                rs.acc[t] = dot2_bf16(w[3], xc[t].w,
+                                      dot2_bf16(w[2], xc[t].z,
+                                                dot2_bf16(w[1], xc[t].y, dot2_bf16(w[0], xc[t].x, rs.acc[t]))));
         } else {
             // Finish the current row with the lanes before B, carry on with the rest.
             float p[TB];
 #pragma unroll
             for (int t = 0; t < TB; ++t)
-                p[t] = dot2_bf16(w[3], xv[t].w,
-                                 dot2_bf16(w[2], xv[t].z, dot2_bf16(w[1], xv[t].y, dot2_bf16(w[0], xv[t].x, 0.0f))));
+                p[t] = dot2_bf16(w[3], xc[t].w,
+                                 dot2_bf16(w[2], xc[t].z, dot2_bf16(w[1], xc[t].y, dot2_bf16(w[0], xc[t].x, 0.0f))));
             const bool in_b = i0 >= B;
 #pragma unroll
             for (int t = 0; t < TB; ++t) rs.acc[t] += in_b ? 0.0f : p[t];
@@ -454,11 +468,7 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
             rs.dirty = true;
             B += m.in_features;
         }
-        if (kAhead) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t) xv[t] = xn[t];
-        }
-        colb = colb_nx;
+        colb = next_col(colb);
         e0 += kRound;
         i0 += kRound;
         cell += kRound;
@@ -466,10 +476,23 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
         if (e0 >= run_end) break;
-        step(sm[j]);
+        if constexpr (kAll) {
+            step(sm[j], xr[j]);
+        } else if constexpr (kAhead) {
+            load_x<TB>(m, next_col(colb), xn);
+            step(sm[j], xv);
+#pragma unroll
+            for (int t = 0; t < TB; ++t) xv[t] = xn[t];
+        } else {
+            load_x<TB>(m, colb, xv);
+            step(sm[j], xv);
+        }
     }
-    while (e0 < run_end)
-        step(*reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(i0 >> 3, a.sm_chunks - 1u)));
+    // Rounds past the prefetched ones (groups of more than 1024 chunks).
+    while (e0 < run_end) {
+        load_x<TB>(m, colb, xv);
+        step(*reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(i0 >> 3, a.sm_chunks - 1u)), xv);
+    }
     flush_wave<TB>(m, rs, row0, yacc);
 }
 
