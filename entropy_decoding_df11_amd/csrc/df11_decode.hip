@@ -1046,21 +1046,26 @@ int validate(const df11_device_stream *s) {
 }
 
 // Workgroup count and pool count for the dynamic schedule of a stream with
-// n_super super-groups given `want` workgroups: the pools must divide the
-// workgroup count, and no counter may serve more than kMaxPerPool of them
-// (else the count is rounded down to a multiple of kPools).  Sets a.sched to
-// null when the schedule does not pay (fewer than kDynamicMinRounds rounds).
+// n_super super-groups given `want` workgroups.  The pools must divide the
+// workgroup count (a pool's share of the work is fixed), and a pool balances
+// only its own workgroups, so the fewest pools that keep every counter within
+// kMaxPerPool workgroups are taken, dropping a few workgroups if no count of
+// kPools or fewer divides theirs.  (The largest divisor gave a batch's small
+// streams pools of two workgroups, which finish late whenever both are slow
+// ones.)  Beyond kPools * kMaxPerPool workgroups the count is rounded down to
+// a multiple of kPools.  Sets a.sched to null when the schedule does not pay
+// (fewer than kDynamicMinRounds rounds).
 uint32_t schedule_pools(DecodeArgs &a, uint64_t n_super, uint64_t want) {
     uint64_t n_wg = std::max<uint64_t>(1, std::min(want, n_super));
-    uint32_t pools = 1;
-    for (uint32_t p = kPools; p >= 1; --p)
-        if (n_wg % p == 0) {
-            pools = p;
-            break;
-        }
-    if (n_wg / pools > kMaxPerPool) {
+    uint32_t pools = 0;
+    if (n_wg > static_cast<uint64_t>(kPools) * kMaxPerPool) {
         n_wg -= n_wg % kPools;
         pools = kPools;
+    }
+    while (!pools) {  // ends by n_wg = kMaxPerPool at the latest (one pool)
+        for (uint32_t p = 1; p <= kPools && !pools; ++p)
+            if (n_wg % p == 0 && n_wg / p <= kMaxPerPool) pools = p;
+        if (!pools) --n_wg;
     }
     a.pools = pools;
     if (n_super < kDynamicMinRounds * n_wg) a.sched = nullptr;
@@ -1257,6 +1262,14 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
         b.s[b.n++] = a;
     }
     if (b.n == 0) return DF11_OK;
+    if (b.n == 1) {  // one non-empty stream: the single-stream kernel
+        switch (bits) {
+        case 10: return launch_k<10>(b.s[0], gpw, max_wg, stream, start, stop);
+        case 11: return launch_k<11>(b.s[0], gpw, max_wg, stream, start, stop);
+        case 12: return launch_k<12>(b.s[0], gpw, max_wg, stream, start, stop);
+        default: return DF11_E_INVALID_ARG;
+        }
+    }
 #define DF11_BATCH_CASE(KB)                                                  \
     case KB:                                                                 \
         switch (gpw) {                                                       \
