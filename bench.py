@@ -607,8 +607,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     # The GPU's clocks take some tens of milliseconds of sustained load to
-    # settle; 100 launches (~15 ms) reach the steady state.
-    ap.add_argument("--warmup", type=int, default=100)
+    # settle: after 100 launches (~15 ms) the decode is within ~1.5% of its
+    # steady state, after 300 (~40 ms) within noise (1000 measure the same).
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-table-bits", type=int, default=11)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=WORKLOAD_CHOICES,
                     help="the Llama-3-8B block (default), the same with a codebook per weight (one batched "
@@ -637,7 +638,7 @@ def main() -> int:
         if have("trace"):
             summarize_profiles(args.summarize_profiles, {
                 "trace": pre + "rocprofv3 --kernel-trace --stats -d $D/trace -o run --output-format csv "
-                               "-- python3 $R/bench.py --steps 100 --warmup 100 --no-cpu-baseline > $D/bench.json",
+                               "-- python3 $R/bench.py --steps 100 --warmup 300 --no-cpu-baseline > $D/bench.json",
                 "fetch": pre + "rocprofv3 --pmc FETCH_SIZE -d $D/fetch -o run --output-format csv "
                                "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
                 "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
@@ -652,7 +653,7 @@ def main() -> int:
             summarize_kernel_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
                                    "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
                                    pre + "rocprofv3 --kernel-trace --stats -d $D/rans_trace -o run --output-format csv "
-                                         "-- python3 $R/bench.py --coder rans --steps 100 --warmup 100 "
+                                         "-- python3 $R/bench.py --coder rans --steps 100 --warmup 300 "
                                          "--no-cpu-baseline > $D/rans_trace.json",
                                    "df11_rans_decode_kernel_llama3_8b_block_trace.md")
         counter_runs = [("df11_decode_kernel", "df11_decode_kernel on llama3_8b_block",
