@@ -7,13 +7,15 @@ in HBM.  Prints one JSON line.  --workload picks another input: the same block
 with a codebook per weight (seven streams, one batched launch), or a single
 stream (LM-head-sized 128256x4096, the 2^28 stress stream, ...).
 
-  value     = K * (algorithmic bytes per step) / (timed wall time), GB/s
+  value     = K * (algorithmic bytes per step) / (wall time of K back-to-back
+              launches), GB/s
   algorithmic bytes per step = EncodedExponent + PackedSignMantissa + Gaps
               + output positions + LUTs + CodeLengths (all unpadded) read,
               plus 2 bytes per BF16 weight written
-  roofline  = the same bytes / the decode kernel's mean duration (a pair of
-              HIP events per launch that the kernel dispatch itself records on
-              its stream, hipExtLaunchKernel) against the 8 TB/s HBM peak;
+  roofline  = the same bytes / the decode kernel's mean duration over K more
+              launches (a pair of HIP events per launch that the kernel
+              dispatch itself records on its stream, hipExtLaunchKernel)
+              against the 8 TB/s HBM peak;
               kernel_ms_cold_median times 20 more launches, each after a 1 GiB
               read that flushes the L2 and the MALL
   cpu_baseline = the CPU oracle's tree-walk decoder, group-parallel over the
@@ -751,11 +753,20 @@ def main() -> int:
     for _ in range(args.warmup):
         decode()
     torch.cuda.synchronize()
+    # Whole-job time: back-to-back launches as an application issues them.
     wall0 = time.perf_counter()
+    for i in range(args.steps):
+        decode()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    # Kernel time: the same launches again, each recording its kernel's own
+    # start and end (dispatch events; recording them widens the gap between
+    # launches by ~4.5 us, so the wall time above is taken without them).
+    # The check of the output comes after both: the copy to the host idles
+    # the GPU long enough for its clocks to drop.
     for i in range(args.steps):
         decode((starts[i], ends[i]))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     if not np.array_equal(decoded(), flat):
         print(f"bench: the timed launches decoded {wl} wrongly", file=sys.stderr)
