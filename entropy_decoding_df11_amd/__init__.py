@@ -2,8 +2,9 @@
 
 Host encoders and gfx950 decoders (DF11 Huffman, the decode fused into a
 small-batch matmul, and an rANS exponent coder) live in libdf11.so (C ABI:
-include/df11.h); this package is its Python binding, a block decoder for model
-forwards (runtime) and the seeded synthetic workloads.
+include/df11.h); this package is its Python binding, the model-forward helpers
+(runtime: blocks decoded before use, projections with the decode fused in,
+forwards captured into HIP graphs) and the seeded synthetic workloads.
 """
 
 from .df11 import (DF11Block, DF11BlockBatch, DF11RansTensor, DF11Tensor, HostStream, RansHostStream, build_codebook,
