@@ -219,11 +219,13 @@ template <int TB>
 __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
                                         uint64_t (&sm)[kPrefetchChunks]);
 
-// Byte offset of the first-level table entry (one uint32 per entry in each
-// array) for the K-bit window at bit p = acc & 63 of the 64-bit pair.
+// Byte offset of the first-level table entry (a pair of uint32: the
+// exponent run, then the aux word) for the K-bit window at bit p = acc & 63
+// of the 64-bit pair.  The entry's start mask is the uint16 at byte offset
+// (offset >> 2) of the masks.
 template <int K>
 __device__ __forceinline__ uint32_t entry_offset(uint64_t pair, uint32_t acc) {
-    return (static_cast<uint32_t>((pair << (acc & 63u)) >> 32) >> (30 - K)) & ~3u;
+    return (static_cast<uint32_t>((pair << (acc & 63u)) >> 32) >> (29 - K)) & ~7u;
 }
 
 template <typename T>
@@ -543,7 +545,7 @@ __device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32
             const uint32_t j = c - cum;
             uint32_t code_end = q + (x & 0xFFu);
             if (j < m) {
-                uint32_t starts = lds_at<uint16_t>(s_start, off >> 1);
+                uint32_t starts = lds_at<uint16_t>(s_start, off >> 2);
                 for (uint32_t i = 0; i < j; ++i) starts &= starts - 1u;
                 code_end = q + __builtin_ctz(starts);
             }
@@ -682,14 +684,16 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 template <int K, int GPW, int TB>
 __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulArgs &m, const uint32_t wg,
                                               const uint32_t n_wg) {
-    // Static LDS: the first-level table (lo words | aux words | start masks)
-    // at a fixed address, so a lookup's address is its index times 4.
+    // Static LDS: the first-level table (2^K (lo, aux) word pairs, then 2^K
+    // start masks) at a fixed address, so a lookup's address is its index
+    // times 8.  A pair is one 64-bit LDS read; lo and aux 8 KB apart (the
+    // same bank for every lane) made random lookups take 1.8x as long.
     // Dynamic LDS: LUTs | CodeLengths | GPW exponent buffers | wave sums |
     // edge flags | ticket | (fused matmul) GPW row-sum arrays.
     __shared__ __align__(16) uint32_t s_tab[(10u << K) / 4u];
     extern __shared__ __align__(16) uint8_t smem[];
-    const uint32_t *s_lo = s_tab;
-    const uint32_t *s_aux = s_tab + (1u << K);
+    const uint32_t *s_lo = s_tab;      // word 0 of each pair
+    const uint32_t *s_aux = s_tab + 1;  // word 1
     const uint16_t *s_start = reinterpret_cast<const uint16_t *>(s_tab + (2u << K));
     uint8_t *s_luts = smem;
     uint8_t *s_clen = s_luts + a.n_luts * 256u;

@@ -348,9 +348,9 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
         }
     }
     const uint32_t size = 1u << bits;
-    uint32_t *lo = static_cast<uint32_t *>(table);
-    uint32_t *aux = lo + size;
-    uint16_t *starts = reinterpret_cast<uint16_t *>(aux + size);
+    // Entry x: words 2x (exponent run) and 2x + 1 (aux), then the start masks.
+    uint32_t *pairs = static_cast<uint32_t *>(table);
+    uint16_t *starts = reinterpret_cast<uint16_t *>(pairs + 2 * size);
     for (uint32_t x = 0; x < size; ++x) {
         uint32_t used = 0, mask = 0, m = 0;
         uint8_t syms[df11::kDecodeTableMaxSyms] = {0};
@@ -373,9 +373,9 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
         uint32_t lo_word = 0;
         for (uint32_t j = 0; j < 4 && j < m; ++j)
             lo_word |= static_cast<uint32_t>(df11::rotate_exponent(syms[j])) << (8 * j);
-        lo[x] = lo_word;
-        aux[x] = m ? (((m << 11) + used) | ((m > 4 ? df11::rotate_exponent(syms[4]) : 0u) << 16))
-                   : df11::kLongCodeIncrement;
+        pairs[2 * x] = lo_word;
+        pairs[2 * x + 1] = m ? (((m << 11) + used) | ((m > 4 ? df11::rotate_exponent(syms[4]) : 0u) << 16))
+                             : df11::kLongCodeIncrement;
         starts[x] = static_cast<uint16_t>(m ? mask : 1u);
     }
     return DF11_OK;

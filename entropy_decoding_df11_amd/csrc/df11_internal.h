@@ -7,8 +7,9 @@
 namespace df11 {
 
 // First-level decode table: indexed by the next `bits` bits of the stream.
-// Entry x is stored in two uint32 arrays of 2^bits words, lo | aux, followed
-// by a uint16 array of 2^bits start masks:
+// Entry x is the pair of uint32 words 2x (lo) and 2x + 1 (aux), read by the
+// decoder as one 64-bit word; the 2^bits pairs are followed by a uint16 array
+// of 2^bits start masks:
 //   lo:    exponents 0..3 of the complete codes at the start of the window
 //          (byte j = j-th code; unused bytes are zero)
 //   aux:   bits 0..15  increment (m << 11) + nb, where m (1..5) is the number

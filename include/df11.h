@@ -206,7 +206,10 @@ uint64_t df11_decode_table_bytes(uint32_t bits);
  * bits-wide window it lists the complete codes at the start of the window
  * (up to five exponents, their start offsets and their total length) so one LDS
  * lookup resolves several short codes; windows whose first code is longer than
- * the index width fall back to the page's LUT hierarchy.
+ * the index width fall back to the page's LUT hierarchy.  Layout: for each
+ * window x, uint32 words 2x (up to four rotated exponents, one per byte) and
+ * 2x + 1 (codes << 11 | bits, the fifth exponent in bits 16..23), then one
+ * uint16 start mask per window.
  * table: host, df11_decode_table_bytes(bits) bytes. */
 int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table, uint64_t table_bytes);
 

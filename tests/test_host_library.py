@@ -257,7 +257,7 @@ def test_decode_table_matches_code_table(workload, bits, case):
     table = df11.decode_table(cb, bits)
     size = 1 << bits
     assert table.nbytes == 10 * size
-    lo, aux = table[:size], table[size:2 * size]
+    lo, aux = table[0:2 * size:2], table[1:2 * size:2]
     starts_mask = table[2 * size:].view(np.uint16)
     rot = lambda e: ((e >> 1) | (e << 7)) & 0xFF
     for x in range(size):
