@@ -89,6 +89,58 @@ def test_small_cases_bitexact(torch_cuda, kind, size):
     assert np.array_equal(got, w), f"first mismatch at {int(np.argmax(got != w))}"
 
 
+def _random_stream(rng):
+    """A seeded random BF16 stream: a random length, and exponents from a
+    random mix (a Gaussian of random scale, random-rate outliers and tiny
+    values, or a random Zipf law over a random set of exponents), so that
+    code lengths, LUT depths and the codes at group edges vary widely."""
+    n = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(5000, 400_000)),
+                        int(rng.integers(400_000, 3_000_000))]))
+    if rng.random() < 0.5:
+        v = rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 1)
+        for scale in (1.0, 1e-6):
+            k = rng.random(n) < 10.0 ** rng.uniform(-5, -2)
+            v[k] = rng.standard_normal(int(k.sum())) * scale
+        return workloads.f32_to_bf16_bits(v)
+    used = rng.choice(np.arange(1, 240), size=int(rng.integers(2, 60)), replace=False)
+    p = 1.0 / np.arange(1, used.size + 1) ** rng.uniform(0.5, 2.5)
+    e = rng.choice(used, n, p=p / p.sum())
+    return workloads.f32_to_bf16_bits(np.ldexp(1.0 + rng.integers(0, 128, n) / 128.0, e - 127)
+                                      * rng.choice([-1.0, 1.0], n))
+
+
+def test_random_streams_bit_exact(torch_cuda):
+    """100 seeded random streams (lengths 1..3M, random exponent laws)
+    decoded bit for bit by the Huffman decoder and by the rANS decoder."""
+    torch = torch_cuda
+    rng = np.random.default_rng(2024)
+    for i in range(100):
+        w = _random_stream(rng)
+        _note(f"random stream {i} n={w.size}")
+        got, _ = _gpu_decode(torch, w, bits=11)
+        assert np.array_equal(got, w), (i, w.size, int(np.argmax(got != w)))
+        r = df11.rans_compress(w, shape=(w.size,))
+        out = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        r.decompress(out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(_to_u16(out), w), ("rans", i, w.size)
+
+
+def test_random_shapes_linear(torch_cuda):
+    """The fused product on 24 seeded random shapes (in_features a multiple
+    of 8 from 512 up, 1..8 tokens) within the float32 bound of the oracle."""
+    torch = torch_cuda
+    rng = np.random.default_rng(77)
+    for i in range(24):
+        in_f = 8 * int(rng.integers(64, 1200))
+        out_f = int(rng.integers(1, max(2, 600_000 // in_f)))
+        T = int(rng.integers(1, 9))
+        w = workloads.f32_to_bf16_bits(rng.standard_normal(out_f * in_f) * 0.02)
+        _note(f"random linear {i} {out_f}x{in_f} T={T}")
+        t = df11.compress(w, shape=(out_f, in_f))
+        _check_linear(torch, t, w, _tokens(T, in_f, 100 + i), out_f, in_f, calls=1)
+
+
 @pytest.mark.parametrize("bits", [10, 11, 12])
 @pytest.mark.parametrize("kind", ["normal", "fib_chain", "stress_tuned", "uniform_bits"])
 def test_decode_table_widths_agree(torch_cuda, bits, kind):
