@@ -173,6 +173,9 @@ class DF11Tensor:
         self._schedule = torch.zeros(_lib.SCHEDULE_WORDS, dtype=torch.int32, device=self.device)
         s.schedule = self._schedule.data_ptr()
         self._stream_struct = s
+        # The uploads and the counters' zero fill ran on the current stream:
+        # finish them, so that a first launch on any stream sees them.
+        torch.cuda.current_stream(self.device).synchronize()
 
     def set_dynamic_schedule(self, on: bool) -> None:
         """Balance work between workgroups at run time (default) or assign it
@@ -605,6 +608,9 @@ class DF11RansTensor:
         for name, t in self._bufs.items():
             setattr(s, name, t.data_ptr())
         self._stream_struct = s
+        # The uploads and the counters' zero fill ran on the current stream:
+        # finish them, so that a first launch on any stream sees them.
+        torch.cuda.current_stream(self.device).synchronize()
 
     @property
     def n_elements(self) -> int:
