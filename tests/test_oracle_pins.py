@@ -39,6 +39,13 @@ def _hist_from_weights(weights, symbols=None):
 # BF16 fields ("Ruang kompresi ...": 1 sign, 8 exponent, 7 mantissa bits)
 # ---------------------------------------------------------------------------
 
+def _page_statistics():
+    """The page's stated figures (tests/golden/page_statistics.json, each
+    with its section)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_statistics.json")) as f:
+        return json.load(f)
+
+
 def test_split_matches_ieee_bf16_semantics_exhaustively():
     w = np.arange(65536, dtype=np.uint32)
     e_all = (w >> 7) & 0xFF
@@ -69,6 +76,8 @@ def test_merge_inverts_split_exhaustively():
 @pytest.mark.parametrize("bits", [0x7F80, 0xFF80, 0x7FC0, 0x7800, 0xF812])
 def test_reserved_exponents_rejected(bits):
     # exponent >= 240: Inf/NaN (255) and |x| >= 2^113; the pages reuse 240..255 as pointers
+    lo, hi = _page_statistics()["pointer_values"]["value"]
+    assert lo <= (bits >> 7) & 0xFF <= hi
     w = np.array([0x3F80, bits, 0x3F00], np.uint16)
     with pytest.raises(oracle.OracleError) as ei:
         oracle.split(w)
@@ -77,6 +86,13 @@ def test_reserved_exponents_rejected(bits):
         oracle.histogram(w)
     with pytest.raises(oracle.OracleError):
         oracle.encode(w)
+
+
+def test_largest_usable_exponent_encodes():
+    """Exponent 239, just below the pointer range, is an ordinary value."""
+    lo, _ = _page_statistics()["pointer_values"]["value"]
+    w = np.array([0x3F80, (lo - 1) << 7, 0x8000 | ((lo - 1) << 7) | 0x55, 0x3F00], np.uint16)
+    assert np.array_equal(oracle.decode_treewalk(oracle.encode(w)), w)
 
 
 # ---------------------------------------------------------------------------
@@ -337,6 +353,7 @@ def test_metadata_invariants(workload, name):
     gaps = oracle.gap_values(s)
     assert gaps[0] == 0
     assert gaps.max() < s["max_len"] <= 32
+    assert gaps.max() < 1 << _page_statistics()["gap_bits"]["value"]  # a gap fits its 5-bit field
     op = s["out_pos"].astype(np.int64)
     assert op[0] == 0 and op[-1] == s["n_elements"] and np.all(np.diff(op) >= 0)
     counts = oracle.check_metadata(s)
@@ -409,8 +426,9 @@ def test_entropy_bound_kraft_and_size(workload, name):
     n = s["n_elements"]
     size = n + -(-s["total_bits"] // 8) + -(-5 * s["n_threads"] // 8) + 4 * (s["n_groups"] + 1) + 256 * (s["n_luts"] + 1)
     # "Format DFloat11": about 11 bits per weight, about 70% of BF16
-    assert 10.5 <= 8 + lbar <= 11.2
-    assert 0.64 <= size / (2 * n) <= 0.72
+    page = _page_statistics()
+    assert abs(8 + lbar - page["bits_per_weight"]["value"]) <= 0.5
+    assert abs(size / (2 * n) - page["size_fraction"]["value"]) <= 0.06
 
 
 @pytest.mark.parametrize("name", ["single_1024x1024", "proj_4096x4096_outliers", "mlp_14336x4096_t5"])
@@ -423,21 +441,25 @@ def test_field_entropies_match_pages(workload, name):
     h_mant = _entropy(np.bincount(sm & 0x7F, minlength=128))
     hist = oracle.histogram(w)
     h_exp = _entropy(hist.astype(np.float64))
+    page = _page_statistics()
     assert h_sign > 0.999
     assert h_mant > 6.9
-    assert 2.4 < h_exp < 2.8
-    assert 20 <= int((hist > 0).sum()) <= 45
+    assert abs(h_exp - page["exponent_entropy_bits"]["value"]) < 0.2
+    assert 20 <= int((hist > 0).sum()) <= page["used_exponent_values"]["value"] + 5
 
 
 def test_block_and_stress_code_lengths_in_pages_range():
     """'Decoding berbasis LUT hierarkis': for LLM weights the longest code is
     about 24-32 bits and 4-8 compact LUTs suffice."""
+    page = _page_statistics()
+    lo_len, hi_len = page["max_code_length_range"]["value"]
+    lo_k, hi_k = page["compact_lut_count_range"]["value"]
     w, _ = workloads.gen_block()
     cb = oracle.codebook(oracle.histogram(w))
-    assert 24 <= cb["max_len"] <= 32 and 4 <= cb["n_luts"] <= 8
+    assert lo_len <= cb["max_len"] <= hi_len and lo_k <= cb["n_luts"] <= hi_k
     w = workloads.gen_stress(n=1 << 24)
     cb = oracle.codebook(oracle.histogram(w))
-    assert 28 <= cb["max_len"] <= 32 and 4 <= cb["n_luts"] <= 8
+    assert 28 <= cb["max_len"] <= hi_len and lo_k <= cb["n_luts"] <= hi_k
     assert 36 <= int((oracle.histogram(w) > 0).sum()) <= 40  # all 40 ranks occur at the full 2^28 size
 
 
