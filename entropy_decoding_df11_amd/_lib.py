@@ -49,6 +49,8 @@ EXPORTED = [
     "df11_linear",
     "df11_linear_timed",
     "df11_linear_batch",
+    "df11_linear_acc",
+    "df11_linear_batch_acc",
     "df11_rans_quantize",
     "df11_rans_encode",
     "df11_rans_build_table",
@@ -182,6 +184,8 @@ def load() -> ctypes.CDLL:
                                                        ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_linear_acc": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                           ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p]),
@@ -189,6 +193,10 @@ def load() -> ctypes.CDLL:
                                              ctypes.c_uint32, ctypes.c_uint32, u32p,
                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p]),
+        "df11_linear_batch_acc": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32, ctypes.c_void_p,
+                                                 ctypes.c_uint32, ctypes.c_uint32, u32p,
+                                                 ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
         "df11_rans_quantize": (ctypes.c_int, [u64p, u32p]),
         "df11_rans_encode": (ctypes.c_int, [u32p, u16p, ctypes.c_uint64, u32p, u32p, u16p, ctypes.c_uint64, u8p,
                                             ctypes.POINTER(RansHeader)]),

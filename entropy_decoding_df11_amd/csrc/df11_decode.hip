@@ -1290,10 +1290,11 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
 #undef DF11_BATCH_CASE
 }
 
-// y = 0 (zero kernel), then the fused kernel over the persistent grid.
+// y = 0 (zero kernel, unless the caller accumulates into y), then the
+// fused kernel over the persistent grid.
 template <int K, int TB>
 int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream,
-                  hipEvent_t start, hipEvent_t stop) {
+                  hipEvent_t start, hipEvent_t stop, bool zero) {
     const size_t lds = dynamic_lds<kLinearGPW>(a) + sizeof(float) * kLinearGPW * m.yacc_rows * TB;
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
@@ -1311,9 +1312,11 @@ int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hip
     float *y = m.y;
     void *zparams[] = {&y, const_cast<uint32_t *>(&n_y)};
     const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((n_y + 255) / 256, 1024));
-    const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256), zparams,
-                                 0, stream, nullptr, nullptr);
-    if (rc) return rc;
+    if (zero) {
+        const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256),
+                                     zparams, 0, stream, nullptr, nullptr);
+        if (rc) return rc;
+    }
     void *params[] = {&args, &margs};
     return launch_kernel(fn, dim3(grid), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop);
 }
@@ -1355,19 +1358,20 @@ int linear_args(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
 uint32_t token_slots(uint32_t n_tokens) { return n_tokens <= 1 ? 1 : n_tokens <= 2 ? 2 : n_tokens <= 4 ? 4 : 8; }
 
 int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
-                uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                bool zero) {
     DecodeArgs a;
     MatmulArgs m;
     bool empty = false;
     const int rc = linear_args(s, x, n_tokens, in_features, out_features, y, a, m, empty);
     if (rc || empty) return rc;
-#define DF11_LINEAR_CASE(KB)                                                       \
-    case KB:                                                                       \
-        switch (token_slots(n_tokens)) {                                           \
-        case 1: return launch_linear<KB, 1>(a, m, s->max_workgroups, stream, start, stop); \
-        case 2: return launch_linear<KB, 2>(a, m, s->max_workgroups, stream, start, stop); \
-        case 4: return launch_linear<KB, 4>(a, m, s->max_workgroups, stream, start, stop); \
-        default: return launch_linear<KB, 8>(a, m, s->max_workgroups, stream, start, stop); \
+#define DF11_LINEAR_CASE(KB)                                                                      \
+    case KB:                                                                                      \
+        switch (token_slots(n_tokens)) {                                                          \
+        case 1: return launch_linear<KB, 1>(a, m, s->max_workgroups, stream, start, stop, zero);  \
+        case 2: return launch_linear<KB, 2>(a, m, s->max_workgroups, stream, start, stop, zero);  \
+        case 4: return launch_linear<KB, 4>(a, m, s->max_workgroups, stream, start, stop, zero);  \
+        default: return launch_linear<KB, 8>(a, m, s->max_workgroups, stream, start, stop, zero); \
         }
     switch (s->decode_table_bits) {
         DF11_LINEAR_CASE(10)
@@ -1382,7 +1386,7 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
 // split between the streams in proportion to their super-groups.
 template <int K, int TB>
 int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
-                        hipEvent_t stop) {
+                        hipEvent_t stop, bool zero) {
     size_t lds = 0;
     uint64_t total_super = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
@@ -1414,16 +1418,18 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
     const uint32_t total = z.end[z.n - 1];
     void *zparams[] = {&z};
     const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((total + 255) / 256, 1024));
-    const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256),
-                                 zparams, 0, stream, nullptr, nullptr);
-    if (rc) return rc;
+    if (zero) {
+        const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256),
+                                     zparams, 0, stream, nullptr, nullptr);
+        if (rc) return rc;
+    }
     void *params[] = {&b};
     return launch_kernel(fn, dim3(next), dim3(kThreadsPerGroup * kLinearGPW), params, lds, stream, start, stop);
 }
 
 int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *x, uint32_t n_tokens,
                       uint32_t in_features, const uint32_t *out_features, float *const *ys, hipStream_t stream,
-                      hipEvent_t start, hipEvent_t stop) {
+                      hipEvent_t start, hipEvent_t stop, bool zero) {
     if (n > kMaxBatch) return DF11_E_TOO_LARGE;
     if (n && (!ws || !out_features || !ys)) return DF11_E_INVALID_ARG;
     LinearBatchArgs b{};
@@ -1466,13 +1472,13 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
     }
     if (b.n == 0) return DF11_OK;
     z.n = b.n;
-#define DF11_LINEAR_BATCH_CASE(KB)                                                              \
-    case KB:                                                                                    \
-        switch (token_slots(n_tokens)) {                                                        \
-        case 1: return launch_linear_batch<KB, 1>(b, z, max_wg, stream, start, stop);           \
-        case 2: return launch_linear_batch<KB, 2>(b, z, max_wg, stream, start, stop);           \
-        case 4: return launch_linear_batch<KB, 4>(b, z, max_wg, stream, start, stop);           \
-        default: return launch_linear_batch<KB, 8>(b, z, max_wg, stream, start, stop);          \
+#define DF11_LINEAR_BATCH_CASE(KB)                                                           \
+    case KB:                                                                                 \
+        switch (token_slots(n_tokens)) {                                                     \
+        case 1: return launch_linear_batch<KB, 1>(b, z, max_wg, stream, start, stop, zero);  \
+        case 2: return launch_linear_batch<KB, 2>(b, z, max_wg, stream, start, stop, zero);  \
+        case 4: return launch_linear_batch<KB, 4>(b, z, max_wg, stream, start, stop, zero);  \
+        default: return launch_linear_batch<KB, 8>(b, z, max_wg, stream, start, stop, zero); \
         }
     switch (bits) {
         DF11_LINEAR_BATCH_CASE(10)
@@ -1517,13 +1523,19 @@ int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_
 int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                 uint32_t out_features, float *y, void *hip_stream) {
     return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
-                       nullptr);
+                       nullptr, true);
+}
+
+int df11_linear_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                    uint32_t out_features, float *y, void *hip_stream) {
+    return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
+                       nullptr, false);
 }
 
 int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event) {
     return linear_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream),
-                       static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+                       static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event), true);
 }
 
 int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
@@ -1531,7 +1543,15 @@ int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const ui
                       void *start_event, void *stop_event) {
     return linear_batch_impl(ws, n_streams, x, n_tokens, in_features, out_features, ys,
                              static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
-                             static_cast<hipEvent_t>(stop_event));
+                             static_cast<hipEvent_t>(stop_event), true);
+}
+
+int df11_linear_batch_acc(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
+                          uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
+                          void *start_event, void *stop_event) {
+    return linear_batch_impl(ws, n_streams, x, n_tokens, in_features, out_features, ys,
+                             static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
+                             static_cast<hipEvent_t>(stop_event), false);
 }
 
 }  // extern "C"

@@ -241,13 +241,14 @@ class DF11Tensor:
 
 
     def linear(self, x: "torch.Tensor", out: Optional["torch.Tensor"] = None, stream=None,  # noqa: F821
-               events=None) -> "torch.Tensor":  # noqa: F821
+               events=None, accumulate: bool = False) -> "torch.Tensor":  # noqa: F821
         """y = x W^T with the decode fused into the product (df11_linear): W
         is this tensor as an (out_features, in_features) matrix, x a
         contiguous bfloat16 (n_tokens, in_features) tensor on the same device
         with 1 <= n_tokens <= 8.  Returns out, a float32 (n_tokens,
         out_features) tensor (a new one by default).  events: as for
-        decompress, recorded at the fused kernel's own start and end."""
+        decompress, recorded at the fused kernel's own start and end.  With
+        accumulate, out (required) receives out + x W^T (df11_linear_acc)."""
         import torch
         if len(self.shape) != 2:
             raise ValueError("linear needs a 2-D weight (out_features, in_features)")
@@ -260,6 +261,8 @@ class DF11Tensor:
             raise ValueError("x must be on the weight's device")
         n_tokens = x.shape[0]
         if out is None:
+            if accumulate:
+                raise ValueError("accumulate needs out")
             out = torch.empty((n_tokens, out_f), dtype=torch.float32, device=self.device)
         if out.dtype != torch.float32 or out.shape != (n_tokens, out_f) or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 (n_tokens, out_features) tensor")
@@ -269,7 +272,11 @@ class DF11Tensor:
         st = self._hip_stream(stream)
         args = (ctypes.byref(self._stream_struct), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, out_f,
                 ctypes.c_void_p(out.data_ptr()), st)
-        if events is None:
+        if accumulate:
+            if events is not None:
+                raise ValueError("accumulate takes no events")
+            _lib.check(lib.df11_linear_acc(*args), "df11_linear_acc")
+        elif events is None:
             _lib.check(lib.df11_linear(*args), "df11_linear")
         else:
             start, stop = events
@@ -279,12 +286,14 @@ class DF11Tensor:
 
 
 def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, stream=None,  # noqa: F821
-                 events=None) -> List["torch.Tensor"]:  # noqa: F821
+                 events=None, accumulate: bool = False) -> List["torch.Tensor"]:  # noqa: F821
     """[x W_i^T for each W_i in tensors] in one launch (df11_linear_batch):
     every W_i is (out_features_i, in_features) with the same in_features, x
     a contiguous bfloat16 (n_tokens, in_features) tensor, 1 <= n_tokens <= 8
     (a block's q, k and v, or gate and up).  Returns the float32 outputs
-    (new tensors by default); events as for DF11Tensor.linear."""
+    (new tensors by default); events as for DF11Tensor.linear.  With
+    accumulate, each of outs (required) receives outs[i] + x W_i^T
+    (df11_linear_batch_acc)."""
     import torch
     if not tensors:
         return []
@@ -301,6 +310,8 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
         raise ValueError("x and every weight must be on the same device")
     n_tokens = x.shape[0]
     if outs is None:
+        if accumulate:
+            raise ValueError("accumulate needs outs")
         outs = [torch.empty((n_tokens, t.shape[0]), dtype=torch.float32, device=x.device) for t in tensors]
     for t, y in zip(tensors, outs):
         if y.dtype != torch.float32 or y.shape != (n_tokens, t.shape[0]) or not y.is_contiguous():
@@ -314,8 +325,10 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
     ptrs = (ctypes.c_void_p * len(tensors))(*[y.data_ptr() for y in outs])
     ev = (None, None) if events is None else (ctypes.c_void_p(_event_handle(events[0], st)),
                                               ctypes.c_void_p(_event_handle(events[1], st)))
-    _lib.check(lib.df11_linear_batch(arr, len(tensors), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f,
-                                     _ptr(out_f, ctypes.c_uint32), ptrs, st, *ev), "df11_linear_batch")
+    fn, name = (lib.df11_linear_batch_acc, "df11_linear_batch_acc") if accumulate else \
+        (lib.df11_linear_batch, "df11_linear_batch")
+    _lib.check(fn(arr, len(tensors), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, _ptr(out_f, ctypes.c_uint32),
+                  ptrs, st, *ev), name)
     return outs
 
 

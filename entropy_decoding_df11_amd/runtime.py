@@ -125,23 +125,34 @@ def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
     weight is ever decompressed to HBM.  The products accumulate in float32
     and are rounded to x's dtype, like the resident path's outputs, but in
     another order, so the last bits can differ from block_forward's."""
+    import torch
     import torch.nn.functional as F
     from .df11 import linear_batch
 
     w = {nm: t for (nm, _, _), t in zip(blk.views, blk.tensors)}
 
     def rms(h):
-        import torch
         return h * torch.rsqrt(h.float().pow(2).mean(-1, keepdim=True) + eps).to(h.dtype)
 
+    # The seven products accumulate into views of one buffer, zeroed by one
+    # fill, rather than each zeroing its own output (df11_linear_acc).
+    names = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+    tokens = x.shape[0]
+    sizes = [tokens * w[nm].shape[0] for nm in names]
+    buf = torch.zeros(sum(sizes), dtype=torch.float32, device=x.device)
+    y = {nm: part.view(tokens, w[nm].shape[0]) for nm, part in zip(names, torch.split(buf, sizes))}
+
     h = rms(x).contiguous()
-    q, k, v = (y.to(x.dtype) for y in linear_batch([w["q_proj"], w["k_proj"], w["v_proj"]], h))
+    linear_batch([w["q_proj"], w["k_proj"], w["v_proj"]], h, outs=[y["q_proj"], y["k_proj"], y["v_proj"]],
+                 accumulate=True)
+    q, k, v = (y[nm].to(x.dtype) for nm in ("q_proj", "k_proj", "v_proj"))
     rep = q.shape[-1] // k.shape[-1]
     a = q + (k * v).repeat_interleave(rep, dim=-1)
-    x = x + w["o_proj"].linear(a.contiguous()).to(x.dtype)
+    x = x + w["o_proj"].linear(a.contiguous(), out=y["o_proj"], accumulate=True).to(x.dtype)
     h = rms(x).contiguous()
-    g, u = (y.to(x.dtype) for y in linear_batch([w["gate_proj"], w["up_proj"]], h))
-    x = x + w["down_proj"].linear((F.silu(g) * u).contiguous()).to(x.dtype)
+    linear_batch([w["gate_proj"], w["up_proj"]], h, outs=[y["gate_proj"], y["up_proj"]], accumulate=True)
+    g, u = (y[nm].to(x.dtype) for nm in ("gate_proj", "up_proj"))
+    x = x + w["down_proj"].linear((F.silu(g) * u).contiguous(), out=y["down_proj"], accumulate=True).to(x.dtype)
     return x
 
 

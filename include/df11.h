@@ -299,6 +299,12 @@ int df11_decompress_batch_timed(const df11_device_stream *streams, uint32_t n_st
 int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                 uint32_t out_features, float *y, void *hip_stream);
 
+/* df11_linear accumulating into y: y += x W^T, with the same arguments,
+ * sums and errors, and no zeroing kernel; y must hold the values to add to
+ * (zeros, say, set once for several products that share one buffer). */
+int df11_linear_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                    uint32_t out_features, float *y, void *hip_stream);
+
 /* df11_linear with start_event and stop_event (hipEvent_t, either may be
  * NULL) recorded when the fused kernel itself starts and ends (the zeroing
  * kernel before it is not included), to measure the fused product.  Same
@@ -327,6 +333,12 @@ int df11_linear_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n
 int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
                       uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
                       void *start_event, void *stop_event);
+
+/* df11_linear_batch accumulating into every output: ys[i] += x W_i^T, with
+ * the same arguments and errors and no zeroing kernel. */
+int df11_linear_batch_acc(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
+                          uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
+                          void *start_event, void *stop_event);
 
 /* ---------------------------------------------------------------------------
  * rANS exponent coder.  The discussion on the page ("Opini Hacker News")

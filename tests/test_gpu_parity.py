@@ -445,6 +445,48 @@ def test_linear_argument_errors(torch_cuda):
         t.linear(torch.zeros((2, 1000), dtype=torch.bfloat16, device="cuda"))
 
 
+def test_linear_accumulate(torch_cuda):
+    """df11_linear_acc and df11_linear_batch_acc add x W^T to what the output
+    holds: starting from a known y0, two calls give y0 + 2 x W^T within twice
+    the float32 bound; without an output the binding refuses."""
+    torch = torch_cuda
+    in_f = 1024
+    shapes = [(300, in_f), (77, in_f)]
+    ws = [_case("normal", r * c, 60 + i) for i, (r, c) in enumerate(shapes)]
+    ts = [df11.compress(w, shape=s) for w, s in zip(ws, shapes)]
+    x = _tokens(3, in_f, 61)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    refs = [oracle.linear(oracle.encode(w), x, r) for w, (r, _) in zip(ws, shapes)]
+    bounds = [_linear_bound(x, w, r, c) for w, (r, c) in zip(ws, shapes)]
+    y0s = [np.random.default_rng(i).standard_normal((3, r)).astype(np.float32) for i, (r, _) in enumerate(shapes)]
+
+    def bound(y0, b):
+        # 2 in_f + 1 float32 additions in any order: gamma_{2n+1} (|y0| + 2 sum |x w|),
+        # where b = 1.01 in_f u sum |x w| is the one-call bound
+        sum_abs = b / (1.01 * in_f * 2.0 ** -24)
+        return 1.01 * (2 * in_f + 1) * 2.0 ** -24 * (np.abs(y0.astype(np.float64)) + 2 * sum_abs)
+
+    # one matrix
+    y = torch.from_numpy(y0s[0].copy()).to("cuda")
+    for _ in range(2):
+        ts[0].linear(xd, out=y, accumulate=True)
+    torch.cuda.synchronize()
+    err = np.abs(y.cpu().numpy().astype(np.float64) - (y0s[0] + 2 * refs[0]))
+    assert np.all(err <= bound(y0s[0], bounds[0]))
+    # a batch
+    ys = [torch.from_numpy(v.copy()).to("cuda") for v in y0s]
+    for _ in range(2):
+        df11.linear_batch(ts, xd, outs=ys, accumulate=True)
+    torch.cuda.synchronize()
+    for got, y0, ref, b in zip(ys, y0s, refs, bounds):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - (y0 + 2 * ref))
+        assert np.all(err <= bound(y0, b))
+    with pytest.raises(ValueError):
+        ts[0].linear(xd, accumulate=True)
+    with pytest.raises(ValueError):
+        df11.linear_batch(ts, xd, accumulate=True)
+
+
 def test_same_stream_twice_in_one_batch(torch_cuda):
     """A batch that holds one tensor twice: both entries would use the same
     work counters, so the second runs the static schedule.  The grid is capped

@@ -360,6 +360,15 @@ def test_linear_validation_runs_before_any_launch():
     es = _lib.DeviceStream()
     es.h = empty.header
     assert lib.df11_linear(ctypes.byref(es), None, 1, 1024, 0, None, None) == 0
+    # the accumulating entry points validate the same way
+    assert lib.df11_linear_acc(ctypes.byref(s), x, 0, 1024, 64, y, None) == -1
+    assert lib.df11_linear_acc(ctypes.byref(s), x, 1, 1024, 64, ctypes.c_void_p(s.sm), None) == -1
+    assert lib.df11_linear_acc(ctypes.byref(bad), x, 1, 1024, 64, y, None) == -6
+    arr = (_lib.DeviceStream * 1)(bad)
+    ys = (ctypes.c_void_p * 1)(y)
+    rows = np.array([64], np.uint32)
+    assert lib.df11_linear_batch_acc(arr, 1, x, 1, 1024, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                     ys, None, None, None) == -6
 
 
 # ---------------------------------------------------------------------------
