@@ -347,7 +347,7 @@ def integration(args, dev) -> int:
             x = runtime.fused_block_forward(x, blk)
         return x
 
-    for tokens in (1, 8, 16, 256, 4096):
+    for tokens in (1, 2, 4, 8, 16, 256, 4096):
         rng = np.random.default_rng(tokens)
         x = workloads.f32_to_bf16_bits(rng.standard_normal(tokens * 4096) * 0.5).reshape(tokens, 4096)
         x = torch.from_numpy(x.astype(np.int16)).to(dev).view(torch.bfloat16)
