@@ -771,6 +771,12 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
 
     uint32_t s_cur = wg, ticket = 0;
     for (uint32_t it = 0; s_cur < n_super; ++it) {
+        // Wave priorities by phase (the SIMD issues the higher one first
+        // among ready waves): the next loads 2, the merge and its stores 0,
+        // phase 1's chain of dependent lookups 3, phase 2 1.  A wave that
+        // starts decoding runs its chain with fewer gaps while the waves in
+        // their merge keep the memory busy.
+        __builtin_amdgcn_s_setprio(2);
         const uint32_t g = s_cur * GPW + slot;
         // Rounds 0..2 are static; the ticket for round it + 1 >= 3 was
         // written to LDS in iteration it - 1.
@@ -795,6 +801,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
         if (sched && tid == 0) fetched = take_ticket(sched, wg % a.pools);  // for round it + 3
+        __builtin_amdgcn_s_setprio(0);
 
         // 2. Merge and store the super-group decoded in the previous
         // iteration (the fused matmul merged it before step 1's loads), then
@@ -804,6 +811,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
             if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
         }
         load_sm<TB>(a, base, end, ltid, sm);
+        __builtin_amdgcn_s_setprio(3);
 
         // 3. Decode this super-group.
         const uint32_t lead = base & 7u;
@@ -864,6 +872,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
             flush_rows<TB>(m, s_yacc, y_row0, y_rows, ltid);
             y_rows = 0;
         }
+        __builtin_amdgcn_s_setprio(1);
         uint32_t wave_off = 0;
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
