@@ -214,7 +214,9 @@ __device__ __forceinline__ GroupLoad load_group(const DecodeArgs &a, uint32_t g,
 // thread merges in its first kPrefetchChunks rounds, loaded (clamped like
 // load_group) one iteration before the merge uses them: chunk ltid + 256 j
 // for the store, or round j of the thread's wave run for the fused matmul
-// (run_chunk).
+// (run_chunk).  Each byte is read once, so the loads are non-temporal (they
+// do not displace the encoded words, which neighbouring threads share, from
+// the caches); the block decode took 122-123 us with them against 126-127.
 template <int TB>
 __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
                                         uint64_t (&sm)[kPrefetchChunks]);
@@ -262,7 +264,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
         }
     }
     for (uint32_t k = ltid + kPrefetchChunks * kThreadsPerGroup; k < n_chunks; k += kThreadsPerGroup) {
-        const uint64_t s8 = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k));
+        const uint64_t s8 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k)));
         uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
         const uint64_t r8 = *cell;
         *cell = 0;
@@ -303,7 +305,7 @@ __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint
         const uint32_t k = TB == 0 ? ltid + j * kThreadsPerGroup
                                    : run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch);
         const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
-        sm[j] = *reinterpret_cast<const uint64_t *>(a.sm + 8ull * c);
+        sm[j] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * c));
     }
 }
 
