@@ -81,8 +81,9 @@ __device__ __forceinline__ void rans_ring_put(uint16_t *ring, uint32_t c, uint32
 }
 
 // Each sign/mantissa byte is read once: a non-temporal load (the block
-// decode took 155-156 us with it against 166; the same hint on the word
-// chunks, which the ring re-reads from the caches, made it slower).
+// decode took 155-156 us with it against 166).  The same hint on the word
+// chunks as well took the block to 173 us and the stress stream from 205 to
+// 243 us.
 __device__ __forceinline__ uint64_t rans_sm8(const RansArgs &a, uint32_t c) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(c, a.sm_chunks - 1u)));
 }
