@@ -529,3 +529,24 @@ def test_device_check_of_the_binding():
     assert not _on_device(torch.zeros(1), "cuda")
     assert not _on_device(torch.zeros(1), "cuda:0")
     assert _on_device(torch.zeros(1), "cpu")
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    """The rocprofv3 summaries under profiles/ name the sha256 prefix of the
+    kernel source they were taken on; the bench line's HBM traffic comes from
+    the counter summary only while that prefix matches the current source."""
+    import hashlib
+    import json
+
+    def prefix(name):
+        with open(os.path.join(REPO, "entropy_decoding_df11_amd", "csrc", name), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+
+    with open(os.path.join(REPO, "profiles", "df11_decode_kernel_llama3_8b_block_pmc.json")) as f:
+        pmc = json.load(f)
+    assert pmc["kernel_source_sha256_16"] == prefix("df11_decode.hip")
+    assert 1.0 <= pmc["traffic_over_algorithmic"] < 1.2
+    for md, src in (("df11_decode_kernel_llama3_8b_block_counters.md", "df11_decode.hip"),
+                    ("df11_rans_decode_kernel_llama3_8b_block_counters.md", "df11_rans_decode.hip")):
+        with open(os.path.join(REPO, "profiles", md)) as f:
+            assert prefix(src) in f.read(), md
