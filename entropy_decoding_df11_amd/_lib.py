@@ -26,6 +26,7 @@ STATUS_NAMES = {
 MAX_LUTS = 17
 SCHEDULE_WORDS = 144  # DF11_SCHEDULE_WORDS
 MAX_BATCH = 16  # DF11_MAX_BATCH
+MAX_ELEMENTS = (1 << 32) - (1 << 16)  # DF11_MAX_ELEMENTS
 LINEAR_MAX_TOKENS = 8  # DF11_LINEAR_MAX_TOKENS
 LINEAR_MIN_IN_FEATURES = 512  # DF11_LINEAR_MIN_IN_FEATURES
 RANS_PROB_BITS = 12  # DF11_RANS_PROB_BITS

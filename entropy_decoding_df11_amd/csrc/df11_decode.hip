@@ -1034,7 +1034,7 @@ int validate(const df11_device_stream *s) {
     if (!s) return DF11_E_INVALID_ARG;
     const df11_header &h = s->h;
     if (h.bytes_per_thread != kBytesPerThread || h.threads_per_group != kThreadsPerGroup) return DF11_E_INVALID_ARG;
-    if (h.n_elements >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    if (h.n_elements > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     if (h.n_elements == 0) return h.total_bits == 0 ? DF11_OK : DF11_E_BAD_STREAM;
     if (df11_decode_table_bytes(s->decode_table_bits) == 0) return DF11_E_INVALID_ARG;
     if (s->groups_per_workgroup != 0 && s->groups_per_workgroup != 1 && s->groups_per_workgroup != 2 &&

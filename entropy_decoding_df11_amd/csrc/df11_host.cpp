@@ -223,7 +223,7 @@ int df11_build_codebook(const uint64_t hist[256], df11_codebook *cb) {
 int df11_plan(const df11_codebook *cb, const uint64_t hist[256], uint64_t n, const df11_layout *lay,
               df11_header *h) {
     if (!cb || !hist || !h || !layout_ok(lay)) return DF11_E_INVALID_ARG;
-    if (n >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    if (n > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     uint64_t total = 0, count = 0;
     for (int e = 0; e < 256; ++e) {
         if (hist[e] && !cb->code_lengths[e]) return DF11_E_INVALID_ARG;
@@ -246,7 +246,7 @@ int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const
                 df11_header *h, uint8_t *enc, uint8_t *sm, uint8_t *gaps, uint32_t *out_pos) {
     if (!cb || !h || !enc || !sm || !gaps || !out_pos || !layout_ok(lay) || (n && !bf16))
         return DF11_E_INVALID_ARG;
-    if (n >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    if (n > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     if (h->n_elements != n || h->bytes_per_thread != lay->bytes_per_thread ||
         h->threads_per_group != lay->threads_per_group)
         return DF11_E_INVALID_ARG;

@@ -233,7 +233,7 @@ int rans_impl(const df11_rans_device_stream *s, uint16_t *out, hipStream_t strea
     const df11_rans_header &h = s->h;
     if (h.prob_bits != DF11_RANS_PROB_BITS || h.lanes != DF11_RANS_LANES || h.steps != DF11_RANS_STEPS)
         return DF11_E_INVALID_ARG;
-    if (h.n_elements >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    if (h.n_elements > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     if (h.n_segments != (h.n_elements + kRansSegment - 1) / kRansSegment || h.n_words > h.n_elements)
         return DF11_E_BAD_STREAM;
     if (h.n_elements == 0) return DF11_OK;

@@ -80,7 +80,7 @@ int df11_rans_build_table(const uint32_t freq[256], uint32_t *table) {
 int df11_rans_encode(const uint32_t freq[256], const uint16_t *w, uint64_t n, uint32_t *states,
                      uint32_t *word_offsets, uint16_t *words, uint64_t words_cap, uint8_t *sm, df11_rans_header *h) {
     if (!freq || !h || !word_offsets || (n && (!w || !states || !sm || !words))) return DF11_E_INVALID_ARG;
-    if (n >= (1ull << 32)) return DF11_E_TOO_LARGE;
+    if (n > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     uint32_t cum[257];
     const bool ok = cumulate(freq, cum);
     if (n && !ok) return DF11_E_INVALID_ARG;

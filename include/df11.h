@@ -36,6 +36,12 @@
 extern "C" {
 #endif
 
+/* Most elements one stream may hold: 2^32 - 2^16.  The decoders index
+ * elements with 32-bit integers; the margin below 2^32 keeps every index
+ * they form (a group's rounded chunk end, a wave's run of rounds ahead)
+ * below 2^32 as well. */
+#define DF11_MAX_ELEMENTS 4294901760ull
+
 typedef enum df11_status {
     DF11_OK = 0,
     DF11_E_INVALID_ARG = -1,        /* null pointer, unsupported layout, bad size argument */
@@ -44,7 +50,7 @@ typedef enum df11_status {
     DF11_E_TOO_MANY_LUTS = -4,      /* the code tree needs more than 16 lower LUTs */
     DF11_E_BUFFER_TOO_SMALL = -5,   /* a caller buffer is smaller than required */
     DF11_E_BAD_STREAM = -6,         /* header fields or codebook are inconsistent */
-    DF11_E_TOO_LARGE = -7,          /* N >= 2^32 elements in one stream */
+    DF11_E_TOO_LARGE = -7,          /* N > DF11_MAX_ELEMENTS elements in one stream */
     DF11_E_HIP = -8                 /* a HIP launch or query failed */
 } df11_status;
 
@@ -394,7 +400,7 @@ int df11_rans_quantize(const uint64_t hist[256], uint32_t freq[256]);
  * sm n bytes.  h is filled in.  Errors: DF11_E_INVALID_ARG (null pointer, a
  * table not summing to M, an exponent with frequency 0),
  * DF11_E_RESERVED_EXPONENT, DF11_E_BUFFER_TOO_SMALL (words_cap), DF11_E_TOO_LARGE
- * (n >= 2^32). */
+ * (n > DF11_MAX_ELEMENTS). */
 int df11_rans_encode(const uint32_t freq[256], const uint16_t *w, uint64_t n, uint32_t *states,
                      uint32_t *word_offsets, uint16_t *words, uint64_t words_cap, uint8_t *sm, df11_rans_header *h);
 

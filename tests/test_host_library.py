@@ -216,6 +216,8 @@ def test_decompress_validation_runs_before_any_launch():
     bad = _lib.DeviceStream.from_buffer_copy(s)
     bad.h.n_elements = 1 << 32
     assert lib.df11_decompress(ctypes.byref(bad), out, None) == -7
+    bad.h.n_elements = _lib.MAX_ELEMENTS + 1
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -7
     # output aliasing an input
     assert lib.df11_decompress(ctypes.byref(s), ctypes.c_void_p(s.sm), None) == -1
     # misaligned output
@@ -482,6 +484,8 @@ def test_rans_decompress_validation_runs_before_any_launch():
     bad = _lib.RansDeviceStream.from_buffer_copy(s)
     bad.h.n_elements = 1 << 32
     assert call(bad) == -7
+    bad.h.n_elements = _lib.MAX_ELEMENTS + 1
+    assert call(bad) == -7
     bad = _lib.RansDeviceStream.from_buffer_copy(s)
     bad.words = (1 << 40) + 8  # not 16-byte aligned
     assert call(bad) == -1
@@ -550,3 +554,24 @@ def test_committed_profiles_match_the_kernel_sources():
                     ("df11_rans_decode_kernel_llama3_8b_block_counters.md", "df11_rans_decode.hip")):
         with open(os.path.join(REPO, "profiles", md)) as f:
             assert prefix(src) in f.read(), md
+
+
+def test_element_limit_of_a_stream():
+    """A stream holds at most DF11_MAX_ELEMENTS = 2^32 - 2^16 elements: the
+    planner accepts that many (sizes only, no data) and rejects one more,
+    and the header mirrors the same limit."""
+    lib = _lib_or_skip()
+    with open(os.path.join(REPO, "include", "df11.h")) as f:
+        m = re.search(r"#define DF11_MAX_ELEMENTS (\d+)ull", f.read())
+    assert m and int(m.group(1)) == _lib.MAX_ELEMENTS == (1 << 32) - (1 << 16)
+    for n, rc in ((_lib.MAX_ELEMENTS, 0), (_lib.MAX_ELEMENTS + 1, -7), (1 << 32, -7)):
+        hist = np.zeros(256, dtype=np.uint64)
+        hist[127], hist[126] = n - n // 3, n // 3
+        cb = df11.build_codebook(hist)
+        h = _lib.Header()
+        lay = _lib.Layout(8, 256)
+        got = lib.df11_plan(ctypes.byref(cb), hist.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n,
+                            ctypes.byref(lay), ctypes.byref(h))
+        assert got == rc, n
+        if rc == 0:
+            assert h.n_elements == n and h.sm_bytes == -(-n // 64) * 64
