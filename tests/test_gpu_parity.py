@@ -769,3 +769,25 @@ def test_linear_lm_head_full_size(torch_cuda):
     ref = oracle.linear(oracle.encode(w), x, out_f)
     assert np.all(np.abs(got - ref) <= _linear_bound(x, w, out_f, in_f))
     assert not np.array_equal(got[0], got[1])
+
+
+@pytest.mark.timeout(600)
+def test_largest_stream(torch_cuda):
+    """The largest stream the library takes, DF11_MAX_ELEMENTS = 2^32 - 2^16
+    weights (the block workload's weights repeated; 8.6 GB of BF16): output
+    indices up to the 32-bit limit decode to the original bits."""
+    torch = torch_cuda
+    from entropy_decoding_df11_amd import _lib
+    n = _lib.MAX_ELEMENTS
+    w = np.resize(workloads.gen_block(seed=3)[0], n)
+    _note(f"largest stream n={n}")
+    t = df11.compress(w, shape=(n,), decode_table_bits=11)
+    assert t.header.n_elements == n
+    ref = torch.from_numpy(w.view(np.int16)).to("cuda")
+    tail = w[-100003:].copy()
+    del w
+    out = torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda")
+    t.decompress(out=out.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert np.array_equal(out[-100003:].cpu().numpy().view(np.uint16), tail)
