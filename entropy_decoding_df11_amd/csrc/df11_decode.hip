@@ -1125,17 +1125,38 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, uint32_t max_wg, hipStream_t str
     }
 }
 
-// Split the resident grid between the streams of a batch in proportion to
-// their super-groups (at least one workgroup each, at most one per
-// super-group) and launch once.
+// Workgroups per stream of a batch, from each stream's super-groups sup[i]
+// and the resident workgroup count.  A batched launch ends with its slowest
+// stream, so the shares minimise the largest number of super-groups per
+// workgroup: each stream's proportional share rounded down (at least one,
+// at most one per super-group), then the workgroups left over one at a time
+// to the stream with the most super-groups per workgroup (D'Hondt's method,
+// which never gives a stream less than its share rounded down).  Rounding
+// down alone left a small stream up to a workgroup short: 5% more work per
+// workgroup for a stream of 15.
+void split_grid(const uint64_t *sup, uint32_t n, uint64_t resident, uint64_t *want) {
+    uint64_t total = 0, given = 0;
+    for (uint32_t i = 0; i < n; ++i) total += sup[i];
+    for (uint32_t i = 0; i < n; ++i) {
+        want[i] = std::min(sup[i], std::max<uint64_t>(1, resident * sup[i] / total));
+        given += want[i];
+    }
+    while (given < resident) {
+        uint32_t best = n;
+        for (uint32_t i = 0; i < n; ++i)
+            if (want[i] < sup[i] && (best == n || sup[i] * want[best] > sup[best] * want[i])) best = i;
+        if (best == n) break;
+        ++want[best];
+        ++given;
+    }
+}
+
+// Split the resident grid between the streams of a batch (split_grid) and
+// launch once.
 template <int K, int GPW>
 int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     size_t lds = 0;
-    uint64_t total_super = 0;
-    for (uint32_t i = 0; i < b.n; ++i) {
-        lds = std::max(lds, dynamic_lds<GPW>(b.s[i]));
-        total_super += (b.s[i].n_groups + GPW - 1) / GPW;
-    }
+    for (uint32_t i = 0; i < b.n; ++i) lds = std::max(lds, dynamic_lds<GPW>(b.s[i]));
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>);
@@ -1143,10 +1164,12 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t s
     if (per_cu < 1) return DF11_E_HIP;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
+    uint64_t sup[kMaxBatch], want[kMaxBatch];
+    for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + GPW - 1) / GPW;
+    split_grid(sup, b.n, resident, want);
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
-        const uint64_t n_super = (b.s[i].n_groups + GPW - 1) / GPW;
-        const uint32_t share = schedule_pools(b.s[i], n_super, resident * n_super / total_super);
+        const uint32_t share = schedule_pools(b.s[i], sup[i], want[i]);
         b.wg_begin[i] = next;
         next += share;
     }
@@ -1394,16 +1417,13 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
 }
 
 // Zero every output, then the batched fused kernel over the persistent grid
-// split between the streams in proportion to their super-groups.
+// split between the streams (split_grid).
 template <int K, int TB>
 int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
                         hipEvent_t stop, bool zero) {
     size_t lds = 0;
-    uint64_t total_super = 0;
-    for (uint32_t i = 0; i < b.n; ++i) {
+    for (uint32_t i = 0; i < b.n; ++i)
         lds = std::max(lds, dynamic_lds<kLinearGPW>(b.s[i]) + sizeof(float) * kLinearGPW * b.m[i].yacc_rows * TB);
-        total_super += (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
-    }
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_linear_batch_kernel<K, TB>);
@@ -1411,10 +1431,12 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
     if (per_cu < 1) return DF11_E_HIP;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
+    uint64_t sup[kMaxBatch], want[kMaxBatch];
+    for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
+    split_grid(sup, b.n, resident, want);
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
-        const uint64_t n_super = (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
-        const uint32_t share = schedule_pools(b.s[i], n_super, resident * n_super / total_super);
+        const uint32_t share = schedule_pools(b.s[i], sup[i], want[i]);
         b.wg_begin[i] = next;
         next += share;
     }
