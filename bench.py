@@ -2,24 +2,31 @@
 
 One step = one batched decompression of the Llama-3-8B-shaped transformer block
 (q, k, v, o, gate, up, down; one DF11 stream, shared codebook, ~218M BF16
-weights) into one scratch buffer, with the compressed stream already resident
-in HBM.  Prints one JSON line.  --workload picks another input: the same block
+weights) into a scratch buffer, with the compressed stream already resident in
+HBM.  Prints one JSON line.  --workload picks another input: the same block
 with a codebook per weight (seven streams, one batched launch), or a single
 stream (LM-head-sized 128256x4096, the 2^28 stress stream, ...).
 
-  value     = K * (algorithmic bytes per step) / (wall time of K back-to-back
-              launches), GB/s
+  step      = a decode of the next of R device copies of the stream (each with
+              its own output), R chosen so that between two uses of a copy
+              the others move at least 768 MiB: no step finds its data in the
+              L2 or the 256 MB MALL, as in a model that decodes each block
+              once per forward
+  value     = K * (algorithmic bytes per step) / (host wall time of the K
+              timed steps), GB/s
   algorithmic bytes per step = EncodedExponent + PackedSignMantissa + Gaps
               + output positions + LUTs + CodeLengths (all unpadded) read,
               plus 2 bytes per BF16 weight written
-  roofline  = the same bytes / the decode kernel's mean duration over K more
-              launches (a pair of HIP events per launch that the kernel
-              dispatch itself records on its stream, hipExtLaunchKernel)
-              against the 8 TB/s HBM peak;
-              kernel_ms_cold_median times 20 more launches, each after a 1 GiB
-              read that flushes the L2 and the MALL
-  cpu_baseline = the CPU oracle's tree-walk decoder, group-parallel over the
-              host's cores, on the same workload
+  roofline  = the same bytes / (HIP events on the launch stream around the K
+              timed steps / K) against the 8 TB/s HBM peak
+  extras    = hot_kernel_ms (one copy decoded back to back), and
+              flushed_kernel_ms_median (50 launches, each after a 1 GiB read,
+              each between events recorded around it)
+  cpu_baseline = the CPU oracle's tree-walk decoder on the same data, over
+              the stream's groups on the job's share of host cores, and on one
+              core
+Before the W warmup steps the script decodes for SETTLE_S seconds, so that the
+GPU clocks have settled whatever W is.
 """
 
 from __future__ import annotations
@@ -37,7 +44,8 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 HBM_PEAK_GBPS = 8000.0
-COLD_LAUNCHES = 20  # cold-cache launches after the timed ones
+FLUSHED_LAUNCHES = 50  # launches after a 1 GiB read, after the timed ones
+SETTLE_S = 0.15  # seconds of decoding before the warmup steps (GPU clocks)
 DEFAULT_WORKLOAD = "llama3_8b_block"
 WORKLOAD_CHOICES = ["llama3_8b_block", "llama3_8b_block_per_weight", "lm_head_128256x4096", "stress_2p28_zipf",
                     "mlp_14336x4096_t5", "proj_4096x4096_outliers", "single_1024x1024"]
@@ -64,28 +72,64 @@ def _traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(flat: np.ndarray, threads: int):
+# Host threads of the CPU baseline: the GPU machine gives one GPU's job a share
+# of 16 cores, whatever the machine's core count.
+CPU_SHARE = 16
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baselines(flat: np.ndarray, args) -> dict:
+    """The oracle (test infrastructure) timed on the host: its tree-walk
+    decoder over the whole stream on one core, and the same decoder over the
+    stream's independent groups on every core of the job's share.  The rANS
+    oracle has only the one-thread decoder."""
     import oracle
+    usable = len(os.sched_getaffinity(0))
+    cpu = {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": _cpu_model()}
+    if args.coder == "rans":
+        s = oracle.rans_encode(flat)
+        t0 = time.perf_counter()
+        out = oracle.rans_decode(s)
+        dt = time.perf_counter() - t0
+        algo = oracle.rans_compressed_bytes(s) + 2 * s["n_elements"]
+        return {"value": round(algo / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole {args.workload} data as one rANS stream ({flat.size} weights) decoded on one "
+                          f"thread in {dt:.2f} s; output {'matches' if np.array_equal(out, flat) else 'DIFFERS FROM'} "
+                          "the original weights", **cpu}
+    threads = args.cpu_threads or min(usable, CPU_SHARE)
     s = oracle.encode(flat)
+    algo = (s["total_bits"] + 7) // 8 + s["n_elements"] + (5 * s["n_threads"] + 7) // 8 \
+        + 4 * (s["n_groups"] + 1) + 256 * (s["n_luts"] + 1) + 2 * s["n_elements"]
     out = np.zeros_like(flat)
     t0 = time.perf_counter()
     oracle.decode_groups_parallel(s, 0, s["n_groups"], out, threads)
-    dt = time.perf_counter() - t0
-    ok = bool(np.array_equal(out, flat))
-    algo = (s["total_bits"] + 7) // 8 + s["n_elements"] + (5 * s["n_threads"] + 7) // 8 \
-        + 4 * (s["n_groups"] + 1) + 256 * (s["n_luts"] + 1) + 2 * s["n_elements"]
-    return algo / dt / 1e9, dt, ok
-
-
-def _cpu_baseline_rans(flat: np.ndarray):
-    """The oracle's rANS decoder (one host thread) on the whole stream."""
-    import oracle
-    s = oracle.rans_encode(flat)
+    dt_all = time.perf_counter() - t0
+    ok_all = bool(np.array_equal(out, flat))
     t0 = time.perf_counter()
-    out = oracle.rans_decode(s)
-    dt = time.perf_counter() - t0
-    algo = oracle.rans_compressed_bytes(s) + 2 * s["n_elements"]
-    return algo / dt / 1e9, dt, bool(np.array_equal(out, flat))
+    out1 = oracle.decode_treewalk(s)
+    dt_one = time.perf_counter() - t0
+    ok_one = bool(np.array_equal(out1, flat))
+    verdict = lambda ok: "matches" if ok else "DIFFERS FROM"  # noqa: E731
+    return {
+        "value": round(algo / dt_all / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"the whole {args.workload} data as one stream ({flat.size} weights), tree-walk decode split by "
+                  f"groups over {threads} threads (the job's share of the host, {usable} CPUs usable) in "
+                  f"{dt_all:.2f} s; output {verdict(ok_all)} the original weights",
+        "one_core": {"value": round(algo / dt_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                     "sample": f"the same stream, tree-walk decode of every code in order on one thread in "
+                               f"{dt_one:.2f} s; output {verdict(ok_one)} the original weights"},
+        **cpu,
+    }
 
 
 def _read_csv(path):
@@ -106,23 +150,76 @@ def _pmc_per_dispatch(run_dir, counter):
     return per
 
 
-def summarize_profiles(prof_dir: str, commands: dict) -> None:
-    """Turn the rocprofv3 output of one kernel-trace run and two PMC runs of this
-    script into the committed summaries under profiles/.
+def _phase_rows(rows, bench):
+    """Split a kernel's trace rows (in start order) into the bench run's
+    phases, in the order the run launches them (bench["launches"])."""
+    phases, at = {}, 0
+    for name, count in bench["launches"].items():
+        phases[name] = rows[at:at + count]
+        at += count
+    if at != len(rows):
+        raise SystemExit(f"summarize: {len(rows)} launches in the trace, the bench line accounts for {at}")
+    return phases
 
-    prof_dir holds trace/ (--kernel-trace --stats), fetch/ (--pmc FETCH_SIZE),
-    write/ (--pmc WRITE_SIZE) and bench.json (the JSON line of the trace run).
-    FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by the ratio
-    of known bytes to counted bytes of the plain copy kernel the same run
-    launches (10 copies of a buffer of known size)."""
-    stats = _read_csv(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))
-    with open(os.path.join(prof_dir, "bench.json")) as f:
+
+def summarize_decode_trace(prof_dir: str, sub: str, kernel: str, title: str, command: str, out_name: str) -> None:
+    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of this
+    script (prof_dir/sub, its bench line in prof_dir/sub.json): the stats
+    table, then the kernel's launches split into the run's phases, each
+    phase's average duration from the trace timestamps against the bench
+    line's own event timing of that phase."""
+    with open(os.path.join(prof_dir, sub + ".json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
-    trace = [r for r in _read_csv(os.path.join(prof_dir, "trace", "run_kernel_trace.csv"))
-             if "df11_decode" in r["Kernel_Name"]]
-    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    timed = trace[-(bench["steps"] + COLD_LAUNCHES):-COLD_LAUNCHES]
-    timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    stats = _read_csv(os.path.join(prof_dir, sub, "run_kernel_stats.csv"))
+    rows = [r for r in _read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv")) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    phases = _phase_rows(rows, bench)
+    algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
+    us = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]  # noqa: E731
+    lines = [f"# {title}: rocprofv3 kernel trace", "",
+             "Command (from the repository root on a one-GPU MI355X box; R = repository root, "
+             "D = R/gpurun_out/prof):", "", "    " + command, "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:6]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
+    bench_us = {"timed": bench["kernel_ms"] * 1e3, "hot": bench["hot_kernel_ms"] * 1e3,
+                "flushed": bench["flushed_kernel_ms_median"] * 1e3}
+    lines += ["", f"The {kernel} launches of the run, by phase (trace timestamps; {algo} algorithmic bytes per "
+              "launch).  The bench line times the timed and hot phases with HIP events around all of their "
+              "launches (gaps between launches included) and the flushed phase with events around each launch "
+              "(median):", "",
+              "| phase | launches | trace average us | trace median us | min us | max us | GB/s (trace average) "
+              "| of 8 TB/s | bench line us | trace / bench |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, rs in phases.items():
+        if not rs:
+            continue
+        v = us(rs)
+        avg = float(np.mean(v))
+        b = bench_us.get(name)
+        lines.append(f"| {name} | {len(v)} | {avg:.2f} | {float(np.median(v)):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{algo / (avg * 1e-6) / 1e9:.1f} | {algo / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} | "
+                     + (f"{b:.2f} | {avg / b:.3f} |" if b else "| |"))
+    t = us(phases["timed"])
+    lines += ["", f"Roofline basis (timed phase: every launch decodes the next of "
+              f"{bench['rotation_copies']} copies, so none finds its data cached): trace average "
+              f"{np.mean(t):.2f} us against the bench line's {bench_us['timed']:.2f} us, "
+              f"frac {algo / (np.mean(t) * 1e-6) / 1e9 / HBM_PEAK_GBPS:.4f} from the trace against "
+              f"{bench['roofline']['frac']:.4f} on the bench line.", "",
+              "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+    with open(os.path.join(REPO, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines))
+
+
+def summarize_traffic(prof_dir: str, commands: dict) -> None:
+    """The HBM-traffic summary from two PMC runs of this script (prof_dir/fetch
+    with --pmc FETCH_SIZE, prof_dir/write with --pmc WRITE_SIZE; the bench
+    line of the fetch run in prof_dir/fetch.json).  FETCH_SIZE and WRITE_SIZE
+    are KiB per dispatch; each is scaled by the ratio of known bytes to
+    counted bytes of the plain copy kernel the same run launches (10 copies of
+    a buffer of known size).  The median over the decode dispatches."""
+    with open(os.path.join(prof_dir, "fetch.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
     algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
     copy_bytes = algo // 2
 
@@ -135,34 +232,11 @@ def summarize_profiles(prof_dir: str, commands: dict) -> None:
     write_dec, write_cpy = split(_pmc_per_dispatch(os.path.join(prof_dir, "write"), "WRITE_SIZE"))
     if not (fetch_dec and fetch_cpy and write_dec and write_cpy):
         raise SystemExit("summarize: decode or copy dispatches missing from the PMC runs")
-    kib = lambda xs: float(np.median(xs))
+    kib = lambda xs: float(np.median(xs))  # noqa: E731
     fetch_scale = copy_bytes / (kib(fetch_cpy) * 1024)
     write_scale = copy_bytes / (kib(write_cpy) * 1024)
     read_b = kib(fetch_dec) * 1024 * fetch_scale
     write_b = kib(write_dec) * 1024 * write_scale
-
-    dec_row = [r for r in stats if "df11_decode" in r["Name"]]
-    lines = ["# df11_decode_kernel on llama3_8b_block: rocprofv3 kernel trace", "",
-             "Command (from the repository root on a one-GPU MI355X box):", "",
-             "    " + commands["trace"], "",
-             "| kernel | calls | average us | min us | max us | share of GPU time |",
-             "|---|---|---|---|---|---|"]
-    for r in stats[:6]:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
-    avg_all = float(dec_row[0]["AverageNs"]) / 1e3
-    avg_us = float(np.mean(timed_us))
-    lines += ["", f"The table averages every decode launch of the run, warmup included ({avg_all:.2f} us).  "
-              f"Over the {len(timed_us)} timed launches (those before the last {COLD_LAUNCHES}, which run after a "
-              f"cache flush) the decode kernel averages "
-              f"{avg_us:.2f} us (min {min(timed_us):.2f}, max {max(timed_us):.2f}) for {algo} algorithmic bytes: "
-              f"{algo / (avg_us * 1e-6) / 1e9:.1f} GB/s, {algo / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s.  "
-              f"The same run's bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with the events "
-              f"that the kernel dispatch records (df11_decompress_timed).", "",
-             "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
-    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
-    with open(os.path.join(os.path.dirname(PMC_SUMMARY), "df11_decode_kernel_llama3_8b_block_trace.md"), "w") as f:
-        f.write("\n".join(lines))
     pmc = {
         "kernel": "df11_decode_kernel",
         "workload": "llama3_8b_block",
@@ -226,37 +300,6 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
               f"({comp / (total * 1e-6) / 1e9:.0f} GB/s of compressed weights).", "",
               "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
     with open(os.path.join(REPO, "profiles", f"df11_linear_kernel_llama3_8b_block_t{T}_trace.md"), "w") as f:
-        f.write("\n".join(lines))
-
-
-def summarize_kernel_trace(prof_dir: str, sub: str, kernel: str, title: str, command: str, out_name: str) -> None:
-    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of this
-    script (prof_dir/sub, its bench line in prof_dir/sub.json): the stats
-    table and the kernel's average over the run's timed launches (the
-    `steps` launches of `kernel` before the cold-cache ones) against the
-    bench line's event timing."""
-    with open(os.path.join(prof_dir, sub + ".json")) as f:
-        bench = json.loads(f.read().strip().splitlines()[-1])
-    stats = _read_csv(os.path.join(prof_dir, sub, "run_kernel_stats.csv"))
-    rows = [r for r in _read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv")) if kernel in r["Kernel_Name"]]
-    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    timed = rows[-(bench["steps"] + COLD_LAUNCHES):-COLD_LAUNCHES]
-    timed_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
-    algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
-    avg = float(np.mean(timed_us))
-    lines = [f"# {title}: rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box):",
-             "", "    " + command, "", "| kernel | calls | average us | min us | max us | share of GPU time |",
-             "|---|---|---|---|---|---|"]
-    for r in stats[:6]:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
-    lines += ["", f"Over the {len(timed_us)} timed launches (those before the last {COLD_LAUNCHES}, which run "
-              f"after a cache flush) the kernel averages "
-              f"{avg:.2f} us (min {min(timed_us):.2f}, max {max(timed_us):.2f}) for {algo} algorithmic bytes: "
-              f"{algo / (avg * 1e-6) / 1e9:.1f} GB/s, {algo / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s.  "
-              f"The bench line measured {bench['kernel_ms_mean'] * 1e3:.2f} us per launch with the events that "
-              f"the kernel dispatch records.", "", "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
-    with open(os.path.join(REPO, "profiles", out_name), "w") as f:
         f.write("\n".join(lines))
 
 
@@ -637,26 +680,29 @@ def main() -> int:
     if args.summarize_profiles:
         pre = "cd /tmp && export TMPDIR=/tmp && "   # R = repository root, D = R/gpurun_out/prof
         have = lambda sub: os.path.isdir(os.path.join(args.summarize_profiles, sub))
+        trace = pre + "rocprofv3 --kernel-trace --stats -d $D/{sub} -o run --output-format csv -- python3 " \
+                      "$R/bench.py {args} > $D/{sub}.json"
         if have("trace"):
-            summarize_profiles(args.summarize_profiles, {
-                "trace": pre + "rocprofv3 --kernel-trace --stats -d $D/trace -o run --output-format csv "
-                               "-- python3 $R/bench.py --steps 100 --warmup 300 --no-cpu-baseline > $D/bench.json",
-                "fetch": pre + "rocprofv3 --pmc FETCH_SIZE -d $D/fetch -o run --output-format csv "
-                               "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-                "write": pre + "rocprofv3 --pmc WRITE_SIZE -d $D/write -o run --output-format csv "
-                               "-- python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-            })
+            summarize_decode_trace(args.summarize_profiles, "trace", "df11_decode_kernel",
+                                   "df11_decode_kernel on llama3_8b_block",
+                                   trace.format(sub="trace", args="--gpus 1 --steps 20 --warmup 5"),
+                                   "df11_decode_kernel_llama3_8b_block_trace.md")
+        if have("fetch") and have("write"):
+            pmc = pre + "rocprofv3 --pmc {c} -d $D/{sub} -o run --output-format csv -- python3 $R/bench.py " \
+                        "--steps 3 --warmup 2 --no-cpu-baseline"
+            summarize_traffic(args.summarize_profiles, {
+                "fetch": pmc.format(c="FETCH_SIZE", sub="fetch") + " > $D/fetch.json",
+                "write": pmc.format(c="WRITE_SIZE", sub="write")})
         if have("lin_trace"):
             summarize_linear_profile(args.summarize_profiles,
                                      pre + "rocprofv3 --kernel-trace --stats -d $D/lin_trace -o run --output-format csv "
                                            "-- python3 $R/bench.py --linear-tokens 1 --steps 50 --warmup 20 "
                                            "--no-cpu-baseline > $D/lin.json")
         if have("rans_trace"):
-            summarize_kernel_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
+            summarize_decode_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
                                    "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
-                                   pre + "rocprofv3 --kernel-trace --stats -d $D/rans_trace -o run --output-format csv "
-                                         "-- python3 $R/bench.py --coder rans --steps 100 --warmup 300 "
-                                         "--no-cpu-baseline > $D/rans_trace.json",
+                                   trace.format(sub="rans_trace", args="--coder rans --steps 20 --warmup 5 "
+                                                                      "--no-cpu-baseline"),
                                    "df11_rans_decode_kernel_llama3_8b_block_trace.md")
         counter_runs = [("df11_decode_kernel", "df11_decode_kernel on llama3_8b_block",
                          "--steps 3 --warmup 2 --no-cpu-baseline", "entropy_decoding_df11_amd/csrc/df11_decode.hip",
@@ -699,99 +745,131 @@ def main() -> int:
         if wl.endswith("_per_weight"):
             print("bench: the rANS coder takes the block as one stream (llama3_8b_block)", file=sys.stderr)
             return 2
-        t = df11.rans_compress(flat, shape=(n,), device=dev)
-        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
-        h, comp = t.header, t.compressed_bytes()
+        first = df11.rans_compress(flat, shape=(n,), device=dev)
+        h, comp = first.header, first.compressed_bytes()
         config["coder"] = "rans"
         config["rans"] = {"prob_bits": int(h.prob_bits), "lanes": int(h.lanes), "steps": int(h.steps),
                           "segments": int(h.n_segments), "words": int(h.n_words)}
-        decode = lambda ev=None: t.decompress(out=out, events=ev)  # noqa: E731
-        decoded = lambda: out.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+        out_elems = n
     elif views is not None:
         codebook = "per_weight" if wl.endswith("_per_weight") else "shared"
-        blk = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views], device=dev,
-                                  decode_table_bits=args.decode_table_bits, codebook=codebook)
-        scratch = torch.empty(blk.n_elements, dtype=torch.bfloat16, device=dev)
+        first = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views], device=dev,
+                                    decode_table_bits=args.decode_table_bits, codebook=codebook)
         config["shapes"] = {name: list(shape) for name, _, shape in views}
         config["codebook"] = codebook
         if codebook == "shared":
-            h, comp = blk.tensor.header, blk.tensor.compressed_bytes()
-            decode = lambda ev=None: blk.decompress(scratch=scratch, events=ev)  # noqa: E731
+            h, comp = first.tensor.header, first.tensor.compressed_bytes()
         else:
-            h, comp = blk.tensors[0].header, blk.compressed_bytes()
-            config["streams"] = len(blk.tensors)
-            decode = lambda ev=None: blk.decompress(scratch=scratch, events=ev)  # noqa: E731
-
-        def decoded():
-            if codebook == "shared":
-                return scratch[:n].view(torch.int16).cpu().numpy().view(np.uint16)
-            outs = blk.decompress(scratch=scratch)  # cached views; decodes once more
-            torch.cuda.synchronize()
-            return np.concatenate([outs[nm].reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
-                                   for nm, _, _ in views])
+            h, comp = first.tensors[0].header, first.compressed_bytes()
+            config["streams"] = len(first.tensors)
+        out_elems = first.n_elements
     else:
-        t = df11.compress(flat, shape=(n,), device=dev, decode_table_bits=args.decode_table_bits)
-        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
-        h, comp = t.header, t.compressed_bytes()
-        decode = lambda ev=None: t.decompress(out=out, events=ev)  # noqa: E731
-        decoded = lambda: out.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+        first = df11.compress(flat, shape=(n,), device=dev, decode_table_bits=args.decode_table_bits)
+        h, comp = first.header, first.compressed_bytes()
+        out_elems = n
     t_enc = time.perf_counter() - t0
     algo_bytes = comp + 2 * n
 
-    # Check the decode first: the copy back and the comparison leave the GPU
-    # idle long enough for its clocks to drop, which the warmup then undoes.
-    decode()
+    # Copies of the compressed stream in other device buffers, each with an
+    # output of its own.  Step i decodes copy i mod R; between two uses of a
+    # copy the others move at least 768 MiB (three times the 256 MB MALL), so
+    # every step finds its stream and output in neither the L2 nor the MALL,
+    # as a model that decodes each block once per forward does.
+    rotate = min(256, 1 + -(-(768 << 20) // algo_bytes))
+    copies = [first] + [first.clone() for _ in range(rotate - 1)]
+    outs = [torch.empty(out_elems, dtype=torch.bfloat16, device=dev) for _ in copies]
+
+    def decoder(obj, out):
+        if args.coder == "rans" or views is None:
+            return lambda: obj.decompress(out=out)
+        return lambda: obj.decompress(scratch=out)
+
+    decoders = [decoder(c, o) for c, o in zip(copies, outs)]
+    # The first launch of every copy; a block's decode returns its per-weight
+    # views, which follow the original data's order.
+    firsts = [d() for d in decoders]
+    parts = [[v.reshape(-1) for v in f.values()] if isinstance(f, dict) else [f.reshape(-1)] for f in firsts]
     torch.cuda.synchronize()
-    if not np.array_equal(decoded(), flat):
+
+    def check(i):
+        got = torch.cat(parts[i]).view(torch.int16).cpu().numpy().view(np.uint16)
+        return np.array_equal(got, flat)
+
+    if not all(check(i) for i in range(rotate)):
         print(f"bench: decoded {wl} differs from the original weights", file=sys.stderr)
         return 1
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + ends:  # create the events outside the timed region
-        e.record(stream)
-    for _ in range(args.warmup):
-        decode()
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # The GPU's clocks need some tens of milliseconds of sustained load to
+    # settle (the first ~60 block launches run 5-15% slow): before the
+    # warmup steps, decode for SETTLE_S seconds, so that the measurement is
+    # the steady state whatever the warmup count.
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(rotate):
+            decoders[settle % rotate]()
+            settle += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        decoders[i % rotate]()
     torch.cuda.synchronize()
-    # Whole-job time: back-to-back launches as an application issues them.
+
+    # Timed steps: K launches over the rotating copies, bracketed by a pair
+    # of HIP events on the launch stream (the kernel time per launch, gaps
+    # between launches included) and by the host clock (the whole-job time).
+    e0, e1 = ev(), ev()
     wall0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        decode()
+        decoders[i % rotate]()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    # Kernel time: the same launches again, each recording its kernel's own
-    # start and end (dispatch events; recording them widens the gap between
-    # launches by ~4.5 us, so the wall time above is taken without them).
-    # The check of the output comes after both: the copy to the host idles
-    # the GPU long enough for its clocks to drop.
-    for i in range(args.steps):
-        decode((starts[i], ends[i]))
-    torch.cuda.synchronize()
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    if not np.array_equal(decoded(), flat):
-        print(f"bench: the timed launches decoded {wl} wrongly", file=sys.stderr)
-        return 1
-    mean_ms = float(np.mean(kern_ms))
-    achieved = algo_bytes / (mean_ms * 1e-3) / 1e9
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
     value = args.steps * algo_bytes / wall / 1e9
 
-    # Cold caches: COLD_LAUNCHES more launches, each after reading 1 GiB so that neither
-    # the L2 nor the 256 MB MALL holds the stream (outside the timed launch;
-    # the hot numbers above come from back-to-back launches).  The flush reads
-    # rather than writes: written lines would be dirty, and the timed launch
-    # would pay for writing them back.
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(COLD_LAUNCHES)]
-    sink = torch.empty((), dtype=torch.float32, device=dev)
-    for ev in cold_ev:
-        torch.sum(flush, dim=0, out=sink)
-        decode(ev)
+    # Hot caches, for comparison: the same copy decoded back to back, so
+    # whatever of it the L2 and the MALL keep serves the next launch.
+    for _ in range(5):
+        decoders[0]()
+    h0, h1 = ev(), ev()
+    h0.record(stream)
+    for _ in range(args.steps):
+        decoders[0]()
+    h1.record(stream)
     torch.cuda.synchronize()
-    cold_ms = float(np.median([a.elapsed_time(b) for a, b in cold_ev]))
+    hot_ms = h0.elapsed_time(h1) / args.steps
+
+    # The flushed-cache recipe: FLUSHED_LAUNCHES launches, each after reading
+    # 1 GiB (so that neither the L2 nor the MALL holds the stream), each
+    # timed by events recorded around it (so the time includes the launch's
+    # dispatch); the median.  The flush reads rather than writes: written
+    # lines would be dirty, and the timed launch would pay for their write-back.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    flushed = [(ev(), ev()) for _ in range(FLUSHED_LAUNCHES)]
+    for a, b in flushed:
+        torch.sum(flush, dim=0, out=sink)
+        a.record(stream)
+        decoders[0]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    flushed_ms = float(np.median([a.elapsed_time(b) for a, b in flushed]))
     del flush
-    if not np.array_equal(decoded(), flat):
-        print(f"bench: the cold-cache launches decoded {wl} wrongly", file=sys.stderr)
+
+    # Verification round: every output overwritten with a pattern, one more
+    # rotation of launches, every copy compared with the original weights.
+    for o in outs:
+        o.view(torch.int16).fill_(0x5A5A)
+    for d in decoders:
+        d()
+    torch.cuda.synchronize()
+    if not all(check(i) for i in range(rotate)):
+        print(f"bench: the repeated launches decoded {wl} wrongly", file=sys.stderr)
         return 1
 
     # A plain copy kernel over the same byte count, as the achievable-bandwidth reference.
@@ -799,7 +877,7 @@ def main() -> int:
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = ev(), ev()
     c0.record(stream)
     for _ in range(10):
         dst.copy_(src)
@@ -809,6 +887,7 @@ def main() -> int:
     del src, dst
 
     traffic = _traffic_from_profile() if wl == DEFAULT_WORKLOAD and args.coder == "huffman" else None
+    gbps = lambda ms: round(algo_bytes / (ms * 1e-3) / 1e9, 1)  # noqa: E731
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -816,7 +895,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -838,33 +917,26 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
         },
-        "kernel_ms_mean": round(mean_ms, 5),
-        "kernel_ms_min": round(float(np.min(kern_ms)), 5),
-        "kernel_ms_cold_median": round(cold_ms, 5),
-        "cache": "kernel_ms_mean and roofline: back-to-back launches (hot caches; a stream larger than the "
-                 "256 MB MALL is read from HBM anyway); kernel_ms_cold_median: after reading 1 GiB",
+        "kernel_ms": round(kern_ms, 5),
+        "cache": f"value and roofline: each step decodes the next of {rotate} copies of the stream (each with its "
+                 "own output), so no step finds its data in the L2 or the 256 MB MALL; kernel_ms = HIP events "
+                 "around the timed steps / steps (launch gaps included)",
+        "hot_kernel_ms": round(hot_ms, 5),
+        "hot": f"one copy decoded back to back ({args.steps} launches, events around them): whatever of the "
+               f"stream the caches keep serves the next launch; {gbps(hot_ms)} GB/s",
+        "flushed_kernel_ms_median": round(flushed_ms, 5),
+        "flushed": f"median of {FLUSHED_LAUNCHES} launches, each after a 1 GiB read and between events recorded "
+                   f"around it (its dispatch included); {gbps(flushed_ms)} GB/s",
+        "launches": {"check": rotate, "settle": settle, "warmup": args.warmup, "timed": args.steps,
+                     "hot": args.steps + 5, "flushed": FLUSHED_LAUNCHES, "verify": rotate},
+        "rotation_copies": rotate,
         "copy_kernel_GBps": round(copy_gbps, 1),
         "frac_of_copy": round(achieved / copy_gbps, 4),
         "host_gen_s": round(t_gen, 2),
         "host_encode_s": round(t_enc, 2),
     }
     if not args.no_cpu_baseline:
-        threads = args.cpu_threads or len(os.sched_getaffinity(0))
-        threads = min(threads, 16)
-        if args.coder == "rans":
-            cpu_gbps, cpu_s, ok = _cpu_baseline_rans(flat)
-            threads, how = 1, "rANS decode on one thread"
-        else:
-            cpu_gbps, cpu_s, ok = _cpu_baseline(flat, threads)
-            how = f"tree-walk decode split by groups over {threads} threads"
-        result["cpu_baseline"] = {
-            "value": round(cpu_gbps, 3),
-            "unit": "GB/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": f"the whole {wl} data as one stream ({n} weights), {how}; {cpu_s:.2f} s wall; output "
-                      f"{'matches' if ok else 'DIFFERS FROM'} the original weights",
-        }
+        result["cpu_baseline"] = _cpu_baselines(flat, args)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -76,5 +76,44 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host code of the sanitizer build: AddressSanitizer and UndefinedBehaviorSanitizer,
+# every report fatal.  Each flag goes to the host compilation only.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that a process loading the
+    sanitizer build must preload."""
+    import glob
+    found = sorted(glob.glob(os.path.join(ROCM, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("the clang AddressSanitizer runtime is not installed")
+    return found[-1]
+
+
+def build_sanitized(out_path: str, verbose: bool = False) -> str:
+    """Build the whole library with the host code (the codec, the argument
+    checks and launch arithmetic of the device entry points) under
+    AddressSanitizer and UndefinedBehaviorSanitizer, for CPU tests; the
+    gfx950 code objects are built as usual.  A process that loads it needs
+    asan_runtime() preloaded."""
+    work = os.path.join(BUILD_DIR, "sanitized")
+    os.makedirs(work, exist_ok=True)
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    objs = []
+    for src in ("df11_host.cpp", "df11_rans_host.cpp", "df11_decode.hip", "df11_rans_decode.hip"):
+        obj = os.path.join(work, src.split(".")[0] + ".o")
+        lang = [] if src.endswith(".hip") else ["-x", "hip"]
+        _run([hipcc, *HIP_FLAGS, *SAN_HOST, "-O1", f"-I{INCLUDE}", f"-I{CSRC}", *lang, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    rpaths = [p for p in (_torch_lib_dir(), os.path.join(ROCM, "lib")) if p]
+    _run([hipcc, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-shared-libasan", *SAN_HOST, "-o", out_path,
+          *objs, *[f"-Wl,-rpath,{p}" for p in rpaths]], verbose)
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

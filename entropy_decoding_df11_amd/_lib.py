@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf11.so")
+# DF11_LIB_PATH names another build of the same library (the sanitizer build
+# of the CPU tests); by default the in-tree libdf11.so.
+LIB_PATH = os.environ.get("DF11_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf11.so")
 
 DF11_OK = 0
 STATUS_NAMES = {

@@ -42,6 +42,7 @@
 #include "df11.h"
 #include "df11_device.h"
 #include "df11_internal.h"
+#include "df11_launch.h"
 
 namespace {
 
@@ -252,7 +253,9 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     const uint32_t c0 = base >> 3;
     const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
     const uint32_t store_base = skip_first ? (base + 7u) & ~7u : base;
-    const uint32_t store_end = whole_last ? (end + 7u) & ~7u : end;
+    // A valid stream always has elements after a group whose last chunk is
+    // written whole; the clamp keeps a corrupt one inside out.
+    const uint32_t store_end = whole_last ? min((end + 7u) & ~7u, a.n_elements) : end;
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
         const uint32_t k = ltid + j * kThreadsPerGroup;
@@ -376,7 +379,7 @@ __device__ __forceinline__ void merge_matmul(const DecodeArgs &a, const MatmulAr
     const uint32_t c0 = base >> 3;
     const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
     const uint32_t lo = skip_first ? (base + 7u) & ~7u : base;
-    const uint32_t hi = whole_last ? (end + 7u) & ~7u : end;
+    const uint32_t hi = whole_last ? min((end + 7u) & ~7u, a.n_elements) : end;  // (as in merge_group)
     row0 = static_cast<uint32_t>(__umul64hi(lo, m.row_magic));
     rows = lo < hi ? min(static_cast<uint32_t>(__umul64hi(hi - 1u, m.row_magic)) - row0 + 1u, m.yacc_rows) : 0u;
     const uint32_t lane = ltid & (kWaveSize - 1), wave = __builtin_amdgcn_readfirstlane(ltid / kWaveSize);
@@ -572,9 +575,7 @@ __device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32
 // every earlier one.  On exit every workgroup counts itself in the done word;
 // the last one zeroes every word for the next launch.  A pool's share of the
 // work is fixed, so P divides the workgroup count (schedule_pools).
-constexpr uint32_t kPools = 8;
-constexpr uint64_t kDynamicMinRounds = 12;
-constexpr uint32_t kMaxPerPool = 96;  // workgroups fetching from one counter
+using df11::kPools;
 constexpr uint32_t kPoolStride = DF11_SCHEDULE_WORDS / (kPools + 1);  // words: one cache line per counter
 
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *sched, uint32_t pool) {
@@ -1060,31 +1061,14 @@ int validate(const df11_device_stream *s) {
     return DF11_OK;
 }
 
-// Workgroup count and pool count for the dynamic schedule of a stream with
-// n_super super-groups given `want` workgroups.  The pools must divide the
-// workgroup count (a pool's share of the work is fixed), and a pool balances
-// only its own workgroups, so the fewest pools that keep every counter within
-// kMaxPerPool workgroups are taken, dropping a few workgroups if no count of
-// kPools or fewer divides theirs.  (The largest divisor gave a batch's small
-// streams pools of two workgroups, which finish late whenever both are slow
-// ones.)  Beyond kPools * kMaxPerPool workgroups the count is rounded down to
-// a multiple of kPools.  Sets a.sched to null when the schedule does not pay
-// (fewer than kDynamicMinRounds rounds).
+// Workgroup count of a stream given `want` workgroups, with its pool count
+// for the dynamic schedule (df11::pool_shape).  Sets a.sched to null when the
+// schedule does not pay.
 uint32_t schedule_pools(DecodeArgs &a, uint64_t n_super, uint64_t want) {
-    uint64_t n_wg = std::max<uint64_t>(1, std::min(want, n_super));
-    uint32_t pools = 0;
-    if (n_wg > static_cast<uint64_t>(kPools) * kMaxPerPool) {
-        n_wg -= n_wg % kPools;
-        pools = kPools;
-    }
-    while (!pools) {  // ends by n_wg = kMaxPerPool at the latest (one pool)
-        for (uint32_t p = 1; p <= kPools && !pools; ++p)
-            if (n_wg % p == 0 && n_wg / p <= kMaxPerPool) pools = p;
-        if (!pools) --n_wg;
-    }
-    a.pools = pools;
-    if (n_super < kDynamicMinRounds * n_wg) a.sched = nullptr;
-    return static_cast<uint32_t>(n_wg);
+    bool dynamic = false;
+    const uint32_t n_wg = df11::pool_shape(n_super, want, &a.pools, &dynamic);
+    if (!dynamic) a.sched = nullptr;
+    return n_wg;
 }
 
 // Dynamic LDS of one stream's workgroup (beyond the static decode table).
@@ -1125,33 +1109,7 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, uint32_t max_wg, hipStream_t str
     }
 }
 
-// Workgroups per stream of a batch, from each stream's super-groups sup[i]
-// and the resident workgroup count.  A batched launch ends with its slowest
-// stream, so the shares minimise the largest number of super-groups per
-// workgroup: each stream's proportional share rounded down (at least one,
-// at most one per super-group), then the workgroups left over one at a time
-// to the stream with the most super-groups per workgroup (D'Hondt's method,
-// which never gives a stream less than its share rounded down).  Rounding
-// down alone left a small stream up to a workgroup short: 5% more work per
-// workgroup for a stream of 15.
-void split_grid(const uint64_t *sup, uint32_t n, uint64_t resident, uint64_t *want) {
-    uint64_t total = 0, given = 0;
-    for (uint32_t i = 0; i < n; ++i) total += sup[i];
-    for (uint32_t i = 0; i < n; ++i) {
-        want[i] = std::min(sup[i], std::max<uint64_t>(1, resident * sup[i] / total));
-        given += want[i];
-    }
-    while (given < resident) {
-        uint32_t best = n;
-        for (uint32_t i = 0; i < n; ++i)
-            if (want[i] < sup[i] && (best == n || sup[i] * want[best] > sup[best] * want[i])) best = i;
-        if (best == n) break;
-        ++want[best];
-        ++given;
-    }
-}
-
-// Split the resident grid between the streams of a batch (split_grid) and
+// Split the resident grid between the streams of a batch (df11::split_grid) and
 // launch once.
 template <int K, int GPW>
 int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -1166,7 +1124,7 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t s
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
     uint64_t sup[kMaxBatch], want[kMaxBatch];
     for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + GPW - 1) / GPW;
-    split_grid(sup, b.n, resident, want);
+    df11::split_grid(sup, b.n, resident, want);
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
         const uint32_t share = schedule_pools(b.s[i], sup[i], want[i]);
@@ -1174,14 +1132,7 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t s
         next += share;
     }
     b.wg_begin[b.n] = next;
-    // A stride near 0.618 of the grid, coprime to it, spreads each stream's
-    // range over the whole grid.
-    b.stride = 1;
-    for (uint32_t c = std::max<uint32_t>(1, static_cast<uint32_t>(next * 0.618)); c < 2 * next + 2; ++c)
-        if (std::gcd(c, next) == 1) {
-            b.stride = c;
-            break;
-        }
+    b.stride = df11::coprime_stride(next);
     (void)hipGetLastError();
     void *params[] = {&b};
     return launch_kernel(fn, dim3(next), dim3(kThreadsPerGroup * GPW), params, lds, stream, start, stop);
@@ -1417,7 +1368,7 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
 }
 
 // Zero every output, then the batched fused kernel over the persistent grid
-// split between the streams (split_grid).
+// split between the streams (df11::split_grid).
 template <int K, int TB>
 int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
                         hipEvent_t stop, bool zero) {
@@ -1433,7 +1384,7 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
     uint64_t sup[kMaxBatch], want[kMaxBatch];
     for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + kLinearGPW - 1) / kLinearGPW;
-    split_grid(sup, b.n, resident, want);
+    df11::split_grid(sup, b.n, resident, want);
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
         const uint32_t share = schedule_pools(b.s[i], sup[i], want[i]);
@@ -1441,12 +1392,7 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
         next += share;
     }
     b.wg_begin[b.n] = next;
-    b.stride = 1;
-    for (uint32_t c = std::max<uint32_t>(1, static_cast<uint32_t>(next * 0.618)); c < 2 * next + 2; ++c)
-        if (std::gcd(c, next) == 1) {
-            b.stride = c;
-            break;
-        }
+    b.stride = df11::coprime_stride(next);
     (void)hipGetLastError();
     const uint32_t total = z.end[z.n - 1];
     void *zparams[] = {&z};
@@ -1530,10 +1476,11 @@ int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream
     return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
 }
 
-int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64_t scratch_elems, void *hip_stream) {
+int df11_decompress_block(const df11_device_stream *s, uint16_t *block_out, uint64_t scratch_elems,
+                          void *hip_stream) {
     if (!s) return DF11_E_INVALID_ARG;
     if (scratch_elems < s->h.n_elements) return DF11_E_BUFFER_TOO_SMALL;
-    return decompress_impl(s, scratch, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
+    return decompress_impl(s, block_out, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);
 }
 
 int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,

@@ -172,10 +172,29 @@ class DF11Tensor:
         # launches).  Launches of one DF11Tensor must not overlap in time.
         self._schedule = torch.zeros(_lib.SCHEDULE_WORDS, dtype=torch.int32, device=self.device)
         s.schedule = self._schedule.data_ptr()
+        self._last_stream = None  # the stream of the latest launch (see _claim)
         self._stream_struct = s
         # The uploads and the counters' zero fill ran on the current stream:
         # finish them, so that a first launch on any stream sees them.
         torch.cuda.current_stream(self.device).synchronize()
+
+    def clone(self) -> "DF11Tensor":
+        """The same stream in new device buffers (same bytes, other addresses)
+        with work counters of its own."""
+        import copy
+        import torch
+        c = copy.copy(self)
+        c._bufs = {name: t.clone() for name, t in self._bufs.items()}
+        c._schedule = torch.zeros_like(self._schedule)
+        s = _lib.DeviceStream.from_buffer_copy(self._stream_struct)
+        for name, t in c._bufs.items():
+            setattr(s, name, t.data_ptr())
+        if self._stream_struct.schedule:
+            s.schedule = c._schedule.data_ptr()
+        c._stream_struct = s
+        c._last_stream = None
+        torch.cuda.current_stream(self.device).synchronize()
+        return c
 
     def set_dynamic_schedule(self, on: bool) -> None:
         """Balance work between workgroups at run time (default) or assign it
@@ -210,6 +229,21 @@ class DF11Tensor:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         return ctypes.c_void_p(st.cuda_stream)
 
+    def _claim(self, stream) -> ctypes.c_void_p:
+        """The HIP stream of a launch of this tensor (torch's current stream
+        by default), ordered after the tensor's previous launch when that one
+        went to another stream: launches of one tensor share its work
+        counters, which a launch leaves at zero only when it has finished,
+        so they must not overlap in time.  (Under graph capture the graph's
+        own dependencies order the launches.)"""
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        last = self._last_stream
+        if last is not None and last.cuda_stream != st.cuda_stream and not torch.cuda.is_current_stream_capturing():
+            st.wait_stream(last)
+        self._last_stream = st
+        return ctypes.c_void_p(st.cuda_stream)
+
     def decompress(self, out: Optional["torch.Tensor"] = None, stream=None, events=None) -> "torch.Tensor":  # noqa: F821
         """Decode into out (a new bf16 tensor of the original shape by default),
         enqueued on stream (torch's current stream by default).  events, a pair
@@ -229,7 +263,7 @@ class DF11Tensor:
 
     def _launch(self, out: "torch.Tensor", stream, events) -> None:  # noqa: F821
         lib = _lib.load()
-        st = self._hip_stream(stream)
+        st = self._claim(stream)
         if events is None:
             _lib.check(lib.df11_decompress(ctypes.byref(self._stream_struct), ctypes.c_void_p(out.data_ptr()), st),
                        "df11_decompress")
@@ -269,7 +303,7 @@ class DF11Tensor:
         if not _on_device(out, self.device):
             raise ValueError("out must be on the weight's device")
         lib = _lib.load()
-        st = self._hip_stream(stream)
+        st = self._claim(stream)
         args = (ctypes.byref(self._stream_struct), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, out_f,
                 ctypes.c_void_p(out.data_ptr()), st)
         if accumulate:
@@ -319,7 +353,7 @@ def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, st
         if not _on_device(y, x.device):
             raise ValueError("every output must be on the weights' device")
     lib = _lib.load()
-    st = tensors[0]._hip_stream(stream)
+    st = [t._claim(stream) for t in tensors][0]
     arr = (_lib.DeviceStream * len(tensors))(*[t._stream_struct for t in tensors])
     out_f = np.array([t.shape[0] for t in tensors], np.uint32)
     ptrs = (ctypes.c_void_p * len(tensors))(*[y.data_ptr() for y in outs])
@@ -384,6 +418,10 @@ class DF11Block:
     def n_elements(self) -> int:
         return self.tensor.n_elements
 
+    def clone(self) -> "DF11Block":
+        """The same block in new device buffers."""
+        return DF11Block(self.tensor.clone(), self.views)
+
     def set_max_workgroups(self, n: int) -> None:
         """Launch at most n workgroups (0: fill the GPU)."""
         self.tensor.set_max_workgroups(n)
@@ -408,7 +446,7 @@ class DF11Block:
         else:
             lib = _lib.load()
             _lib.check(lib.df11_decompress_block(ctypes.byref(t.device_stream()), ctypes.c_void_p(scratch.data_ptr()),
-                                                 scratch.numel(), t._hip_stream(stream)), "df11_decompress_block")
+                                                 scratch.numel(), t._claim(stream)), "df11_decompress_block")
         cached, views = self._view_cache
         if cached is not scratch:  # the views of a scratch buffer are built once
             flat = scratch.reshape(-1)
@@ -435,7 +473,7 @@ def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor
     n = len(tensors)
     arr = (_lib.DeviceStream * max(n, 1))(*[t.device_stream() for t in tensors])
     ptrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
-    st = tensors[0]._hip_stream(stream) if n else ctypes.c_void_p(0)
+    st = [t._claim(stream) for t in tensors][0] if n else ctypes.c_void_p(0)
     lib = _lib.load()
     if events is None:
         _lib.check(lib.df11_decompress_batch(arr, n, ptrs, st), "df11_decompress_batch")
@@ -463,6 +501,10 @@ class DF11BlockBatch:
 
     def compressed_bytes(self) -> int:
         return sum(t.compressed_bytes() for t in self.tensors)
+
+    def clone(self) -> "DF11BlockBatch":
+        """The same streams in new device buffers."""
+        return DF11BlockBatch([t.clone() for t in self.tensors], self.views, self._n)
 
     def set_max_workgroups(self, n: int) -> None:
         """Launch at most n workgroups in total (0: fill the GPU)."""
@@ -632,6 +674,19 @@ class DF11RansTensor:
     @property
     def header(self) -> _lib.RansHeader:
         return self.host_header
+
+    def clone(self) -> "DF11RansTensor":
+        """The same stream in new device buffers."""
+        import copy
+        import torch
+        c = copy.copy(self)
+        c._bufs = {name: t.clone() for name, t in self._bufs.items()}
+        s = _lib.RansDeviceStream.from_buffer_copy(self._stream_struct)
+        for name, t in c._bufs.items():
+            setattr(s, name, t.data_ptr())
+        c._stream_struct = s
+        torch.cuda.current_stream(self.device).synchronize()
+        return c
 
     def compressed_bytes(self) -> int:
         return self._compressed_bytes

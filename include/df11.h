@@ -150,7 +150,11 @@ typedef struct df11_header {
  *   max_workgroups                       launch at most this many workgroups (0: as
  *                                        many as fit on the GPU at once); a smaller
  *                                        grid leaves CUs to kernels running
- *                                        concurrently on other streams */
+ *                                        concurrently on other streams.  A
+ *                                        batched launch takes the smallest cap
+ *                                        of its streams and still gives every
+ *                                        non-empty stream one workgroup, so it
+ *                                        launches at most max(cap, streams). */
 typedef struct df11_device_stream {
     df11_header h;
     const uint8_t *enc;
@@ -186,8 +190,11 @@ int df11_histogram(const uint16_t *bf16, uint64_t n, uint64_t hist[256]);
 int df11_build_codebook(const uint64_t hist[256], df11_codebook *cb);
 
 /* Exact buffer sizes for n elements whose exponent histogram is hist (host).
- * hist must be the histogram of exactly the data that df11_encode will see.
- * Fills every header field; max_group_elems is an upper bound until encode. */
+ * Not on the page: the page fixes what the arrays hold, not how a caller
+ * sizes them; this lets the caller allocate every buffer of df11_encode
+ * before encoding.  hist must be the histogram of exactly the data that
+ * df11_encode will see.  Fills every header field; max_group_elems is an
+ * upper bound until encode. */
 int df11_plan(const df11_codebook *cb, const uint64_t hist[256], uint64_t n, const df11_layout *lay,
               df11_header *h);
 
@@ -204,7 +211,9 @@ int df11_plan(const df11_codebook *cb, const uint64_t hist[256], uint64_t n, con
 int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const df11_layout *lay,
                 df11_header *h, uint8_t *enc, uint8_t *sm, uint8_t *gaps, uint32_t *out_pos);
 
-/* Size in bytes of the decode table for index width bits (10..12), 0 if unsupported. */
+/* Size in bytes of the decode table for index width bits (10..12), 0 if
+ * unsupported.  Not on the page: the decode table is this decoder's own
+ * derived data (see df11_build_decode_table). */
 uint64_t df11_decode_table_bytes(uint32_t bits);
 
 /* Build the GPU decoder's first-level table from the codebook (host).
@@ -438,7 +447,8 @@ int df11_rans_decompress(const df11_rans_device_stream *s, uint16_t *out, void *
 int df11_rans_decompress_timed(const df11_rans_device_stream *s, uint16_t *out, void *hip_stream,
                                void *start_event, void *stop_event);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code.  Not on the page (the page
+ * describes no API); the names are those of enum df11_status. */
 const char *df11_status_str(int status);
 
 #ifdef __cplusplus

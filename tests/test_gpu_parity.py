@@ -247,6 +247,27 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
     t.set_max_workgroups(0)
 
 
+def test_launches_on_two_streams_are_serialised(torch_cuda):
+    """Launches of one tensor share its work counters, so the binding orders
+    a launch after the tensor's previous one when that went to another
+    stream.  Alternating two streams with no synchronisation of the caller's
+    own must leave every output bit-exact and the counters zero."""
+    torch = torch_cuda
+    w = _case("uniform_bits", 64 << 20, 12)
+    _note("two streams, one tensor")
+    t = df11.compress(w, shape=(w.size,), decode_table_bits=11)
+    assert t.header.n_groups >= 2 * 12 * 768  # long enough for the dynamic schedule
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16) for _ in range(4)]
+    torch.cuda.synchronize()  # the fills ran on the default stream
+    for i, o in enumerate(outs):
+        t.decompress(out=o, stream=streams[i % 2])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(_to_u16(o), w)
+    assert not t._schedule.cpu().numpy().any()
+
+
 @pytest.mark.parametrize("bits", [10, 11, 12])
 def test_timed_entry_point_matches(torch_cuda, bits):
     """df11_decompress_timed decodes the same bytes and records the kernel's
