@@ -966,6 +966,7 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(Deco
 // and a stream made only of late ids would run ~20% slower than the rest.
 // The descriptors travel in the kernel arguments.
 constexpr uint32_t kMaxBatch = DF11_MAX_BATCH;
+constexpr uint32_t kZero = 0;
 
 struct BatchArgs {
     DecodeArgs s[kMaxBatch];
@@ -1211,8 +1212,15 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     }
 }
 
+__global__ __launch_bounds__(256) void df11_fill_u32_kernel(uint32_t *p, uint32_t n, uint32_t v) {
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = v;
+}
+
+// counters: when not null, stream i of the call takes its dynamic-schedule
+// counters from counters + i * DF11_SCHEDULE_WORDS (zeroed by a fill kernel
+// launched before the decode) instead of streams[i].schedule.
 int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_t *const *outs,
-                          hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop, uint32_t *counters = nullptr) {
     if (n > kMaxBatch) return DF11_E_TOO_LARGE;
     if (n && (!streams || !outs)) return DF11_E_INVALID_ARG;
     BatchArgs b{};
@@ -1237,7 +1245,11 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
                 return DF11_E_INVALID_ARG;
         }
         if (streams[i].h.n_elements == 0) continue;
-        if (shares_schedule(streams, i)) a.sched = nullptr;
+        if (counters) {
+            a.sched = counters + i * DF11_SCHEDULE_WORDS;
+        } else if (shares_schedule(streams, i)) {
+            a.sched = nullptr;
+        }
         const uint32_t g = streams[i].groups_per_workgroup ? streams[i].groups_per_workgroup
                                                            : kDefaultGroupsPerWorkgroup;
         if (streams[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, streams[i].max_workgroups)
@@ -1251,6 +1263,13 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
         b.s[b.n++] = a;
     }
     if (b.n == 0) return DF11_OK;
+    if (counters) {
+        const uint32_t words = n * DF11_SCHEDULE_WORDS;
+        void *fparams[] = {&counters, const_cast<uint32_t *>(&words), const_cast<uint32_t *>(&kZero)};
+        const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_fill_u32_kernel), dim3(1), dim3(256),
+                                     fparams, 0, stream, nullptr, nullptr);
+        if (rc) return rc;
+    }
     if (b.n == 1) {  // one non-empty stream: the single-stream kernel
         switch (bits) {
         case 10: return launch_k<10>(b.s[0], gpw, max_wg, stream, start, stop);
@@ -1468,9 +1487,47 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
 #undef DF11_LINEAR_BATCH_CASE
 }
 
+// The allocation-free batched decode's work counters: one set of
+// DF11_SCHEDULE_WORDS words per stream of a call, in a file-scope device
+// array that every call on a GPU shares (each GPU holds its own copy until
+// the process ends).  Host code never uses the array's name as an address:
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr uint32_t kNoAllocWords = DF11_MAX_BATCH * DF11_SCHEDULE_WORDS;
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (looked up on the
+// first call on each device, with that device current).
+int scratch_address(uint32_t **ptr) {
+    static std::mutex mu;
+    static uint32_t *per_device[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DF11_E_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DF11_E_HIP;
+        per_device[dev] = static_cast<uint32_t *>(p);
+    }
+    *ptr = per_device[dev];
+    return DF11_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int df11_decompress_batch_noalloc(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
+                                  void *hip_stream) {
+    // (the counters hold n_streams * DF11_SCHEDULE_WORDS words at most kNoAllocWords)
+    if (n_streams > kNoAllocWords / DF11_SCHEDULE_WORDS) return DF11_E_TOO_LARGE;
+    if (n_streams && (!streams || !outs)) return DF11_E_INVALID_ARG;
+    uint32_t *counters = nullptr;
+    const int rc = scratch_address(&counters);
+    if (rc) return rc;
+    return decompress_batch_impl(streams, n_streams, outs, static_cast<hipStream_t>(hip_stream), nullptr, nullptr,
+                                 counters);
+}
 
 int df11_decompress(const df11_device_stream *s, uint16_t *out, void *hip_stream) {
     return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), nullptr, nullptr);

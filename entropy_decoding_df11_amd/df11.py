@@ -483,6 +483,26 @@ def decompress_batch(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor
                "df11_decompress_batch_timed")
 
 
+def decompress_batch_noalloc(tensors: Sequence[DF11Tensor], outs: Sequence["torch.Tensor"],  # noqa: F821
+                             stream=None) -> None:
+    """decompress_batch through df11_decompress_batch_noalloc: the library
+    allocates nothing and uses its own fixed work counters, which every call
+    on a GPU shares (calls must not overlap in time on one GPU)."""
+    import torch
+    if len(tensors) != len(outs):
+        raise ValueError("one output per stream")
+    for t, o in zip(tensors, outs):
+        if o.dtype != torch.bfloat16 or o.numel() != t.n_elements or not o.is_contiguous():
+            raise ValueError("each out must be a contiguous bfloat16 tensor with its stream's element count")
+        if not (_on_device(o, tensors[0].device) and _on_device(o, t.device)):
+            raise ValueError("every stream and output must be on one device")
+    n = len(tensors)
+    arr = (_lib.DeviceStream * max(n, 1))(*[t.device_stream() for t in tensors])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    st = tensors[0]._hip_stream(stream) if n else ctypes.c_void_p(0)
+    _lib.check(_lib.load().df11_decompress_batch_noalloc(arr, n, ptrs, st), "df11_decompress_batch_noalloc")
+
+
 class DF11BlockBatch:
     """Every linear weight of one transformer block as its own DF11 stream
     (a codebook per weight), decoded in one batched launch into one scratch

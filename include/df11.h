@@ -269,6 +269,22 @@ int df11_decompress_block(const df11_device_stream *s, uint16_t *scratch, uint64
 int df11_decompress_batch(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
                           void *hip_stream);
 
+/* df11_decompress_batch for callers that cannot allocate device memory or
+ * own work-counter buffers (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same decode, with each
+ * stream's dynamic-schedule counters taken from a fixed device array inside
+ * the library (DF11_MAX_BATCH sets of DF11_SCHEDULE_WORDS uint32, 9 KB per
+ * GPU, held until the process ends) instead of streams[i].schedule, which is
+ * ignored.  The call allocates nothing: it launches a small kernel that zeroes
+ * the counters of this call's streams, then the decode, both on hip_stream.
+ * Every call on one GPU shares that array, so calls that overlap in time on
+ * one GPU race (serialize them, e.g. on one stream).  Arguments, output and
+ * errors as for df11_decompress_batch; DF11_E_TOO_LARGE for more than
+ * DF11_MAX_BATCH streams, DF11_E_HIP if the array's device address cannot
+ * be found. */
+int df11_decompress_batch_noalloc(const df11_device_stream *streams, uint32_t n_streams, uint16_t *const *outs,
+                                  void *hip_stream);
+
 /* df11_decompress with the decode kernel timed by the GPU: start_event and
  * stop_event (hipEvent_t created by the caller, either may be NULL) are
  * recorded when the kernel itself starts and ends, so hipEventElapsedTime of
