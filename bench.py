@@ -647,6 +647,125 @@ def linear_bench(args, dev) -> int:
     return 0
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def matmul_bench(args, dev) -> int:
+    """One step = y = x W^T for each of the seven Llama-3-8B block matrices
+    (each its own DF11 stream in MFMA tile order) at --matmul-tokens tokens,
+    on the matrix cores with the decode fused in (df11_matmul), compressed
+    weights resident in HBM.  The same run times resident BF16 weights
+    (torch F.linear) and decode-then-F.linear.  The roofline is HBM-bound
+    (compressed bytes + x + y per step over the step time) while the
+    product's arithmetic intensity is under MI355X's flop:byte balance
+    (2.5 PFLOP/s over 8 TB/s), matrix-core-bound (2 T flops per weight
+    against 2.5 PFLOP/s) above it."""
+    import torch
+    import torch.nn.functional as F
+    from entropy_decoding_df11_amd import df11, workloads
+    T = args.matmul_tokens
+    stream = torch.cuda.current_stream(dev)
+    t0 = time.perf_counter()
+    flat, views = workloads.gen_block()
+    mats = []
+    xs = {}
+    for nm, o, (r, c) in views:
+        w = np.ascontiguousarray(flat[o:o + r * c])
+        t = df11.compress(w, shape=(r, c), device=dev, layout="mfma_tiles")
+        wd = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16).reshape(r, c)
+        if c not in xs:
+            rng = np.random.default_rng(c)
+            xb = workloads.f32_to_bf16_bits(rng.standard_normal(T * c) * 0.5).reshape(T, c)
+            xs[c] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((T, r), dtype=torch.float32, device=dev)
+        mats.append((nm, r, c, t, wd, xs[c], y))
+    t_prep = time.perf_counter() - t0
+    n = int(flat.size)
+    del flat
+    comp = sum(m[3].compressed_bytes() for m in mats)
+    hbm_bytes = comp + sum(2 * T * m[2] + 4 * T * m[1] for m in mats)
+    flops = 2.0 * T * n
+
+    def step():
+        for _, _, _, t, _, x, y in mats:
+            t.matmul(x, out=y)
+
+    # Every output against a float64 product of the same BF16 values, within
+    # the float32 summation bound: |y - ref| <= 1.01 * in_features * 2^-24 * sum |x w|.
+    step()
+    torch.cuda.synchronize()
+    for nm, r, c, t, wd, x, y in mats:
+        rows = torch.arange(0, T, max(1, T // 64), device=dev)  # every token up to 64, a sample above
+        xd = x[rows].double()
+        ref = xd @ wd.double().T
+        bound = 1.01 * c * 2.0 ** -24 * (xd.abs() @ wd.double().abs().T)
+        if not bool(((y[rows].double() - ref).abs() <= bound).all()):
+            print(f"bench: matmul of {nm} is outside the float32 bound", file=sys.stderr)
+            return 1
+    del ref, bound, xd
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps, (time.perf_counter() - w0) * 1e3 / reps
+
+    for _ in range(args.warmup):
+        step()
+    fused_ms, wall_ms = timed(step, args.steps)
+    scratch = torch.empty(max(m[1] * m[2] for m in mats), dtype=torch.bfloat16, device=dev)
+    resident_ms, _ = timed(lambda: [F.linear(m[5], m[4]) for m in mats], max(3, args.steps // 2))
+    decode_gemm_ms, _ = timed(lambda: [F.linear(m[5], m[3].decompress(out=scratch[:m[1] * m[2]].view(m[1], m[2])))
+                                       for m in mats], max(3, args.steps // 2))
+    intensity = flops / hbm_bytes
+    compute_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    tflops = flops / (fused_ms * 1e-3) / 1e12
+    gbps = hbm_bytes / (fused_ms * 1e-3) / 1e9
+    roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None} if compute_bound else
+            {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None})
+    result = {
+        "metric": "DF11 decode fused into y = x W^T on the matrix cores: "
+                  + ("TFLOP/s" if compute_bound else "GB/s of compressed weights + x + y"),
+        "value": round(tflops if compute_bound else hbm_bytes / (wall_ms * 1e-3) / 1e9, 2),
+        "unit": "TFLOP/s" if compute_bound else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_block_matmul", "tokens": T,
+                   "shapes": {m[0]: [m[1], m[2]] for m in mats}, "streams": len(mats), "codebook": "per_weight",
+                   "layout": "mfma_tiles", "n_elements": n, "compressed_bytes": comp},
+        "roofline": roof,
+        "kernel_ms": round(fused_ms, 5),
+        "kernel_ms_note": "HIP events around the timed steps / steps: seven products, each a zeroing kernel and "
+                          "the fused kernel",
+        "arithmetic_intensity_flop_per_byte": round(intensity, 2),
+        "achieved_tflops": round(tflops, 2),
+        "achieved_hbm_gbps": round(gbps, 1),
+        "same_run_ms_per_step": {"fused_df11_matmul": round(fused_ms, 4),
+                                 "resident_bf16_F_linear": round(resident_ms, 4),
+                                 "decode_then_F_linear": round(decode_gemm_ms, 4)},
+        "outputs": "within the float32 summation bound of a float64 product (every token up to 64, a sample above)",
+        "host_prep_s": round(t_prep, 1),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -660,6 +779,9 @@ def main() -> int:
                     help="the Llama-3-8B block (default), the same with a codebook per weight (one batched "
                          "launch), or one of the single-stream workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-table", action="store_true",
+                    help="launch with the page's arrays alone: every workgroup derives the first-level decode "
+                         "table in LDS from the LUTs and CodeLengths")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: usable host cores)")
     ap.add_argument("--integration", action="store_true",
                     help="instead of the decode line, time a synthetic model forward over full-size blocks with "
@@ -673,6 +795,10 @@ def main() -> int:
     ap.add_argument("--linear-tokens", type=int, default=0,
                     help="time the decode fused into y = x W^T over the block's seven matrices at this many "
                          "tokens (1..8) instead of the decompression")
+    ap.add_argument("--matmul-tokens", type=int, default=0,
+                    help="time the decode fused into y = x W^T on the matrix cores (weights in MFMA tile order) "
+                         "over the block's seven matrices at this many tokens, against resident BF16 and "
+                         "decode-then-F.linear")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 runs of this script under DIR, then exit")
     args = ap.parse_args()
@@ -731,6 +857,8 @@ def main() -> int:
         return integration(args, dev)
     if args.linear_tokens:
         return linear_bench(args, dev)
+    if args.matmul_tokens:
+        return matmul_bench(args, dev)
     wl = args.workload
     t0 = time.perf_counter()
     if wl.startswith("llama3_8b_block"):
@@ -769,6 +897,10 @@ def main() -> int:
         out_elems = n
     t_enc = time.perf_counter() - t0
     algo_bytes = comp + 2 * n
+    if args.no_decode_table and args.coder == "huffman":
+        for t in ([first] if views is None else [first.tensor] if codebook == "shared" else first.tensors):
+            t.use_decode_table(False)
+        config["decode_table"] = "derived in LDS by every workgroup"
 
     # Copies of the compressed stream in other device buffers, each with an
     # output of its own.  Step i decodes copy i mod R; between two uses of a

@@ -42,6 +42,7 @@ EXPORTED = [
     "df11_build_codebook",
     "df11_plan",
     "df11_encode",
+    "df11_tile_order",
     "df11_decode_table_bytes",
     "df11_build_decode_table",
     "df11_decompress",
@@ -50,6 +51,9 @@ EXPORTED = [
     "df11_decompress_timed",
     "df11_decompress_batch_timed",
     "df11_decompress_batch_noalloc",
+    "df11_matmul",
+    "df11_matmul_acc",
+    "df11_matmul_timed",
     "df11_linear",
     "df11_linear_timed",
     "df11_linear_batch",
@@ -119,7 +123,7 @@ class DeviceStream(ctypes.Structure):
         ("groups_per_workgroup", ctypes.c_uint32),
         ("schedule", ctypes.c_void_p),
         ("max_workgroups", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("tile_cols", ctypes.c_uint32),
     ]
 
 
@@ -188,6 +192,14 @@ def load() -> ctypes.CDLL:
                                                        ctypes.c_void_p, ctypes.c_void_p]),
         "df11_decompress_batch_noalloc": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32,
                                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
+        "df11_tile_order": (ctypes.c_int, [u16p, ctypes.c_uint64, ctypes.c_uint64, u16p]),
+        "df11_matmul": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_matmul_acc": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                           ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_matmul_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
+                                             ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear_acc": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,

@@ -82,11 +82,25 @@ struct DecodeArgs {
     uint32_t ebuf_cap;       // bytes of the LDS exponent buffer, a multiple of 16
     uint32_t last_seg_bits;  // payload bits in the last thread's segment (1..64)
     uint32_t sm_chunks;      // 8-byte chunks in the PackedSignMantissa buffer
-    uint32_t pad;
+    uint32_t tile_cols;      // 0, or the columns C of a matrix held in MFMA tile order
     uint32_t *sched;         // work counters (dynamic schedule) or null
     uint32_t pools;          // dynamic schedule: counters in use, dividing the workgroup count
-    uint32_t pad2;
+    uint32_t tile_ks;        // C / 32: k-steps per 64-row panel of a tiled matrix
+    uint64_t tile_magic;     // floor(2^64 / tile_ks) + 1: umulhi64(i, tile_magic) == i / tile_ks, i < 2^32
 };
+
+// MFMA tile order (df11_tile_order): 512-element blocks, each the operand
+// of one 16 x 16 x 32 bf16 matrix instruction; block b is n-tile b mod 4 of
+// global k-step b / 4, and global k-step g is k-step g mod (C / 32) of the
+// 64-row panel g / (C / 32).  Lane l of a block holds the 8 elements of row
+// 16 nt + (l mod 16), columns 32 ks + 8 (l / 16) .. + 7.  Element index in
+// the row-major matrix of the first element of chunk c (8 elements):
+__device__ __forceinline__ uint32_t tiled_chunk_origin(const DecodeArgs &a, uint32_t c) {
+    const uint32_t l = c & 63u, nt = (c >> 6) & 3u, g = c >> 8;
+    const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
+    const uint32_t ks = g - panel * a.tile_ks;
+    return (64u * panel + 16u * nt + (l & 15u)) * a.tile_cols + 32u * ks + 8u * (l >> 4);
+}
 
 // The fused decode + matmul: y = x W^T, W (out_features x in_features,
 // row-major) being the decoded stream.
@@ -96,8 +110,10 @@ struct MatmulArgs {
     uint64_t row_magic;    // floor(2^64 / in_features) + 1: row of element i = umulhi64(i, row_magic)
     uint32_t in_features;  // a multiple of 8, at least 512
     uint32_t out_features;
-    uint32_t n_tokens;     // 1 .. the kernel's token slots
+    uint32_t n_tokens;     // 1 .. the kernel's token slots (any count for the matrix-core product)
     uint32_t yacc_rows;    // rows of W that one group's outputs can touch
+    uint32_t passes;       // matrix-core product: sweeps of the stream, 16 MT tokens each
+    uint32_t pad;
 };
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
@@ -121,6 +137,91 @@ __device__ __forceinline__ uint32_t walk_luts(uint32_t win, uint32_t ptr, const 
     const uint32_t l = s_clen[v];
     len = l ? l : 32u;
     return v;
+}
+
+// Build the first-level decode table in LDS from the staged LUTs and
+// CodeLengths, for a stream given without one, so that it holds exactly what
+// df11_build_decode_table writes for the same codebook.  Two passes over the
+// 2^K windows, with the bits past a window taken as zero (a code inside the
+// window decodes the same either way, and one that does not cannot fit):
+//   1. s_first[x]: the first code of window x, through the LUT hierarchy:
+//      its rotated exponent and its length, or 0 if it is longer than K;
+//   2. entry x: the code at offset u of window x is the first code of window
+//      (x << u) mod 2^K when it fits in the K - u bits left, so the run of
+//      complete codes is a chain of s_first reads.
+// Each thread takes kPer windows at once, so that their chains of dependent
+// LDS reads overlap.
+template <int K, uint32_t kThreads>
+__device__ __forceinline__ void derive_table(uint32_t *s_tab, uint16_t *s_first, const uint8_t *s_luts,
+                                             const uint8_t *s_clen, uint32_t n_luts, uint32_t tid) {
+    constexpr uint32_t kSize = 1u << K;
+    constexpr uint32_t kPer = (kSize + kThreads - 1) / kThreads;
+    constexpr uint32_t kBatch = kPer < 4 ? kPer : 4;  // windows in flight per thread
+    // Both passes are branch-free (every lookup is made, selects pick the
+    // result), so that the windows' chains of dependent LDS reads overlap.
+    for (uint32_t j0 = 0; j0 < kPer; j0 += kBatch) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (uint32_t j = 0; j < kBatch; ++j) v[j] = s_luts[min(tid + (j0 + j) * kThreads, kSize - 1u) >> (K - 8)];
+#pragma unroll
+        for (uint32_t level = 1; level < 4; ++level) {
+#pragma unroll
+            for (uint32_t j = 0; j < kBatch; ++j) {
+                const uint32_t x = min(tid + (j0 + j) * kThreads, kSize - 1u);
+                const uint32_t byte = ((x << (32 - K)) >> (24 - 8 * level)) & 0xFFu;
+                const bool ptr = v[j] >= DF11_FIRST_POINTER;
+                const uint32_t id = ptr ? min(256u - v[j], n_luts - 1u) : 0u;
+                const uint32_t nv = s_luts[id * 256u + byte];
+                v[j] = ptr ? nv : v[j];
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kBatch; ++j) {
+            const uint32_t x = tid + (j0 + j) * kThreads;
+            const uint32_t len = s_clen[v[j]];
+            if (x < kSize)
+                s_first[x] = static_cast<uint16_t>(len && len <= K ? df11::rotate_exponent(v[j]) | (len << 8) : 0u);
+        }
+    }
+    __syncthreads();
+    uint16_t *s_start = reinterpret_cast<uint16_t *>(s_tab + (2u << K));
+    for (uint32_t j0 = 0; j0 < kPer; j0 += kBatch) {
+        uint32_t used[kBatch], lo[kBatch], fifth[kBatch], mask[kBatch], m[kBatch];
+        bool open[kBatch];
+#pragma unroll
+        for (uint32_t j = 0; j < kBatch; ++j) {
+            used[j] = lo[j] = fifth[j] = mask[j] = m[j] = 0;
+            open[j] = true;
+        }
+#pragma unroll
+        for (uint32_t step = 0; step < df11::kDecodeTableMaxSyms; ++step) {
+#pragma unroll
+            for (uint32_t j = 0; j < kBatch; ++j) {
+                const uint32_t x = min(tid + (j0 + j) * kThreads, kSize - 1u);
+                const uint32_t f = s_first[(x << used[j]) & (kSize - 1u)];
+                const uint32_t len = f >> 8;
+                open[j] = open[j] && len != 0 && len <= K - used[j];
+                const uint32_t r = open[j] ? f & 0xFFu : 0u;
+                if (step < 4) {
+                    lo[j] |= r << (8 * step);
+                } else {
+                    fifth[j] = r;
+                }
+                mask[j] |= open[j] ? 1u << used[j] : 0u;
+                used[j] += open[j] ? len : 0u;
+                m[j] += open[j] ? 1u : 0u;
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kBatch; ++j) {
+            const uint32_t x = tid + (j0 + j) * kThreads;
+            if (x < kSize) {
+                s_tab[2 * x] = lo[j];
+                s_tab[2 * x + 1] = m[j] ? ((m[j] << 11) + used[j]) | (fifth[j] << 16) : df11::kLongCodeIncrement;
+                s_start[x] = static_cast<uint16_t>(m[j] ? mask[j] : 1u);
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
@@ -256,6 +357,15 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     // A valid stream always has elements after a group whose last chunk is
     // written whole; the clamp keeps a corrupt one inside out.
     const uint32_t store_end = whole_last ? min((end + 7u) & ~7u, a.n_elements) : end;
+    // A matrix in MFMA tile order goes back to row-major: each chunk is 8
+    // consecutive elements of one row (tiled_chunk_origin).
+    auto store = [&](uint32_t c, uint4 v) {
+        if (a.tile_cols) {
+            store_chunk_at(a.out, tiled_chunk_origin(a, c), 8u * c, v, store_base, store_end);
+        } else {
+            store_chunk(a.out, c, v, store_base, store_end);
+        }
+    };
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
         const uint32_t k = ltid + j * kThreadsPerGroup;
@@ -263,7 +373,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
             uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
             const uint64_t r8 = *cell;
             *cell = 0;
-            store_chunk(a.out, c0 + k, merge8(sm[j], r8), store_base, store_end);
+            store(c0 + k, merge8(sm[j], r8));
         }
     }
     for (uint32_t k = ltid + kPrefetchChunks * kThreadsPerGroup; k < n_chunks; k += kThreadsPerGroup) {
@@ -271,7 +381,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
         uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
         const uint64_t r8 = *cell;
         *cell = 0;
-        store_chunk(a.out, c0 + k, merge8(s8, r8), store_base, store_end);
+        store(c0 + k, merge8(s8, r8));
     }
     // Codes past the group's last output reach at most 4 bytes into the next chunk.
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
@@ -305,8 +415,10 @@ __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint
     const uint32_t nch = min(group_chunks(base, end), a.ebuf_cap / 8u);
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
-        const uint32_t k = TB == 0 ? ltid + j * kThreadsPerGroup
-                                   : run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch);
+        // (the matrix-core product takes rounds aligned to 256 chunks: mfma_chunk)
+        const uint32_t k = TB == 0  ? ltid + j * kThreadsPerGroup
+                           : TB > 0 ? run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch)
+                                    : ltid + j * kThreadsPerGroup - (c0 & 255u);
         const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
         sm[j] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * c));
     }
@@ -517,6 +629,117 @@ __device__ __forceinline__ void flush_rows(const MatmulArgs &m, float *yacc, uin
     }
 }
 
+// The matrix-core product (y = x W^T, W stored in MFMA tile order; see
+// tiled_chunk_origin).  A group's chunks are taken in rounds of 256 aligned
+// to the blocks: round j holds the chunks 256 (c0 / 256 + j) .. + 255, one
+// per thread, so that wave w, lane l holds lane l of n-tile w of one global
+// k-step, exactly the B operand of a v_mfma_f32_16x16x32_bf16 for the 16
+// rows of that n-tile; chunks outside the group, and elements of its edge
+// chunks outside [base, end), merge as zero (the neighbouring group adds
+// them).  Each wave keeps the running 16 x 16 sums of its n-tile for MT
+// tiles of 16 tokens of the current pass, and adds them into y when its
+// panel or pass changes, or at the end (float atomics: the groups of a panel
+// can lie in several workgroups).  x must hold finite values.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int MT>
+struct PanelSums {
+    floatx4 d[MT];   // lane l, entry r: token 16 mt + 4 (l / 16) + r, row 16 wave + (l mod 16)
+    uint32_t panel;  // 64-row panel of the sums (wave-uniform), ~0 when empty
+    uint32_t pass;   // pass of the sums (wave-uniform)
+};
+
+template <int MT>
+__device__ __forceinline__ void flush_panel(const MatmulArgs &m, PanelSums<MT> &ps, uint32_t wave, uint32_t lane) {
+    if (ps.panel == ~0u) return;
+    const uint32_t row = 64u * ps.panel + 16u * wave + (lane & 15u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t t = (ps.pass * MT + mt) * 16u + 4u * (lane >> 4) + r;
+            if (t < m.n_tokens) unsafeAtomicAdd(m.y + static_cast<size_t>(t) * m.out_features + row, ps.d[mt][r]);
+            ps.d[mt][r] = 0.0f;
+        }
+    }
+    ps.panel = ~0u;
+}
+
+// x operands of one round: token tiles mt of the pass, the 8 columns of the
+// lane at global k-step g (tokens past n_tokens read as zero).
+template <int MT>
+__device__ __forceinline__ void load_xa(const DecodeArgs &a, const MatmulArgs &m, uint32_t g, uint32_t pass,
+                                        uint32_t lane, uint4 (&xa)[MT]) {
+    const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
+    const uint32_t col = 32u * (g - panel * a.tile_ks) + 8u * (lane >> 4);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t t = (pass * MT + mt) * 16u + (lane & 15u);
+        const uint4 v = *reinterpret_cast<const uint4 *>(m.x + static_cast<size_t>(min(t, m.n_tokens - 1u)) *
+                                                                   m.in_features + col);
+        xa[mt] = t < m.n_tokens ? v : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void merge_mfma(const DecodeArgs &a, const MatmulArgs &m, uint8_t *ebuf,
+                                           const uint64_t (&sm)[kPrefetchChunks], uint32_t base, uint32_t end,
+                                           uint32_t pass, uint32_t ltid, PanelSums<MT> &ps) {
+    const uint32_t c0 = base >> 3;
+    const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
+    const uint32_t lead = c0 & 255u;
+    const uint32_t rounds = (lead + n_chunks + 255u) >> 8;
+    const uint32_t lane = ltid & (kWaveSize - 1), wave = __builtin_amdgcn_readfirstlane(ltid / kWaveSize);
+    if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+    if (n_chunks == 0) return;
+    const uint32_t g0 = c0 >> 8;
+    uint4 xa[MT], xn[MT];
+    load_xa<MT>(a, m, g0, pass, lane, xa);
+    for (uint32_t j = 0; j < rounds; ++j) {
+        if (j + 1 < rounds) load_xa<MT>(a, m, g0 + j + 1, pass, lane, xn);
+        const uint32_t kk = ltid + 256u * j;
+        const uint32_t k = kk - lead;
+        const bool in = kk >= lead && k < n_chunks;
+        uint64_t s8 = 0, r8 = 0;
+        if (j < static_cast<uint32_t>(kPrefetchChunks)) {
+#pragma unroll
+            for (int q = 0; q < kPrefetchChunks; ++q)
+                if (j == static_cast<uint32_t>(q)) s8 = sm[q];
+        } else if (in) {
+            s8 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k)));
+        }
+        if (in) {
+            uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
+            r8 = *cell;
+            *cell = 0;
+        }
+        const uint4 v = merge8(in ? s8 : 0ull, r8);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t e0 = 8u * (c0 + k);
+        if (!in) {
+            w[0] = w[1] = w[2] = w[3] = 0u;
+        } else if (e0 < base || e0 + 8u > end) {
+#pragma unroll
+            for (uint32_t e = 0; e < 8; ++e)
+                if (e0 + e < base || e0 + e >= end) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+        const uint32_t g = g0 + j;
+        const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
+        if (panel != ps.panel || pass != ps.pass) {
+            flush_panel<MT>(m, ps, wave, lane);
+            ps.panel = panel;
+            ps.pass = pass;
+        }
+        const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            ps.d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mt]), b, ps.d[mt], 0, 0, 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xa[mt] = xn[mt];
+    }
+}
+
 // Group edges.  When a group's first element is not a multiple of 8, the
 // group shares an 8-element output chunk with the previous group; stored
 // separately, each half of it would be a partial write of one cache line from
@@ -712,8 +935,14 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     uint32_t *s_edge = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * kWaves + slot * 2u;
     // The next super-group of the dynamic schedule, from thread 0.
     uint32_t *s_ticket = reinterpret_cast<uint32_t *>(s_clen + 256u + GPW * a.ebuf_cap) + GPW * (kWaves + 2u);
-    // The fused matmul's row sums (yacc_rows x TB floats per group).
-    float *s_yacc = reinterpret_cast<float *>(s_ticket + 4) + slot * m.yacc_rows * TB;
+    // The fused matmul's row sums (yacc_rows x TB floats per group; none
+    // for the matrix-core product, TB < 0, whose sums stay in registers).
+    constexpr uint32_t kRowTB = TB > 0 ? TB : 0;
+    float *s_yacc = reinterpret_cast<float *>(s_ticket + 4) + slot * m.yacc_rows * kRowTB;
+    // Only for a stream without a decode table: the first code of each
+    // window, while the table is derived (2^K uint16).
+    uint16_t *s_first =
+        reinterpret_cast<uint16_t *>(reinterpret_cast<float *>(s_ticket + 4) + GPW * m.yacc_rows * kRowTB);
     uint32_t y_row0 = 0, y_rows = 0;  // rows of the merged group awaiting flush_rows
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
@@ -722,11 +951,32 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         finish_schedule(sched, n_wg);
         return;
     }
+    // The matrix-core product (TB < 0, MT = -TB tiles of 16 tokens) gives
+    // each workgroup a contiguous range of super-groups [r0, r0 + len),
+    // swept m.passes times (16 MT tokens each), so that consecutive groups
+    // of a workgroup mostly share a panel and its sums stay in registers.
+    // Its iterations are numbered v = pass * len + (super-group - r0).
+    constexpr bool kMfma = TB < 0;
+    constexpr int MT = kMfma ? -TB : 1;
+    const uint32_t r0 = kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg) * n_super / n_wg) : 0u;
+    const uint32_t len = kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg + 1) * n_super / n_wg) - r0 : 1u;
+    const uint32_t v_end = kMfma ? len * m.passes : n_super;
+    // Super-group of iteration v (n_super past the end).
+    auto super_of = [&](uint32_t v) -> uint32_t { return kMfma ? (v < v_end ? r0 + v % len : n_super) : v; };
+    PanelSums<MT> ps;
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ps.d[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        ps.panel = ~0u;
+        ps.pass = 0;
+    }
+    uint32_t prev_pass = 0;
 
     // Pipeline state: the group's output range (scalar) and thread inputs one
     // super-group ahead; the sign/mantissa chunks of the group waiting to be
     // merged.
-    const uint32_t g_first = wg * GPW + slot;
+    const uint32_t s_first_it = kMfma ? 0u : wg;
+    const uint32_t g_first = super_of(s_first_it) * GPW + slot;
     uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
     GroupLoad cur = load_group(a, g_first, ltid);
     uint64_t sm[kPrefetchChunks] = {};  // the previous group's, until the merge, then this group's
@@ -741,13 +991,19 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         constexpr uint32_t kTabVecs = (10u << K) / 16u;
         constexpr uint32_t kTabPer = (kTabVecs + kThreads - 1) / kThreads;
         constexpr uint32_t kLutPer = (DF11_MAX_LUTS * 64u + kThreads - 1) / kThreads;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.dtab);
+        // Without a table (derived below) every lane loads the first 16
+        // bytes of EncodedExponent instead and stores them anywhere in the
+        // table's place: the loads and stores stay unconditional.
+        const bool have_tab = a.dtab != nullptr;
+        const uint4 *src = reinterpret_cast<const uint4 *>(have_tab ? static_cast<const void *>(a.dtab)
+                                                                    : static_cast<const void *>(a.enc));
+        const uint32_t tab_last = have_tab ? kTabVecs - 1u : 0u;
         const uint32_t *l32 = reinterpret_cast<const uint32_t *>(a.luts);
         const uint32_t lut_words = a.n_luts * 64u;
         uint4 tv[kTabPer];
         uint32_t lv[kLutPer];
 #pragma unroll
-        for (uint32_t j = 0; j < kTabPer; ++j) tv[j] = src[min(tid + j * kThreads, kTabVecs - 1u)];
+        for (uint32_t j = 0; j < kTabPer; ++j) tv[j] = src[min(tid + j * kThreads, tab_last)];
 #pragma unroll
         for (uint32_t j = 0; j < kLutPer; ++j) lv[j] = l32[min(tid + j * kThreads, lut_words - 1u)];
         const uint32_t cv = reinterpret_cast<const uint32_t *>(a.code_lengths)[tid & 63u];
@@ -771,20 +1027,25 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         reinterpret_cast<uint32_t *>(s_clen)[tid & 63u] = cv;
     }
     __syncthreads();
+    if (!a.dtab) {  // a stream without a decode table: derive it from the LUTs and CodeLengths
+        derive_table<K, kThreadsPerGroup * GPW>(s_tab, s_first, s_luts, s_clen, a.n_luts, tid);
+        __syncthreads();
+    }
 
-    uint32_t s_cur = wg, ticket = 0;
-    for (uint32_t it = 0; s_cur < n_super; ++it) {
+    uint32_t s_cur = s_first_it, ticket = 0;
+    for (uint32_t it = 0; s_cur < v_end; ++it) {
         // Wave priorities by phase (the SIMD issues the higher one first
         // among ready waves): the next loads 2, the merge and its stores 0,
         // phase 1's chain of dependent lookups 3, phase 2 1.  A wave that
         // starts decoding runs its chain with fewer gaps while the waves in
         // their merge keep the memory busy.
         __builtin_amdgcn_s_setprio(2);
-        const uint32_t g = s_cur * GPW + slot;
+        const uint32_t g = super_of(s_cur) * GPW + slot;
         // Rounds 0..2 are static; the ticket for round it + 1 >= 3 was
         // written to LDS in iteration it - 1.
-        const uint32_t s_nx =
-            (sched && it >= 2u) ? __builtin_amdgcn_readfirstlane(*s_ticket) : min(s_cur + n_wg, n_super);
+        const uint32_t s_nx = kMfma                  ? s_cur + 1u
+                              : (sched && it >= 2u) ? __builtin_amdgcn_readfirstlane(*s_ticket)
+                                                    : min(s_cur + n_wg, n_super);
 
         // 1. Loads of the next super-group's thread inputs and output range
         // (group numbers past the end are clamped inside the loads and never
@@ -792,7 +1053,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         // output range is clamped so that a corrupt out_pos stays in bounds.
         const uint32_t end = min(cur_end, a.n_elements);
         const uint32_t base = min(cur_base, end);
-        const uint32_t g_nx = min(s_nx * GPW + slot, a.n_groups);
+        const uint32_t g_nx = min(super_of(s_nx) * GPW + slot, a.n_groups);
         const uint32_t nx_base = out_pos_at(a, g_nx), nx_end = out_pos_at(a, g_nx + 1);
         if constexpr (TB > 0) {
             // The fused merge waits for its own loads of x; issued before
@@ -800,6 +1061,8 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
             if (it > 0)
                 merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc,
                                  y_row0, y_rows);
+        } else if constexpr (kMfma) {
+            if (it > 0) merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps);
         }
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
@@ -934,6 +1197,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
 
         prev_base = base;
         prev_end = end;
+        if constexpr (kMfma) prev_pass = s_cur / len;
         cur = nx;
         cur_base = nx_base;
         cur_end = nx_end;
@@ -942,6 +1206,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     }
     if constexpr (TB == 0) {
         merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+    } else if constexpr (kMfma) {
+        merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps);
+        flush_panel<MT>(m, ps, wave, lane);
     } else {
         merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc, y_row0,
                          y_rows);
@@ -996,6 +1263,16 @@ __global__ __launch_bounds__(256) void df11_zero_kernel(float *y, uint32_t n) {
     for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) y[i] = 0.0f;
 }
 
+// Decode fused with y = x W^T on the matrix cores, for any token count: W
+// stored in MFMA tile order, 16 MT tokens per pass over the stream (see
+// merge_mfma).  y must be zero at the start, or hold what the products add to.
+constexpr int kGemmGPW = 2;
+
+template <int K, int MT>
+__global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) void df11_gemm_kernel(DecodeArgs a, MatmulArgs m) {
+    decode_stream<K, kGemmGPW, -MT>(a, m, blockIdx.x, gridDim.x);
+}
+
 // Several weight matrices multiplying the same x in one launch (a block's q,
 // k and v, or gate and up): the grid is split between them as for
 // df11_decode_batch_kernel.
@@ -1032,17 +1309,26 @@ __global__ __launch_bounds__(256) void df11_zero_batch_kernel(ZeroArgs z) {
 }
 
 
+// Index width of a stream's first-level decode table: decode_table_bits,
+// which may be 0 (the default width) for a stream without a table, whose
+// table the kernel derives in LDS.
+constexpr uint32_t kDefaultTableBits = 11;
+
+uint32_t table_bits(const df11_device_stream *s) {
+    return !s->decode_table && s->decode_table_bits == 0 ? kDefaultTableBits : s->decode_table_bits;
+}
+
 int validate(const df11_device_stream *s) {
     if (!s) return DF11_E_INVALID_ARG;
     const df11_header &h = s->h;
     if (h.bytes_per_thread != kBytesPerThread || h.threads_per_group != kThreadsPerGroup) return DF11_E_INVALID_ARG;
     if (h.n_elements > DF11_MAX_ELEMENTS) return DF11_E_TOO_LARGE;
     if (h.n_elements == 0) return h.total_bits == 0 ? DF11_OK : DF11_E_BAD_STREAM;
-    if (df11_decode_table_bytes(s->decode_table_bits) == 0) return DF11_E_INVALID_ARG;
+    if (df11_decode_table_bytes(table_bits(s)) == 0) return DF11_E_INVALID_ARG;
     if (s->groups_per_workgroup != 0 && s->groups_per_workgroup != 1 && s->groups_per_workgroup != 2 &&
         s->groups_per_workgroup != 4)
         return DF11_E_INVALID_ARG;
-    if (!s->enc || !s->sm || !s->gaps || !s->out_pos || !s->luts || !s->code_lengths || !s->decode_table)
+    if (!s->enc || !s->sm || !s->gaps || !s->out_pos || !s->luts || !s->code_lengths)
         return DF11_E_INVALID_ARG;
     if (!aligned(s->enc, 16) || !aligned(s->sm, 16) || !aligned(s->gaps, 4) || !aligned(s->out_pos, 4) ||
         !aligned(s->luts, 4) || !aligned(s->code_lengths, 4) || !aligned(s->decode_table, 16) ||
@@ -1059,6 +1345,7 @@ int validate(const df11_device_stream *s) {
         h.out_pos_bytes != 4 * (groups + 1))
         return DF11_E_BAD_STREAM;
     if (h.max_group_elems == 0 || h.max_group_elems > seg_bits * h.threads_per_group) return DF11_E_BAD_STREAM;
+    if (s->tile_cols && (s->tile_cols % 32 || h.n_elements % (64ull * s->tile_cols))) return DF11_E_INVALID_ARG;
     return DF11_OK;
 }
 
@@ -1072,15 +1359,17 @@ uint32_t schedule_pools(DecodeArgs &a, uint64_t n_super, uint64_t want) {
     return n_wg;
 }
 
-// Dynamic LDS of one stream's workgroup (beyond the static decode table).
-template <int GPW>
-size_t dynamic_lds(const DecodeArgs &a) {
-    return a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u;
+// Dynamic LDS of one stream's workgroup (beyond the static decode table),
+// with `extra` bytes of the fused product's row sums; a stream without a
+// decode table adds the first-code array of its derivation.
+template <int K, int GPW>
+size_t dynamic_lds(const DecodeArgs &a, size_t extra = 0) {
+    return a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u + extra + (a.dtab ? 0u : 2u << K);
 }
 
 template <int K, int GPW>
 int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = dynamic_lds<GPW>(a);
+    const size_t lds = dynamic_lds<K, GPW>(a);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>);
@@ -1115,7 +1404,7 @@ int launch_k(const DecodeArgs &a, uint32_t gpw, uint32_t max_wg, hipStream_t str
 template <int K, int GPW>
 int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     size_t lds = 0;
-    for (uint32_t i = 0; i < b.n; ++i) lds = std::max(lds, dynamic_lds<GPW>(b.s[i]));
+    for (uint32_t i = 0; i < b.n; ++i) lds = std::max(lds, dynamic_lds<K, GPW>(b.s[i]));
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>);
@@ -1162,7 +1451,7 @@ int make_args(const df11_device_stream *s, uint16_t *out, DecodeArgs &a) {
     if (h.n_elements == 0) return DF11_OK;
     if (!out || !aligned(out, 16)) return DF11_E_INVALID_ARG;
     const uint64_t out_bytes = 2 * h.n_elements;
-    const uint32_t bits = s->decode_table_bits;
+    const uint32_t bits = table_bits(s);
     if (overlaps(out, out_bytes, s->enc, h.enc_bytes) || overlaps(out, out_bytes, s->sm, h.sm_bytes) ||
         overlaps(out, out_bytes, s->gaps, h.gaps_bytes) || overlaps(out, out_bytes, s->out_pos, h.out_pos_bytes) ||
         overlaps(out, out_bytes, s->luts, 256ull * h.n_luts) || overlaps(out, out_bytes, s->code_lengths, 256) ||
@@ -1196,6 +1485,11 @@ void fill_args(const df11_device_stream *s, DecodeArgs &a) {
     a.last_seg_bits = static_cast<uint32_t>(h.total_bits - kSegBits * (h.n_threads - 1));
     a.sm_chunks = static_cast<uint32_t>(h.sm_bytes / 8);
     a.sched = s->schedule;
+    a.tile_cols = s->tile_cols;
+    if (s->tile_cols) {
+        a.tile_ks = s->tile_cols / 32u;
+        a.tile_magic = ~0ull / a.tile_ks + 1ull;  // umulhi64(i, tile_magic) == i / tile_ks for all i < 2^32
+    }
 }
 
 int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stream, hipEvent_t start,
@@ -1204,7 +1498,7 @@ int decompress_impl(const df11_device_stream *s, uint16_t *out, hipStream_t stre
     const int rc = make_args(s, out, a);
     if (rc || s->h.n_elements == 0) return rc;
     const uint32_t gpw = s->groups_per_workgroup ? s->groups_per_workgroup : kDefaultGroupsPerWorkgroup;
-    switch (s->decode_table_bits) {
+    switch (table_bits(s)) {
     case 10: return launch_k<10>(a, gpw, s->max_workgroups, stream, start, stop);
     case 11: return launch_k<11>(a, gpw, s->max_workgroups, stream, start, stop);
     case 12: return launch_k<12>(a, gpw, s->max_workgroups, stream, start, stop);
@@ -1240,7 +1534,7 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
                 overlaps(outs[i], out_bytes, o.out_pos, o.h.out_pos_bytes) ||
                 overlaps(outs[i], out_bytes, o.luts, 256ull * o.h.n_luts) ||
                 overlaps(outs[i], out_bytes, o.code_lengths, 256) ||
-                overlaps(outs[i], out_bytes, o.decode_table, df11_decode_table_bytes(o.decode_table_bits)) ||
+                overlaps(outs[i], out_bytes, o.decode_table, df11_decode_table_bytes(table_bits(&o))) ||
                 overlaps(outs[i], out_bytes, o.schedule, o.schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
                 return DF11_E_INVALID_ARG;
         }
@@ -1255,9 +1549,9 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
         if (streams[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, streams[i].max_workgroups)
                                                        : streams[i].max_workgroups;
         if (b.n == 0) {
-            bits = streams[i].decode_table_bits;
+            bits = table_bits(&streams[i]);
             gpw = g;
-        } else if (streams[i].decode_table_bits != bits || g != gpw) {
+        } else if (table_bits(&streams[i]) != bits || g != gpw) {
             return DF11_E_INVALID_ARG;
         }
         b.s[b.n++] = a;
@@ -1299,7 +1593,7 @@ int decompress_batch_impl(const df11_device_stream *streams, uint32_t n, uint16_
 template <int K, int TB>
 int launch_linear(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream,
                   hipEvent_t start, hipEvent_t stop, bool zero) {
-    const size_t lds = dynamic_lds<kLinearGPW>(a) + sizeof(float) * kLinearGPW * m.yacc_rows * TB;
+    const size_t lds = dynamic_lds<K, kLinearGPW>(a, sizeof(float) * kLinearGPW * m.yacc_rows * TB);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_linear_kernel<K, TB>);
@@ -1333,7 +1627,7 @@ int linear_args(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
     if (rc) return rc;
     const df11_header &h = s->h;
     if (n_tokens < 1 || n_tokens > DF11_LINEAR_MAX_TOKENS || in_features < DF11_LINEAR_MIN_IN_FEATURES ||
-        in_features % 8 || static_cast<uint64_t>(in_features) * out_features != h.n_elements)
+        in_features % 8 || static_cast<uint64_t>(in_features) * out_features != h.n_elements || s->tile_cols)
         return DF11_E_INVALID_ARG;
     empty = h.n_elements == 0;
     if (empty) return DF11_OK;
@@ -1343,7 +1637,7 @@ int linear_args(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
         overlaps(y, y_bytes, s->sm, h.sm_bytes) || overlaps(y, y_bytes, s->gaps, h.gaps_bytes) ||
         overlaps(y, y_bytes, s->out_pos, h.out_pos_bytes) || overlaps(y, y_bytes, s->luts, 256ull * h.n_luts) ||
         overlaps(y, y_bytes, s->code_lengths, 256) ||
-        overlaps(y, y_bytes, s->decode_table, df11_decode_table_bytes(s->decode_table_bits)) ||
+        overlaps(y, y_bytes, s->decode_table, df11_decode_table_bytes(table_bits(s))) ||
         overlaps(y, y_bytes, s->schedule, s->schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
         return DF11_E_INVALID_ARG;
     if (y_bytes / 4 >= (1ull << 32)) return DF11_E_TOO_LARGE;
@@ -1377,7 +1671,7 @@ int linear_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_token
         case 4: return launch_linear<KB, 4>(a, m, s->max_workgroups, stream, start, stop, zero);  \
         default: return launch_linear<KB, 8>(a, m, s->max_workgroups, stream, start, stop, zero); \
         }
-    switch (s->decode_table_bits) {
+    switch (table_bits(s)) {
         DF11_LINEAR_CASE(10)
         DF11_LINEAR_CASE(11)
         DF11_LINEAR_CASE(12)
@@ -1393,7 +1687,7 @@ int launch_linear_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStr
                         hipEvent_t stop, bool zero) {
     size_t lds = 0;
     for (uint32_t i = 0; i < b.n; ++i)
-        lds = std::max(lds, dynamic_lds<kLinearGPW>(b.s[i]) + sizeof(float) * kLinearGPW * b.m[i].yacc_rows * TB);
+        lds = std::max(lds, dynamic_lds<K, kLinearGPW>(b.s[i], sizeof(float) * kLinearGPW * b.m[i].yacc_rows * TB));
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_linear_batch_kernel<K, TB>);
@@ -1450,14 +1744,14 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
                 overlaps(ys[i], y_bytes, o.out_pos, o.h.out_pos_bytes) ||
                 overlaps(ys[i], y_bytes, o.luts, 256ull * o.h.n_luts) ||
                 overlaps(ys[i], y_bytes, o.code_lengths, 256) ||
-                overlaps(ys[i], y_bytes, o.decode_table, df11_decode_table_bytes(o.decode_table_bits)) ||
+                overlaps(ys[i], y_bytes, o.decode_table, df11_decode_table_bytes(table_bits(&o))) ||
                 overlaps(ys[i], y_bytes, o.schedule, o.schedule ? 4 * DF11_SCHEDULE_WORDS : 0))
                 return DF11_E_INVALID_ARG;
         }
         if (empty) continue;
         if (shares_schedule(ws, i)) a.sched = nullptr;
-        if (b.n && ws[i].decode_table_bits != bits) return DF11_E_INVALID_ARG;
-        bits = ws[i].decode_table_bits;
+        if (b.n && table_bits(&ws[i]) != bits) return DF11_E_INVALID_ARG;
+        bits = table_bits(&ws[i]);
         if (ws[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, ws[i].max_workgroups) : ws[i].max_workgroups;
         if (static_cast<uint64_t>(total) + static_cast<uint64_t>(n_tokens) * out_features[i] >= (1ull << 32))
             return DF11_E_TOO_LARGE;
@@ -1485,6 +1779,101 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
     default: return DF11_E_INVALID_ARG;
     }
 #undef DF11_LINEAR_BATCH_CASE
+}
+
+// The matrix-core product: y = 0 (unless accumulating), then the fused
+// kernel over as many workgroups as fit at once (at most one per
+// super-group), each with a contiguous range of the stream.
+template <int K, int MT>
+int launch_gemm(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
+                hipEvent_t stop, bool zero) {
+    const size_t lds = dynamic_lds<K, kGemmGPW>(a);
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const void *fn = reinterpret_cast<const void *>(&df11_gemm_kernel<K, MT>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
+    const uint64_t n_super = (a.n_groups + kGemmGPW - 1) / kGemmGPW;
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, max_wg);
+    const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min(resident, n_super)));
+    (void)hipGetLastError();
+    DecodeArgs args = a;
+    args.sched = nullptr;  // (contiguous ranges: no dynamic schedule)
+    MatmulArgs margs = m;
+    margs.passes = (m.n_tokens + 16u * MT - 1u) / (16u * MT);
+    if (zero) {
+        float *y = m.y;
+        const uint32_t n_y = m.n_tokens * m.out_features;
+        void *zparams[] = {&y, const_cast<uint32_t *>(&n_y)};
+        const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((n_y + 255) / 256, 1024));
+        const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_kernel), dim3(zgrid), dim3(256),
+                                     zparams, 0, stream, nullptr, nullptr);
+        if (rc) return rc;
+    }
+    void *params[] = {&args, &margs};
+    return launch_kernel(fn, dim3(grid), dim3(kThreadsPerGroup * kGemmGPW), params, lds, stream, start, stop);
+}
+
+// Checks one matrix-core product's arguments (no launch) and fills its
+// kernel arguments; *empty is set for a stream with no elements.
+int gemm_args(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+              uint32_t out_features, float *y, DecodeArgs &a, MatmulArgs &m, bool &empty) {
+    int rc = validate(s);
+    if (rc) return rc;
+    const df11_header &h = s->h;
+    if (n_tokens < 1 || in_features < 32 || in_features % 32 || out_features % 64 ||
+        static_cast<uint64_t>(in_features) * out_features != h.n_elements ||
+        (h.n_elements && s->tile_cols != in_features))
+        return DF11_E_INVALID_ARG;
+    empty = h.n_elements == 0;
+    if (empty) return DF11_OK;
+    if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return DF11_E_INVALID_ARG;
+    const uint64_t y_elems = static_cast<uint64_t>(n_tokens) * out_features;
+    const uint64_t y_bytes = 4 * y_elems, x_bytes = 2ull * n_tokens * in_features;
+    // (the kernel numbers its iterations, passes x super-groups, with 32 bits)
+    const uint64_t sweeps = (n_tokens + 15ull) / 16ull, n_super = (h.n_groups + kGemmGPW - 1) / kGemmGPW;
+    if (y_elems >= (1ull << 32) || sweeps * n_super >= (1ull << 31)) return DF11_E_TOO_LARGE;
+    if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, s->enc, h.enc_bytes) ||
+        overlaps(y, y_bytes, s->sm, h.sm_bytes) || overlaps(y, y_bytes, s->gaps, h.gaps_bytes) ||
+        overlaps(y, y_bytes, s->out_pos, h.out_pos_bytes) || overlaps(y, y_bytes, s->luts, 256ull * h.n_luts) ||
+        overlaps(y, y_bytes, s->code_lengths, 256) ||
+        overlaps(y, y_bytes, s->decode_table, df11_decode_table_bytes(table_bits(s))))
+        return DF11_E_INVALID_ARG;
+    fill_args(s, a);
+    m = MatmulArgs{};
+    m.x = x;
+    m.y = y;
+    m.in_features = in_features;
+    m.out_features = out_features;
+    m.n_tokens = n_tokens;
+    return DF11_OK;
+}
+
+// Token tiles of 16 per pass: 1 up to 16 tokens, 2 up to 32, else 4.
+uint32_t gemm_tiles(uint32_t n_tokens) { return n_tokens <= 16 ? 1 : n_tokens <= 32 ? 2 : 4; }
+
+int gemm_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+              uint32_t out_features, float *y, hipStream_t stream, hipEvent_t start, hipEvent_t stop, bool zero) {
+    DecodeArgs a;
+    MatmulArgs m;
+    bool empty = false;
+    const int rc = gemm_args(s, x, n_tokens, in_features, out_features, y, a, m, empty);
+    if (rc || empty) return rc;
+#define DF11_GEMM_CASE(KB)                                                                   \
+    case KB:                                                                                 \
+        switch (gemm_tiles(n_tokens)) {                                                      \
+        case 1: return launch_gemm<KB, 1>(a, m, s->max_workgroups, stream, start, stop, zero); \
+        case 2: return launch_gemm<KB, 2>(a, m, s->max_workgroups, stream, start, stop, zero); \
+        default: return launch_gemm<KB, 4>(a, m, s->max_workgroups, stream, start, stop, zero); \
+        }
+    switch (table_bits(s)) {
+        DF11_GEMM_CASE(10)
+        DF11_GEMM_CASE(11)
+        DF11_GEMM_CASE(12)
+    default: return DF11_E_INVALID_ARG;
+    }
+#undef DF11_GEMM_CASE
 }
 
 // The allocation-free batched decode's work counters: one set of
@@ -1555,6 +1944,24 @@ int df11_decompress_timed(const df11_device_stream *s, uint16_t *out, void *hip_
                           void *stop_event) {
     return decompress_impl(s, out, static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
                            static_cast<hipEvent_t>(stop_event));
+}
+
+int df11_matmul(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, void *hip_stream) {
+    return gemm_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
+                     nullptr, true);
+}
+
+int df11_matmul_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                    uint32_t out_features, float *y, void *hip_stream) {
+    return gemm_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
+                     nullptr, false);
+}
+
+int df11_matmul_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                      uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event) {
+    return gemm_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream),
+                     static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event), true);
 }
 
 int df11_linear(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,

@@ -64,6 +64,24 @@ __device__ __forceinline__ void store_chunk(uint16_t *out, uint32_t c, uint4 v, 
     }
 }
 
+// store_chunk for a chunk whose 8 elements (stream positions first ..
+// first + 7, kept where they lie in [base, end)) go to out[dst .. dst + 7]:
+// a matrix stored in another order than the one it is written back in.
+__device__ __forceinline__ void store_chunk_at(uint16_t *out, uint32_t dst, uint32_t first, uint4 v, uint32_t base,
+                                               uint32_t end) {
+    if (first >= base && first + 8u <= end) {
+        u32x4 x = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(out + dst));
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            const uint32_t gi = first + i;
+            if (gi >= base && gi < end) out[dst + i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
+        }
+    }
+}
+
 uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

@@ -381,6 +381,25 @@ int df11_build_decode_table(const df11_codebook *cb, uint32_t bits, void *table,
     return DF11_OK;
 }
 
+int df11_tile_order(const uint16_t *w, uint64_t rows, uint64_t cols, uint16_t *out) {
+    if (!w || !out || rows % 64 || cols % 32) return DF11_E_INVALID_ARG;
+    const uint64_t n = rows * cols;
+    if (n && (w < out ? w + n > out : out + n > w)) return DF11_E_INVALID_ARG;
+    // Walk the ordered sequence block by block: block b is n-tile b mod 4 of
+    // global k-step b / 4 (k-step ks of panel p); lane l of a block takes 8
+    // consecutive columns of one row.
+    const uint64_t ks_per_panel = cols / 32;
+    uint64_t s = 0;
+    for (uint64_t p = 0; p < rows / 64; ++p)
+        for (uint64_t ks = 0; ks < ks_per_panel; ++ks)
+            for (uint64_t nt = 0; nt < 4; ++nt)
+                for (uint64_t l = 0; l < 64; ++l, s += 8) {
+                    const uint64_t r = 64 * p + 16 * nt + l % 16, c = 32 * ks + 8 * (l / 16);
+                    memcpy(out + s, w + r * cols + c, 8 * sizeof(uint16_t));
+                }
+    return DF11_OK;
+}
+
 const char *df11_status_str(int status) {
     switch (status) {
     case DF11_OK: return "DF11_OK";

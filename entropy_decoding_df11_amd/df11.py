@@ -138,7 +138,8 @@ class DF11Tensor:
     """A DF11 stream resident in GPU memory, decompressed on demand."""
 
     def __init__(self, host: HostStream, shape: Sequence[int], device="cuda",
-                 decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS, groups_per_workgroup: int = 0):
+                 decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS, groups_per_workgroup: int = 0,
+                 tile_cols: int = 0):
         import torch
         self.host_header = host.header
         self.shape = tuple(int(s) for s in shape)
@@ -168,6 +169,10 @@ class DF11Tensor:
             setattr(s, name, t.data_ptr())
         s.decode_table_bits = decode_table_bits
         s.groups_per_workgroup = groups_per_workgroup
+        # A matrix stored in MFMA tile order (df11_tile_order) for matmul():
+        # its column count; decompress() writes it back row-major.
+        s.tile_cols = tile_cols
+        self.tile_cols = tile_cols
         # The kernel's work counter for dynamic load balancing (zero between
         # launches).  Launches of one DF11Tensor must not overlap in time.
         self._schedule = torch.zeros(_lib.SCHEDULE_WORDS, dtype=torch.int32, device=self.device)
@@ -189,12 +194,20 @@ class DF11Tensor:
         s = _lib.DeviceStream.from_buffer_copy(self._stream_struct)
         for name, t in c._bufs.items():
             setattr(s, name, t.data_ptr())
+        if not self._stream_struct.decode_table:  # (launched without the table)
+            s.decode_table = None
         if self._stream_struct.schedule:
             s.schedule = c._schedule.data_ptr()
         c._stream_struct = s
         c._last_stream = None
         torch.cuda.current_stream(self.device).synchronize()
         return c
+
+    def use_decode_table(self, on: bool) -> None:
+        """Launch with the host-built first-level decode table (default), or
+        with the page's arrays alone (no table): every workgroup then derives
+        the same table in LDS from the LUTs and CodeLengths."""
+        self._stream_struct.decode_table = self._bufs["decode_table"].data_ptr() if on else None
 
     def set_dynamic_schedule(self, on: bool) -> None:
         """Balance work between workgroups at run time (default) or assign it
@@ -318,6 +331,50 @@ class DF11Tensor:
                                              ctypes.c_void_p(_event_handle(stop, st))), "df11_linear_timed")
         return out
 
+    def matmul(self, x: "torch.Tensor", out: Optional["torch.Tensor"] = None, stream=None,  # noqa: F821
+               events=None, accumulate: bool = False) -> "torch.Tensor":  # noqa: F821
+        """y = x W^T on the matrix cores with the decode fused in (df11_matmul),
+        for any number of tokens: W is this tensor, compressed with
+        layout="mfma_tiles", as an (out_features, in_features) matrix; x a
+        contiguous bfloat16 (n_tokens, in_features) tensor.  Returns out, a
+        float32 (n_tokens, out_features) tensor (a new one by default).
+        events: as for decompress.  With accumulate, out (required)
+        receives out + x W^T (df11_matmul_acc)."""
+        import torch
+        if len(self.shape) != 2 or not self.tile_cols:
+            raise ValueError("matmul needs a 2-D weight compressed with layout='mfma_tiles'")
+        out_f, in_f = self.shape
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != in_f or not x.is_contiguous():
+            raise ValueError("x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
+        if not _on_device(x, self.device):
+            raise ValueError("x must be on the weight's device")
+        n_tokens = x.shape[0]
+        if out is None:
+            if accumulate:
+                raise ValueError("accumulate needs out")
+            out = torch.empty((n_tokens, out_f), dtype=torch.float32, device=self.device)
+        if out.dtype != torch.float32 or out.shape != (n_tokens, out_f) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 (n_tokens, out_features) tensor")
+        if not _on_device(out, self.device):
+            raise ValueError("out must be on the weight's device")
+        lib = _lib.load()
+        st = self._claim(stream)
+        args = (ctypes.byref(self._stream_struct), ctypes.c_void_p(x.data_ptr()), n_tokens, in_f, out_f,
+                ctypes.c_void_p(out.data_ptr()), st)
+        if accumulate:
+            if events is not None:
+                raise ValueError("accumulate takes no events")
+            _lib.check(lib.df11_matmul_acc(*args), "df11_matmul_acc")
+        elif events is None:
+            _lib.check(lib.df11_matmul(*args), "df11_matmul")
+        else:
+            start, stop = events
+            _lib.check(lib.df11_matmul_timed(*args, ctypes.c_void_p(_event_handle(start, st)),
+                                             ctypes.c_void_p(_event_handle(stop, st))), "df11_matmul_timed")
+        return out
+
 
 def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, stream=None,  # noqa: F821
                  events=None, accumulate: bool = False) -> List["torch.Tensor"]:  # noqa: F821
@@ -390,14 +447,37 @@ def _event_handle(ev, stream: ctypes.c_void_p) -> int:
     return ev.cuda_event
 
 
+def tile_order(w: ArrayLike, rows: int, cols: int) -> np.ndarray:
+    """A rows x cols BF16 matrix (uint16 patterns) reordered into MFMA tile
+    order (df11_tile_order)."""
+    src = _u16(w)
+    if src.size != rows * cols:
+        raise ValueError("rows * cols must equal the element count")
+    out = np.empty_like(src)
+    _lib.check(_lib.load().df11_tile_order(_ptr(src, ctypes.c_uint16), rows, cols, _ptr(out, ctypes.c_uint16)),
+               "df11_tile_order")
+    return out
+
+
 def compress(tensor: ArrayLike, shape: Optional[Sequence[int]] = None, device="cuda",
              codebook: Optional[_lib.Codebook] = None,
-             decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS) -> DF11Tensor:
-    """Encode a BF16 tensor on the host and upload the stream to the GPU."""
+             decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS, layout: str = "rows") -> DF11Tensor:
+    """Encode a BF16 tensor on the host and upload the stream to the GPU.
+    layout="rows" keeps the elements in their own order; layout="mfma_tiles"
+    (a 2-D weight, rows a multiple of 64, columns of 32) stores them in the
+    order the matrix-core product consumes them (DF11Tensor.matmul)."""
     if shape is None:
         shape = tuple(tensor.shape)
-    host = encode(tensor, codebook=codebook)
-    return DF11Tensor(host, shape, device=device, decode_table_bits=decode_table_bits)
+    if layout == "rows":
+        host = encode(tensor, codebook=codebook)
+        return DF11Tensor(host, shape, device=device, decode_table_bits=decode_table_bits)
+    if layout != "mfma_tiles":
+        raise ValueError("layout must be 'rows' or 'mfma_tiles'")
+    if len(shape) != 2:
+        raise ValueError("layout='mfma_tiles' needs a 2-D (out_features, in_features) weight")
+    rows, cols = (int(v) for v in shape)
+    host = encode(tile_order(tensor, rows, cols), codebook=codebook)
+    return DF11Tensor(host, shape, device=device, decode_table_bits=decode_table_bits, tile_cols=cols)
 
 
 def decompress(t: DF11Tensor, out=None, stream=None):

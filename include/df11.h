@@ -131,8 +131,14 @@ typedef struct df11_header {
  *   luts         device, n_luts * 256    df11_codebook.luts rows 0..n_luts-1
  *   code_lengths device, 256             df11_codebook.code_lengths
  *   decode_table device, df11_decode_table_bytes(decode_table_bits)
- *                                        built by df11_build_decode_table
- *   decode_table_bits                    index width of decode_table (10..12)
+ *                                        built by df11_build_decode_table, or
+ *                                        NULL: a caller holding only the page's
+ *                                        arrays passes NULL, and every
+ *                                        workgroup then derives the same table
+ *                                        in LDS from luts and code_lengths
+ *                                        (about a microsecond per launch)
+ *   decode_table_bits                    index width of decode_table (10..12);
+ *                                        0 with a NULL decode_table selects 11
  *   groups_per_workgroup                 launch shape: groups decoded together by one
  *                                        workgroup (1, 2 or 4); 0 picks the default
  *   schedule     device, DF11_SCHEDULE_WORDS uint32, or NULL
@@ -154,7 +160,16 @@ typedef struct df11_header {
  *                                        batched launch takes the smallest cap
  *                                        of its streams and still gives every
  *                                        non-empty stream one workgroup, so it
- *                                        launches at most max(cap, streams). */
+ *                                        launches at most max(cap, streams).
+ *   tile_cols                            0: the stream holds its elements in their
+ *                                        own order.  Else the stream holds a
+ *                                        (N / tile_cols) x tile_cols matrix in
+ *                                        MFMA tile order (df11_tile_order;
+ *                                        tile_cols a multiple of 32, N a
+ *                                        multiple of 64 * tile_cols): the
+ *                                        decompress entry points write it back
+ *                                        row-major, and df11_matmul takes only
+ *                                        such streams. */
 typedef struct df11_device_stream {
     df11_header h;
     const uint8_t *enc;
@@ -168,7 +183,7 @@ typedef struct df11_device_stream {
     uint32_t groups_per_workgroup;
     uint32_t *schedule;
     uint32_t max_workgroups;
-    uint32_t reserved;
+    uint32_t tile_cols;
 } df11_device_stream;
 
 /* Accumulate the 256-bin exponent histogram of n BF16 words (host).
@@ -210,6 +225,21 @@ int df11_plan(const df11_codebook *cb, const uint64_t hist[256], uint64_t n, con
  * code, or h does not match the data), DF11_E_TOO_LARGE. */
 int df11_encode(const df11_codebook *cb, const uint16_t *bf16, uint64_t n, const df11_layout *lay,
                 df11_header *h, uint8_t *enc, uint8_t *sm, uint8_t *gaps, uint32_t *out_pos);
+
+/* Reorder a rows x cols row-major BF16 matrix (host) into MFMA tile order,
+ * the element order df11_matmul consumes.  Not on the page (the page fixes no
+ * element order); the order of this library's matrix-core product.  Position
+ * s of the ordered sequence holds W[r][c] with
+ *   panel p = s / (64 cols), q = s mod (64 cols)
+ *   k-step ks = q / 2048, u = q mod 2048
+ *   n-tile nt = u / 512, v = u mod 512, lane l = v / 8, j = v mod 8
+ *   r = 64 p + 16 nt + (l mod 16),  c = 32 ks + 8 (l / 16) + j
+ * so every 8 consecutive elements are 8 consecutive columns of one row, and
+ * each 512-element block is the B operand that the 64 lanes of a gfx950
+ * v_mfma_f32_16x16x32_bf16 read for 16 rows x 32 columns of W.
+ * w, out: host, rows * cols uint16, not overlapping.  rows a multiple of 64,
+ * cols a multiple of 32, else DF11_E_INVALID_ARG. */
+int df11_tile_order(const uint16_t *w, uint64_t rows, uint64_t cols, uint16_t *out);
 
 /* Size in bytes of the decode table for index width bits (10..12), 0 if
  * unsupported.  Not on the page: the decode table is this decoder's own
@@ -310,7 +340,8 @@ int df11_decompress_batch_timed(const df11_device_stream *streams, uint32_t n_st
  * News" suggests a GEMM that decompresses each tile before the arithmetic,
  * which this is for small token counts (token-by-token generation), where the
  * product is bound by reading W.
- *   w             device stream, h.n_elements == out_features * in_features
+ *   w             device stream, h.n_elements == out_features * in_features,
+ *                 elements in their own (row-major) order: tile_cols == 0
  *   x             device, n_tokens x in_features BF16 (uint16 bit patterns),
  *                 row-major, 16-byte aligned; read only
  *   n_tokens      1 .. DF11_LINEAR_MAX_TOKENS
@@ -370,6 +401,44 @@ int df11_linear_batch(const df11_device_stream *ws, uint32_t n_streams, const ui
 int df11_linear_batch_acc(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *x, uint32_t n_tokens,
                           uint32_t in_features, const uint32_t *out_features, float *const *ys, void *hip_stream,
                           void *start_event, void *stop_event);
+
+/* y = x W^T on the matrix cores with the decompression fused in, for any
+ * number of tokens: the page's section "Dekompresi yang disesuaikan untuk
+ * inferensi GPU" decompresses each weight matrix right before its matrix
+ * multiplication and discards the BF16 copy; the section "Opini Hacker News"
+ * suggests a GEMM that decompresses each tile before the arithmetic.  Here
+ * every decoded 16 x 32 tile of W goes from the decoder's registers straight
+ * into v_mfma_f32_16x16x32_bf16 with the matching tile of x; W's BF16 never
+ * reaches HBM.
+ *   w             device stream in MFMA tile order: tile_cols == in_features
+ *                 (df11_tile_order), h.n_elements == out_features * in_features
+ *   x             device, n_tokens x in_features BF16, row-major, 16-byte
+ *                 aligned, finite values; read only
+ *   n_tokens      >= 1; the stream is swept once per 64 tokens (once up to 16,
+ *                 32 or 64)
+ *   in_features   a multiple of 32;  out_features a multiple of 64
+ *   y             device, n_tokens x out_features float, row-major, 4-byte
+ *                 aligned, overlapping neither x nor the stream's buffers;
+ *                 every element is overwritten
+ * y[t][r] is the sum over c of x[t][c] * W[r][c]: products exact in float,
+ * sums in float in an unspecified order (partial sums of a row from several
+ * workgroups meet in float atomics), so the low bits can differ between
+ * calls.  Enqueued on hip_stream: a zeroing kernel for y, then the fused
+ * kernel; the stream's schedule counters are not used.  Errors:
+ * DF11_E_INVALID_ARG (sizes, alignment, overlap, a stream not in tile order,
+ * or as for df11_decompress), DF11_E_BAD_STREAM, DF11_E_TOO_LARGE
+ * (n_tokens * out_features >= 2^32), DF11_E_HIP. */
+int df11_matmul(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                uint32_t out_features, float *y, void *hip_stream);
+
+/* df11_matmul accumulating into y (y += x W^T): no zeroing kernel. */
+int df11_matmul_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                    uint32_t out_features, float *y, void *hip_stream);
+
+/* df11_matmul with start_event and stop_event (hipEvent_t, either may be
+ * NULL) recorded when the fused kernel itself starts and ends. */
+int df11_matmul_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
+                      uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
 /* ---------------------------------------------------------------------------
  * rANS exponent coder.  The discussion on the page ("Opini Hacker News")

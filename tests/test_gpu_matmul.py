@@ -1,0 +1,172 @@
+"""GPU parity of the matrix-core product (df11_matmul) and of decompressing
+a weight stored in MFMA tile order, through the C ABI.
+
+The product's reference is the oracle's float64 y = x W^T on the original
+row-major W (oracle.linear); the bound is the float32 summation bound
+gamma_n = 1.01 * in_features * 2^-24 * sum |x w| per output (every BF16 x
+BF16 product is exact in float32; in_features additions in float32 in some
+order).  Decompression must give back W's bits exactly.
+
+Method: GeekNews, "DFloat11: Kompresi inferensi GPU lossless yang mengecilkan
+LLM menjadi 70% ukurannya", sections "Dekompresi yang disesuaikan untuk
+inferensi GPU" and "Opini Hacker News" (a GEMM that decompresses each tile).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_decoding_df11_amd import df11, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    return torch
+
+
+def _note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _u16(t):
+    import torch
+    return t.detach().reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _weights(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return workloads.f32_to_bf16_bits(rng.standard_normal(n) * 0.02)
+    if kind == "student_t":
+        return workloads.f32_to_bf16_bits(rng.standard_t(5, n) * 0.015)
+    if kind == "stress_tuned":  # codes of up to ~29 bits through the LUT hierarchy
+        return workloads.gen_stress(seed=seed, n=n)
+    if kind == "zeros":
+        return np.zeros(n, np.uint16)
+    if kind == "integers":  # small integers: every sum exact, so y must equal the oracle exactly
+        return workloads.f32_to_bf16_bits(rng.integers(-8, 9, n).astype(np.float64))
+    raise ValueError(kind)
+
+
+def _tokens(t, c, seed, integers=False):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-4, 5, t * c).astype(np.float64) if integers else rng.standard_normal(t * c) * 0.5
+    return workloads.f32_to_bf16_bits(x).reshape(t, c)
+
+
+def _bound(xb, w, rows, cols):
+    xa = np.abs(oracle.bf16_to_f64(xb).reshape(-1, cols))
+    wa = np.abs(oracle.bf16_to_f64(w).reshape(rows, cols))
+    return 1.01 * cols * 2.0 ** -24 * (xa @ wa.T)
+
+
+def _device_x(torch, xb):
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 32), (128, 1024), (192, 4096), (64, 14336), (1024, 4096)])
+@pytest.mark.parametrize("kind", ["normal", "stress_tuned"])
+def test_tiled_decompress_is_row_major(torch_cuda, rows, cols, kind):
+    torch = torch_cuda
+    _note(f"tiled decompress {kind} {rows}x{cols}")
+    w = _weights(kind, rows * cols, rows + cols)
+    t = df11.compress(w, shape=(rows, cols), layout="mfma_tiles")
+    out = torch.full((rows, cols), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    t.decompress(out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out), w)
+
+
+MATMUL_CASES = [  # (weights, rows, cols)
+    ("normal", 64, 32),          # one panel of one k-step: groups span many panels
+    ("normal", 128, 1024),       # groups across panel edges
+    ("student_t", 192, 4096),
+    ("stress_tuned", 64, 14336),  # one long panel; codes through the LUT hierarchy
+    ("zeros", 128, 512),          # one exponent: y is exactly zero
+]
+
+
+@pytest.mark.parametrize("n_tokens", [1, 3, 16, 17, 33, 64, 65, 130])
+@pytest.mark.parametrize("kind,rows,cols", MATMUL_CASES)
+def test_matmul_matches_oracle(torch_cuda, kind, rows, cols, n_tokens):
+    torch = torch_cuda
+    _note(f"matmul {kind} {rows}x{cols} tokens={n_tokens}")
+    w = _weights(kind, rows * cols, 7 + rows)
+    xb = _tokens(n_tokens, cols, n_tokens + cols)
+    t = df11.compress(w, shape=(rows, cols), layout="mfma_tiles")
+    ref = oracle.linear(oracle.encode(w), xb, rows)
+    bound = _bound(xb, w, rows, cols)
+    x = _device_x(torch, xb)
+    for _ in range(2):  # y is overwritten on every call
+        y = t.matmul(x)
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+
+
+def test_matmul_exact_on_integers_and_accumulate(torch_cuda):
+    """Small integer weights and tokens: every partial sum is an integer below
+    2^24, so y equals the oracle exactly whatever the summation order; the
+    accumulating entry point adds to what y holds."""
+    torch = torch_cuda
+    rows, cols, n_tokens = 256, 2048, 40
+    w = _weights("integers", rows * cols, 1)
+    xb = _tokens(n_tokens, cols, 2, integers=True)
+    t = df11.compress(w, shape=(rows, cols), layout="mfma_tiles")
+    ref = oracle.linear(oracle.encode(w), xb, rows)
+    x = _device_x(torch, xb)
+    y = t.matmul(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    t.matmul(x, out=y, accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), 2 * ref)
+
+
+def test_matmul_one_hot_tokens_return_columns(torch_cuda):
+    """Token t one-hot at column c gives y[t] = W[:, c] exactly (a transposed
+    or misplaced operand fails)."""
+    torch = torch_cuda
+    rows, cols = 192, 1024
+    w = _weights("normal", rows * cols, 5)
+    cs = np.random.default_rng(9).choice(cols, 37, replace=False)
+    xb = np.zeros((cs.size, cols), np.uint16)
+    xb[np.arange(cs.size), cs] = 0x3F80  # 1.0
+    t = df11.compress(w, shape=(rows, cols), layout="mfma_tiles")
+    y = t.matmul(_device_x(torch, xb))
+    torch.cuda.synchronize()
+    wf = oracle.bf16_to_f64(w).reshape(rows, cols)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), wf[:, cs].T)
+
+
+@pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
+@pytest.mark.parametrize("n_tokens", [16, 256, 4096])
+def test_matmul_full_size_block_matrix(torch_cuda, name, n_tokens):
+    """The Llama-3-8B block's gate_proj (14336 x 4096) and down_proj (4096 x
+    14336) at full size: every output row against the oracle for a sample of
+    the tokens (all of them up to 16)."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block()
+    (off, (rows, cols)), = [(o, shp) for nm, o, shp in views if nm == name]
+    w = np.ascontiguousarray(flat[off:off + rows * cols])
+    del flat
+    _note(f"matmul full size {name} {rows}x{cols} tokens={n_tokens}")
+    xb = _tokens(n_tokens, cols, n_tokens)
+    t = df11.compress(w, shape=(rows, cols), layout="mfma_tiles")
+    y = t.matmul(_device_x(torch, xb))
+    torch.cuda.synchronize()
+    sample = np.arange(n_tokens) if n_tokens <= 16 else np.sort(
+        np.random.default_rng(n_tokens).choice(n_tokens, 24, replace=False))
+    ref = oracle.linear(oracle.encode(w), xb[sample], rows)
+    bound = _bound(xb[sample], w, rows, cols)
+    got = y.cpu().numpy()[sample].astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+    assert np.all(np.isfinite(y.cpu().numpy()))

@@ -247,6 +247,54 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
     t.set_max_workgroups(0)
 
 
+@pytest.mark.parametrize("bits", [0, 10, 11, 12])
+@pytest.mark.parametrize("kind", ["normal", "fib_chain", "stress_tuned", "stress_literal", "uniform_bits", "zeros"])
+def test_derived_decode_table(torch_cuda, kind, bits):
+    """A stream given with the page's arrays alone (no decode table): every
+    workgroup derives the first-level table in LDS from the LUTs and
+    CodeLengths (bits 0: the default width)."""
+    torch = torch_cuda
+    w = _case(kind, 300001, 5 + bits)
+    _note(f"derived table {kind} bits={bits}")
+    t = df11.compress(w, shape=(w.size,), decode_table_bits=bits or 11)
+    t.use_decode_table(False)
+    t.device_stream().decode_table_bits = bits
+    out = torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    t.decompress(out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_to_u16(out), w)
+
+
+def test_derived_decode_table_full_block_batch_and_linear(torch_cuda):
+    """The derived table on the full-size block, in a batched launch and in
+    the fused product."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block()
+    _note("derived table: full block")
+    blk = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views])
+    blk.tensor.use_decode_table(False)
+    scratch = torch.empty(blk.n_elements, dtype=torch.bfloat16, device="cuda")
+    blk.decompress(scratch=scratch)
+    torch.cuda.synchronize()
+    assert np.array_equal(_to_u16(scratch), flat)
+    del blk, scratch
+    _note("derived table: batch of three")
+    ws = [_case(k, n, 9) for k, n in (("normal", 100003), ("fib_chain", 7), ("stress_tuned", 654321))]
+    ts = [df11.compress(w, shape=(w.size,)) for w in ws]
+    for t in ts[:2]:
+        t.use_decode_table(False)
+    outs = [torch.empty(w.size, dtype=torch.bfloat16, device="cuda") for w in ws]
+    df11.decompress_batch(ts, outs)
+    torch.cuda.synchronize()
+    for w, o in zip(ws, outs):
+        assert np.array_equal(_to_u16(o), w)
+    _note("derived table: fused product")
+    wm = _case("stress_tuned", 256 * 1024, 3)
+    t = df11.compress(wm, shape=(256, 1024))
+    t.use_decode_table(False)
+    _check_linear(torch, t, wm, _tokens(3, 1024, 4), 256, 1024)
+
+
 def test_launches_on_two_streams_are_serialised(torch_cuda):
     """Launches of one tensor share its work counters, so the binding orders
     a launch after the tensor's previous one when that went to another

@@ -210,6 +210,14 @@ def test_decompress_validation_runs_before_any_launch():
     bad = _lib.DeviceStream.from_buffer_copy(s)
     bad.decode_table_bits = 9
     assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    # without a decode table (the kernel derives it), the width must still be 10..12, or 0
+    bad.decode_table = None
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    bad.decode_table_bits = 13
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
+    bad.decode_table_bits = 0
+    bad.h.enc_bytes += 16  # (a later check still fails: nothing is launched)
+    assert lib.df11_decompress(ctypes.byref(bad), out, None) == -6
     bad = _lib.DeviceStream.from_buffer_copy(s)
     bad.sm = (1 << 40) + 8  # misaligned
     assert lib.df11_decompress(ctypes.byref(bad), out, None) == -1
@@ -575,3 +583,81 @@ def test_element_limit_of_a_stream():
         assert got == rc, n
         if rc == 0:
             assert h.n_elements == n and h.sm_bytes == -(-n // 64) * 64
+
+
+def _tile_order_reference(w, rows, cols):
+    """MFMA tile order from its definition: position (p, ks, nt, l, j) holds
+    W[64 p + 16 nt + l % 16][32 ks + 8 (l // 16) + j]; numpy axes
+    (p, nt, l % 16, ks, l // 16, j) put in the order (p, ks, nt, l // 16, l % 16, j)."""
+    t = w.reshape(rows // 64, 4, 16, cols // 32, 4, 8)
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2, 5)).reshape(-1)
+
+
+def test_tile_order_matches_its_definition():
+    _lib_or_skip()
+    rng = np.random.default_rng(3)
+    for rows, cols in ((64, 32), (128, 96), (192, 4096), (64, 14336)):
+        w = rng.integers(0, 1 << 16, rows * cols, dtype=np.uint16)
+        got = df11.tile_order(w, rows, cols)
+        assert np.array_equal(got, _tile_order_reference(w, rows, cols)), (rows, cols)
+    # spot checks straight from the formula, one element at a time
+    rows, cols = 128, 96
+    w = np.arange(rows * cols, dtype=np.uint32).astype(np.uint16)
+    got = df11.tile_order(w, rows, cols)
+    for s in rng.integers(0, rows * cols, 200):
+        p, q = divmod(int(s), 64 * cols)
+        ks, u = divmod(q, 2048)
+        nt, v = divmod(u, 512)
+        lane, j = divmod(v, 8)
+        r, c = 64 * p + 16 * nt + lane % 16, 32 * ks + 8 * (lane // 16) + j
+        assert got[s] == w[r * cols + c]
+
+
+def test_tile_order_errors():
+    lib = _lib_or_skip()
+    w = np.zeros(64 * 32, np.uint16)
+    out = np.zeros_like(w)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))  # noqa: E731
+    assert lib.df11_tile_order(p(w), 64, 32, p(out)) == 0
+    assert lib.df11_tile_order(p(w), 32, 64, p(out)) == -1    # rows not a multiple of 64
+    assert lib.df11_tile_order(p(w), 64 * 2, 16, p(out)) == -1  # cols not a multiple of 32
+    assert lib.df11_tile_order(None, 64, 32, p(out)) == -1
+    assert lib.df11_tile_order(p(w), 64, 32, p(w)) == -1      # in place
+
+
+def test_matmul_validation_runs_before_any_launch():
+    lib = _lib_or_skip()
+    w = workloads.gen_single_matrix(rows=128, cols=1024)
+    host = df11.encode(df11.tile_order(w, 128, 1024))
+    s = _fake_device_stream(host)
+    s.tile_cols = 1024
+    x, y = ctypes.c_void_p(1 << 46), ctypes.c_void_p(1 << 47)
+
+    def call(st, t=4, i=1024, o=128, xp=x, yp=y):
+        return lib.df11_matmul(ctypes.byref(st) if st is not None else None, xp, t, i, o, yp, None)
+
+    assert call(None) == -1
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.tile_cols = 0                    # a stream in row order
+    assert call(bad) == -1
+    bad.tile_cols = 512                  # tile columns that do not match in_features
+    assert call(bad) == -1
+    bad.tile_cols = 48                   # not a multiple of 32
+    assert call(bad) == -1
+    assert call(s, t=0) == -1            # no tokens
+    assert call(s, i=512, o=256) == -1   # in_features does not match the tile columns
+    assert call(s, xp=ctypes.c_void_p((1 << 46) + 8)) == -1  # x not 16-byte aligned
+    assert call(s, yp=ctypes.c_void_p(s.sm)) == -1  # y overlaps the stream
+    assert call(s, yp=ctypes.c_void_p((1 << 46) + 64)) == -1  # y overlaps x
+    assert call(s, t=1 << 26) == -7      # n_tokens * out_features >= 2^32
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.enc_bytes += 16
+    assert call(bad) == -6
+    # the row-order product takes no tiled stream
+    assert lib.df11_linear(ctypes.byref(s), x, 1, 1024, 128, y, None) == -1
+    assert lib.df11_matmul_acc(ctypes.byref(s), x, 4, 1024, 64, y, None) == -1
+    assert lib.df11_matmul_timed(ctypes.byref(s), x, 0, 1024, 128, y, None, None, None) == -1
+    # decompressing a tiled stream checks its shape: N a multiple of 64 * tile_cols
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.tile_cols = 96
+    assert lib.df11_decompress(ctypes.byref(bad), ctypes.c_void_p(1 << 48), None) == -1
