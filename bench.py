@@ -303,6 +303,41 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
         f.write("\n".join(lines))
 
 
+def summarize_matmul_profile(prof_dir: str, sub: str, command: str) -> None:
+    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of
+    bench.py --matmul-tokens T (prof_dir/sub, its line in prof_dir/sub.json):
+    the stats table and the seven-product batched kernel's timed launches
+    (trace timestamps) against the bench line."""
+    with open(os.path.join(prof_dir, sub + ".json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    stats = _read_csv(os.path.join(prof_dir, sub, "run_kernel_stats.csv"))
+    rows = [r for r in _read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv"))
+            if "df11_gemm_batch_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    n = bench["launches"]
+    timed = rows[n["check"] + n["warmup"]:n["check"] + n["warmup"] + n["timed"]]
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    T = bench["config"]["tokens"]
+    avg = float(np.mean(us))
+    hbm = bench["config"]["compressed_bytes"] + sum(2 * T * c + 4 * T * r for r, c in bench["config"]["shapes"].values())
+    lines = [f"# df11_gemm_batch_kernel on llama3_8b_block_matmul ({T} token{'s' if T > 1 else ''}): "
+             "rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box; "
+             "R = repository root, D = R/gpurun_out/prof):", "", "    " + command, "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']}% |")
+    lines += ["", f"The {len(us)} timed launches of the batched fused kernel (all seven products in one launch; the "
+              "kernel calls above also count the forward's smaller batches): trace average "
+              f"{avg:.2f} us (min {min(us):.2f}, max {max(us):.2f}); {hbm / (avg * 1e-6) / 1e9:.1f} GB/s of "
+              f"compressed weights + x + y, {hbm / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s; "
+              f"{2.0 * T * bench['config']['n_elements'] / (avg * 1e-6) / 1e12:.2f} TFLOP/s.  The bench line's "
+              f"events give {bench['kernel_ms'] * 1e3:.2f} us per step (the fused kernel plus one zeroing kernel).",
+              "", "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+    with open(os.path.join(REPO, "profiles", f"df11_gemm_kernel_llama3_8b_block_t{T}_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 # The two rocprofv3 --pmc passes of the instruction-mix summary.  Each stays
 # within one pass's hardware limits (8 SQ counters, counting those that the
 # derived metrics VALUBusy, LDSBankConflict and VALUUtilization read, and one
@@ -686,7 +721,18 @@ def matmul_bench(args, dev) -> int:
     hbm_bytes = comp + sum(2 * T * m[2] + 4 * T * m[1] for m in mats)
     flops = 2.0 * T * n
 
-    def step():
+    tensors, xlist, ylist = [m[3] for m in mats], [m[5] for m in mats], [m[6] for m in mats]
+
+    def step():  # the seven products in one launch (df11_matmul_batch)
+        df11.matmul_batch(tensors, xlist, outs=ylist)
+
+    by = {m[0]: m for m in mats}
+
+    def step_forward():  # as a forward issues them: q, k, v; o; gate, up; down
+        for group in (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",)):
+            df11.matmul_batch([by[g][3] for g in group], [by[g][5] for g in group], outs=[by[g][6] for g in group])
+
+    def step_seven():  # one launch per product
         for _, _, _, t, _, x, y in mats:
             t.matmul(x, out=y)
 
@@ -720,6 +766,8 @@ def matmul_bench(args, dev) -> int:
     for _ in range(args.warmup):
         step()
     fused_ms, wall_ms = timed(step, args.steps)
+    forward_ms, _ = timed(step_forward, max(3, args.steps // 2))
+    seven_ms, _ = timed(step_seven, max(3, args.steps // 2))
     scratch = torch.empty(max(m[1] * m[2] for m in mats), dtype=torch.bfloat16, device=dev)
     resident_ms, _ = timed(lambda: [F.linear(m[5], m[4]) for m in mats], max(3, args.steps // 2))
     decode_gemm_ms, _ = timed(lambda: [F.linear(m[5], m[3].decompress(out=scratch[:m[1] * m[2]].view(m[1], m[2])))
@@ -751,15 +799,20 @@ def matmul_bench(args, dev) -> int:
                    "layout": "mfma_tiles", "n_elements": n, "compressed_bytes": comp},
         "roofline": roof,
         "kernel_ms": round(fused_ms, 5),
-        "kernel_ms_note": "HIP events around the timed steps / steps: seven products, each a zeroing kernel and "
-                          "the fused kernel",
+        "kernel_ms_note": "HIP events around the timed steps / steps: one zeroing kernel and one batched fused "
+                          "kernel for the seven products",
         "arithmetic_intensity_flop_per_byte": round(intensity, 2),
         "achieved_tflops": round(tflops, 2),
         "achieved_hbm_gbps": round(gbps, 1),
         "same_run_ms_per_step": {"fused_df11_matmul": round(fused_ms, 4),
+                                 "fused_df11_matmul_as_a_forward_issues_it": round(forward_ms, 4),
+                                 "fused_df11_matmul_seven_launches": round(seven_ms, 4),
                                  "resident_bf16_F_linear": round(resident_ms, 4),
                                  "decode_then_F_linear": round(decode_gemm_ms, 4)},
         "outputs": "within the float32 summation bound of a float64 product (every token up to 64, a sample above)",
+        # launches of the batched fused kernel with all seven products, in order (then the forward's
+        # four batches per step, then single-product kernels)
+        "launches": {"check": 1, "warmup": args.warmup + 3, "timed": args.steps},
         "host_prep_s": round(t_prep, 1),
     }
     print(json.dumps(result), flush=True)
@@ -824,6 +877,10 @@ def main() -> int:
                                      pre + "rocprofv3 --kernel-trace --stats -d $D/lin_trace -o run --output-format csv "
                                            "-- python3 $R/bench.py --linear-tokens 1 --steps 50 --warmup 20 "
                                            "--no-cpu-baseline > $D/lin.json")
+        for T in (1, 16, 64, 256):
+            if have(f"mm{T}"):
+                summarize_matmul_profile(args.summarize_profiles, f"mm{T}",
+                                         trace.format(sub=f"mm{T}", args=f"--matmul-tokens {T} --steps 20 --warmup 5"))
         if have("rans_trace"):
             summarize_decode_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
                                    "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",

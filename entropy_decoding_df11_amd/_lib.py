@@ -54,6 +54,7 @@ EXPORTED = [
     "df11_matmul",
     "df11_matmul_acc",
     "df11_matmul_timed",
+    "df11_matmul_batch",
     "df11_linear",
     "df11_linear_timed",
     "df11_linear_batch",
@@ -199,6 +200,10 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),
         "df11_matmul_timed": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
+        "df11_matmul_batch": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_uint32,
+                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32, u32p, u32p,
+                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p]),
         "df11_linear": (ctypes.c_int, [ctypes.POINTER(DeviceStream), ctypes.c_void_p, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]),

@@ -639,7 +639,7 @@ __device__ __forceinline__ void flush_rows(const MatmulArgs &m, float *yacc, uin
 // them).  Each wave keeps the running 16 x 16 sums of its n-tile for MT
 // tiles of 16 tokens of the current pass, and adds them into y when its
 // panel or pass changes, or at the end (float atomics: the groups of a panel
-// can lie in several workgroups).  x must hold finite values.
+// lie in several workgroups).  x must hold finite values.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -682,10 +682,45 @@ __device__ __forceinline__ void load_xa(const DecodeArgs &a, const MatmulArgs &m
     }
 }
 
+// The x operands of a group's first kXTiles rounds are staged in LDS for
+// the merge (one copy per group slot, read by its four waves, which would
+// otherwise each load the same tiles): a 1 KB tile per (round, token tile),
+// lane l's 16 bytes at 16 l.  The four waves load them straight from
+// global memory into LDS (global_load_lds_dwordx4, no registers), each a
+// quarter of the tiles, right after the scan barrier of the iteration that
+// decodes the group: every wave has finished the previous merge's reads by
+// then, so one buffer per slot suffices; the loads land during phase 2 and
+// are waited for before the iteration's last barrier.  Rounds past
+// kXTiles (groups of more than about 1000 chunks) load theirs in the round.
+template <int MT>
+constexpr int kXTiles = MT <= 2 ? 4 : 2;
+
+template <int MT>
+__device__ __forceinline__ void stage_x(const DecodeArgs &a, const MatmulArgs &m, uint32_t base, uint32_t pass,
+                                        uint32_t wave, uint32_t lane, uint8_t *s_x) {
+    // (global_load_lds writes lane l's 16 bytes at the wave-uniform LDS
+    // address + 16 l)
+    const uint32_t g0 = base >> 11;
+    wave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int q = 0; q < kXTiles<MT> * MT; q += 4) {
+        const uint32_t tile = q + wave;  // (round tile / MT, token tile tile % MT)
+        if (tile < static_cast<uint32_t>(kXTiles<MT> * MT)) {
+            const uint32_t g = g0 + tile / MT, mt = tile % MT;
+            const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
+            const uint32_t col = 32u * (g - panel * a.tile_ks) + 8u * (lane >> 4);
+            const uint32_t t = min((pass * MT + mt) * 16u + (lane & 15u), m.n_tokens - 1u);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(m.x + static_cast<size_t>(t) * m.in_features + col),
+                (__attribute__((address_space(3))) void *)(s_x + 1024u * tile), 16, 0, 0);
+        }
+    }
+}
+
 template <int MT>
 __device__ __forceinline__ void merge_mfma(const DecodeArgs &a, const MatmulArgs &m, uint8_t *ebuf,
                                            const uint64_t (&sm)[kPrefetchChunks], uint32_t base, uint32_t end,
-                                           uint32_t pass, uint32_t ltid, PanelSums<MT> &ps) {
+                                           uint32_t pass, uint32_t ltid, PanelSums<MT> &ps, const uint8_t *s_x) {
     const uint32_t c0 = base >> 3;
     const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
     const uint32_t lead = c0 & 255u;
@@ -694,21 +729,11 @@ __device__ __forceinline__ void merge_mfma(const DecodeArgs &a, const MatmulArgs
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
     if (n_chunks == 0) return;
     const uint32_t g0 = c0 >> 8;
-    uint4 xa[MT], xn[MT];
-    load_xa<MT>(a, m, g0, pass, lane, xa);
-    for (uint32_t j = 0; j < rounds; ++j) {
-        if (j + 1 < rounds) load_xa<MT>(a, m, g0 + j + 1, pass, lane, xn);
+    auto round = [&](uint32_t j, const uint4 (&xa)[MT], uint64_t s8) {
         const uint32_t kk = ltid + 256u * j;
         const uint32_t k = kk - lead;
         const bool in = kk >= lead && k < n_chunks;
-        uint64_t s8 = 0, r8 = 0;
-        if (j < static_cast<uint32_t>(kPrefetchChunks)) {
-#pragma unroll
-            for (int q = 0; q < kPrefetchChunks; ++q)
-                if (j == static_cast<uint32_t>(q)) s8 = sm[q];
-        } else if (in) {
-            s8 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + k)));
-        }
+        uint64_t r8 = 0;
         if (in) {
             uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
             r8 = *cell;
@@ -735,8 +760,35 @@ __device__ __forceinline__ void merge_mfma(const DecodeArgs &a, const MatmulArgs
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             ps.d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mt]), b, ps.d[mt], 0, 0, 0);
+    };
+    // (sm holds the chunks of rounds 0 .. kPrefetchChunks - 1, load_sm)
+    static_assert(kXTiles<MT> <= kPrefetchChunks, "staged rounds must have their sign/mantissa chunks");
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xa[mt] = xn[mt];
+    for (int j = 0; j < kXTiles<MT>; ++j) {
+        if (static_cast<uint32_t>(j) < rounds) {
+            uint4 xa[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                // (tokens past n_tokens were staged from the last token: zero them)
+                const uint4 v = *reinterpret_cast<const uint4 *>(s_x + 1024u * (j * MT + mt) + 16u * lane);
+                xa[mt] = (pass * MT + mt) * 16u + (lane & 15u) < m.n_tokens ? v : make_uint4(0, 0, 0, 0);
+            }
+            round(j, xa, sm[j]);
+        }
+    }
+    for (uint32_t j = kXTiles<MT>; j < rounds; ++j) {
+        uint4 xa[MT];
+        load_xa<MT>(a, m, g0 + j, pass, lane, xa);
+        uint64_t s8 = 0;
+        const uint32_t kk = ltid + 256u * j;
+        if (j < static_cast<uint32_t>(kPrefetchChunks)) {
+#pragma unroll
+            for (int q = 0; q < kPrefetchChunks; ++q)
+                if (j == static_cast<uint32_t>(q)) s8 = sm[q];
+        } else if (kk >= lead && kk - lead < n_chunks) {
+            s8 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * (c0 + kk - lead)));
+        }
+        round(j, xa, s8);
     }
 }
 
@@ -941,8 +993,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     float *s_yacc = reinterpret_cast<float *>(s_ticket + 4) + slot * m.yacc_rows * kRowTB;
     // Only for a stream without a decode table: the first code of each
     // window, while the table is derived (2^K uint16).
-    uint16_t *s_first =
-        reinterpret_cast<uint16_t *>(reinterpret_cast<float *>(s_ticket + 4) + GPW * m.yacc_rows * kRowTB);
+    constexpr uint32_t kXBytes = TB < 0 ? GPW * kXTiles<(TB < 0 ? -TB : 1)> * (TB < 0 ? -TB : 1) * 1024u : 0u;
+    uint16_t *s_first = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(
+                                                         reinterpret_cast<float *>(s_ticket + 4) + GPW * m.yacc_rows * kRowTB) +
+                                                     kXBytes);
     uint32_t y_row0 = 0, y_rows = 0;  // rows of the merged group awaiting flush_rows
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
@@ -954,8 +1008,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     // The matrix-core product (TB < 0, MT = -TB tiles of 16 tokens) gives
     // each workgroup a contiguous range of super-groups [r0, r0 + len),
     // swept m.passes times (16 MT tokens each), so that consecutive groups
-    // of a workgroup mostly share a panel and its sums stay in registers.
-    // Its iterations are numbered v = pass * len + (super-group - r0).
+    // of a workgroup mostly share a panel and its sums stay in registers
+    // (dealing the super-groups out round-robin, with a flush of the sums
+    // after every group, took twice as long at 16 tokens).  Its iterations
+    // are numbered v = pass * len + (super-group - r0).
     constexpr bool kMfma = TB < 0;
     constexpr int MT = kMfma ? -TB : 1;
     const uint32_t r0 = kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg) * n_super / n_wg) : 0u;
@@ -964,6 +1020,8 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     // Super-group of iteration v (n_super past the end).
     auto super_of = [&](uint32_t v) -> uint32_t { return kMfma ? (v < v_end ? r0 + v % len : n_super) : v; };
     PanelSums<MT> ps;
+    // matrix-core product: the next merge's staged x tiles (stage_x)
+    uint8_t *s_x = reinterpret_cast<uint8_t *>(s_ticket + 4) + slot * kXTiles<MT> * MT * 1024u * (kMfma ? 1u : 0u);
     if constexpr (kMfma) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) ps.d[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1062,7 +1120,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
                 merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc,
                                  y_row0, y_rows);
         } else if constexpr (kMfma) {
-            if (it > 0) merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps);
+            if (it > 0) merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps, s_x);
         }
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
@@ -1137,6 +1195,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
             // of the iteration orders the zeroing before the next merge.
             flush_rows<TB>(m, s_yacc, y_row0, y_rows, ltid);
             y_rows = 0;
+        } else if constexpr (kMfma) {
+            // Every wave's merge has read the staged tiles: stage this group's.
+            stage_x<MT>(a, m, base, s_cur / len, wave, lane, s_x);
         }
         __builtin_amdgcn_s_setprio(1);
         uint32_t wave_off = 0;
@@ -1193,6 +1254,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
                 skip = boundary_codes<K>(pa, gap, 0, c, 0, false, s_lo, s_aux, s_start);
             s_edge[0] = skip;
         }
+        if constexpr (kMfma) __builtin_amdgcn_s_waitcnt(0);  // (stage_x's loads have landed)
         __syncthreads();
 
         prev_base = base;
@@ -1207,7 +1269,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     if constexpr (TB == 0) {
         merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
     } else if constexpr (kMfma) {
-        merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps);
+        merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps, s_x);
         flush_panel<MT>(m, ps, wave, lane);
     } else {
         merge_matmul<TB>(a, m, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_yacc, y_row0,
@@ -1268,10 +1330,17 @@ __global__ __launch_bounds__(256) void df11_zero_kernel(float *y, uint32_t n) {
 // merge_mfma).  y must be zero at the start, or hold what the products add to.
 constexpr int kGemmGPW = 2;
 
+// Waves per SIMD the matrix-core kernels are built for (registers per lane:
+// 80 at six waves, the decoder's occupancy).
+template <int MT>
+constexpr int kGemmWaves = MT == 1 ? 6 : MT == 2 ? 5 : 4;
+
 template <int K, int MT>
-__global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) void df11_gemm_kernel(DecodeArgs a, MatmulArgs m) {
+__global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) __attribute__((amdgpu_waves_per_eu(kGemmWaves<MT>)))
+void df11_gemm_kernel(DecodeArgs a, MatmulArgs m) {
     decode_stream<K, kGemmGPW, -MT>(a, m, blockIdx.x, gridDim.x);
 }
+
 
 // Several weight matrices multiplying the same x in one launch (a block's q,
 // k and v, or gate and up): the grid is split between them as for
@@ -1290,6 +1359,18 @@ __global__ __launch_bounds__(kThreadsPerGroup *kLinearGPW) void df11_linear_batc
     uint32_t i = 0;
     while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
     decode_stream<K, kLinearGPW, TB>(b.s[i], b.m[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+}
+
+// Several matrix-core products in one launch, the grid split between them
+// as for df11_decode_batch_kernel (LinearBatchArgs: each stream with its
+// own x, y and shape).
+template <int K, int MT>
+__global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) __attribute__((amdgpu_waves_per_eu(kGemmWaves<MT>)))
+void df11_gemm_batch_kernel(LinearBatchArgs b) {
+    const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
+    uint32_t i = 0;
+    while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
+    decode_stream<K, kGemmGPW, -MT>(b.s[i], b.m[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
 }
 
 // Zero several outputs: y[i] has end[i] - end[i - 1] floats (end[-1] = 0).
@@ -1784,10 +1865,14 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
 // The matrix-core product: y = 0 (unless accumulating), then the fused
 // kernel over as many workgroups as fit at once (at most one per
 // super-group), each with a contiguous range of the stream.
+// LDS of the staged x tiles of a matrix-core workgroup (stage_x).
+template <int MT>
+constexpr size_t kGemmXBytes = kGemmGPW * kXTiles<MT> * MT * 1024u;
+
 template <int K, int MT>
 int launch_gemm(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
                 hipEvent_t stop, bool zero) {
-    const size_t lds = dynamic_lds<K, kGemmGPW>(a);
+    const size_t lds = dynamic_lds<K, kGemmGPW>(a, kGemmXBytes<MT>);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_gemm_kernel<K, MT>);
@@ -1876,6 +1961,107 @@ int gemm_impl(const df11_device_stream *s, const uint16_t *x, uint32_t n_tokens,
 #undef DF11_GEMM_CASE
 }
 
+// Several matrix-core products in one launch: every output zeroed by one
+// kernel (unless accumulating), then the batched fused kernel over the
+// resident grid split between the streams in proportion to their
+// super-groups (every stream sweeps its range the same number of times).
+template <int K, int MT>
+int launch_gemm_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
+                      hipEvent_t stop, bool zero) {
+    size_t lds = 0;
+    for (uint32_t i = 0; i < b.n; ++i) lds = std::max(lds, dynamic_lds<K, kGemmGPW>(b.s[i], kGemmXBytes<MT>));
+    int dev = 0, cus = 0;
+    if (device_cus(dev, cus)) return DF11_E_HIP;
+    const void *fn = reinterpret_cast<const void *>(&df11_gemm_batch_kernel<K, MT>);
+    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    if (per_cu < 1) return DF11_E_HIP;
+    uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
+    uint64_t sup[kMaxBatch], want[kMaxBatch];
+    for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + kGemmGPW - 1) / kGemmGPW;
+    df11::split_grid(sup, b.n, resident, want);
+    uint32_t next = 0;
+    for (uint32_t i = 0; i < b.n; ++i) {
+        b.s[i].sched = nullptr;  // (contiguous ranges: no dynamic schedule)
+        b.m[i].passes = (b.m[i].n_tokens + 16u * MT - 1u) / (16u * MT);
+        b.wg_begin[i] = next;
+        next += static_cast<uint32_t>(want[i]);
+    }
+    b.wg_begin[b.n] = next;
+    b.stride = df11::coprime_stride(next);
+    (void)hipGetLastError();
+    if (zero) {
+        const uint32_t total = z.end[z.n - 1];
+        void *zparams[] = {&z};
+        const uint32_t zgrid = std::max<uint32_t>(1, std::min<uint32_t>((total + 255) / 256, 1024));
+        const int rc = launch_kernel(reinterpret_cast<const void *>(&df11_zero_batch_kernel), dim3(zgrid), dim3(256),
+                                     zparams, 0, stream, nullptr, nullptr);
+        if (rc) return rc;
+    }
+    void *params[] = {&b};
+    return launch_kernel(fn, dim3(next), dim3(kThreadsPerGroup * kGemmGPW), params, lds, stream, start, stop);
+}
+
+int gemm_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *const *xs, uint32_t n_tokens,
+                    const uint32_t *in_features, const uint32_t *out_features, float *const *ys, hipStream_t stream,
+                    hipEvent_t start, hipEvent_t stop, bool zero) {
+    if (n > kMaxBatch) return DF11_E_TOO_LARGE;
+    if (n && (!ws || !xs || !in_features || !out_features || !ys)) return DF11_E_INVALID_ARG;
+    LinearBatchArgs b{};
+    ZeroArgs z{};
+    uint32_t bits = 0, max_wg = 0, total = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        DecodeArgs a;
+        MatmulArgs m;
+        bool empty = false;
+        const int rc = gemm_args(&ws[i], xs[i], n_tokens, in_features[i], out_features[i], ys[i], a, m, empty);
+        if (rc) return rc;
+        // every output must also stay clear of the other outputs, every x and the other streams' buffers
+        const uint64_t y_bytes = 4ull * n_tokens * out_features[i];
+        for (uint32_t j = 0; j < n && !empty; ++j) {
+            if (overlaps(ys[i], y_bytes, xs[j], 2ull * n_tokens * in_features[j])) return DF11_E_INVALID_ARG;
+            if (j == i) continue;
+            const df11_device_stream &o = ws[j];
+            if (overlaps(ys[i], y_bytes, ys[j], 4ull * n_tokens * out_features[j]) ||
+                overlaps(ys[i], y_bytes, o.enc, o.h.enc_bytes) || overlaps(ys[i], y_bytes, o.sm, o.h.sm_bytes) ||
+                overlaps(ys[i], y_bytes, o.gaps, o.h.gaps_bytes) ||
+                overlaps(ys[i], y_bytes, o.out_pos, o.h.out_pos_bytes) ||
+                overlaps(ys[i], y_bytes, o.luts, 256ull * o.h.n_luts) ||
+                overlaps(ys[i], y_bytes, o.code_lengths, 256) ||
+                overlaps(ys[i], y_bytes, o.decode_table, df11_decode_table_bytes(table_bits(&o))))
+                return DF11_E_INVALID_ARG;
+        }
+        if (empty) continue;
+        if (b.n && table_bits(&ws[i]) != bits) return DF11_E_INVALID_ARG;
+        bits = table_bits(&ws[i]);
+        if (ws[i].max_workgroups) max_wg = max_wg ? std::min(max_wg, ws[i].max_workgroups) : ws[i].max_workgroups;
+        if (static_cast<uint64_t>(total) + static_cast<uint64_t>(n_tokens) * out_features[i] >= (1ull << 32))
+            return DF11_E_TOO_LARGE;
+        total += n_tokens * out_features[i];
+        z.y[b.n] = ys[i];
+        z.end[b.n] = total;
+        b.s[b.n] = a;
+        b.m[b.n] = m;
+        ++b.n;
+    }
+    if (b.n == 0) return DF11_OK;
+    z.n = b.n;
+#define DF11_GEMM_BATCH_CASE(KB)                                                                \
+    case KB:                                                                                    \
+        switch (gemm_tiles(n_tokens)) {                                                         \
+        case 1: return launch_gemm_batch<KB, 1>(b, z, max_wg, stream, start, stop, zero);        \
+        case 2: return launch_gemm_batch<KB, 2>(b, z, max_wg, stream, start, stop, zero);        \
+        default: return launch_gemm_batch<KB, 4>(b, z, max_wg, stream, start, stop, zero);       \
+        }
+    switch (bits) {
+        DF11_GEMM_BATCH_CASE(10)
+        DF11_GEMM_BATCH_CASE(11)
+        DF11_GEMM_BATCH_CASE(12)
+    default: return DF11_E_INVALID_ARG;
+    }
+#undef DF11_GEMM_BATCH_CASE
+}
+
 // The allocation-free batched decode's work counters: one set of
 // DF11_SCHEDULE_WORDS words per stream of a call, in a file-scope device
 // array that every call on a GPU shares (each GPU holds its own copy until
@@ -1956,6 +2142,14 @@ int df11_matmul_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_t
                     uint32_t out_features, float *y, void *hip_stream) {
     return gemm_impl(w, x, n_tokens, in_features, out_features, y, static_cast<hipStream_t>(hip_stream), nullptr,
                      nullptr, false);
+}
+
+int df11_matmul_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *const *xs, uint32_t n_tokens,
+                      const uint32_t *in_features, const uint32_t *out_features, float *const *ys, int accumulate,
+                      void *hip_stream, void *start_event, void *stop_event) {
+    return gemm_batch_impl(ws, n_streams, xs, n_tokens, in_features, out_features, ys,
+                           static_cast<hipStream_t>(hip_stream), static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event), accumulate == 0);
 }
 
 int df11_matmul_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,

@@ -376,6 +376,55 @@ class DF11Tensor:
         return out
 
 
+def matmul_batch(tensors: Sequence[DF11Tensor], xs: Sequence["torch.Tensor"], outs=None, stream=None,  # noqa: F821
+                 events=None, accumulate: bool = False) -> List["torch.Tensor"]:  # noqa: F821
+    """[xs[i] W_i^T for each W_i in tensors] on the matrix cores in one launch
+    (df11_matmul_batch): every W_i compressed with layout="mfma_tiles", every
+    xs[i] a contiguous bfloat16 (n_tokens, in_features_i) tensor with the
+    same n_tokens (the same tensor may serve several weights).  Returns the
+    float32 outputs (new tensors by default); events as for
+    DF11Tensor.decompress.  With accumulate, each of outs (required)
+    receives outs[i] + xs[i] W_i^T."""
+    import torch
+    if not tensors:
+        return []
+    if len(tensors) > _lib.MAX_BATCH or len(xs) != len(tensors):
+        raise ValueError(f"one x per weight, at most {_lib.MAX_BATCH} weights per launch")
+    n_tokens = None
+    for t, x in zip(tensors, xs):
+        if len(t.shape) != 2 or not t.tile_cols:
+            raise ValueError("every weight must be 2-D and compressed with layout='mfma_tiles'")
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != t.shape[1] or not x.is_contiguous():
+            raise ValueError("each x must be a contiguous bfloat16 (n_tokens, in_features) tensor")
+        if n_tokens is not None and x.shape[0] != n_tokens:
+            raise ValueError("every x must have the same number of tokens")
+        n_tokens = x.shape[0]
+        if not _on_device(x, t.device):
+            raise ValueError("every x must be on its weight's device")
+    if outs is None:
+        if accumulate:
+            raise ValueError("accumulate needs outs")
+        outs = [torch.empty((n_tokens, t.shape[0]), dtype=torch.float32, device=t.device) for t in tensors]
+    for t, y in zip(tensors, outs):
+        if y.dtype != torch.float32 or y.shape != (n_tokens, t.shape[0]) or not y.is_contiguous():
+            raise ValueError("each output must be a contiguous float32 (n_tokens, out_features) tensor")
+        if not _on_device(y, t.device):
+            raise ValueError("every output must be on its weight's device")
+    lib = _lib.load()
+    st = [t._claim(stream) for t in tensors][0]
+    n = len(tensors)
+    arr = (_lib.DeviceStream * n)(*[t._stream_struct for t in tensors])
+    in_f = np.array([t.shape[1] for t in tensors], np.uint32)
+    out_f = np.array([t.shape[0] for t in tensors], np.uint32)
+    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in outs])
+    ev = (None, None) if events is None else (ctypes.c_void_p(_event_handle(events[0], st)),
+                                              ctypes.c_void_p(_event_handle(events[1], st)))
+    _lib.check(lib.df11_matmul_batch(arr, n, xp, n_tokens, _ptr(in_f, ctypes.c_uint32), _ptr(out_f, ctypes.c_uint32),
+                                     yp, 1 if accumulate else 0, st, *ev), "df11_matmul_batch")
+    return outs
+
+
 def linear_batch(tensors: Sequence[DF11Tensor], x: "torch.Tensor", outs=None, stream=None,  # noqa: F821
                  events=None, accumulate: bool = False) -> List["torch.Tensor"]:  # noqa: F821
     """[x W_i^T for each W_i in tensors] in one launch (df11_linear_batch):

@@ -440,6 +440,30 @@ int df11_matmul_acc(const df11_device_stream *w, const uint16_t *x, uint32_t n_t
 int df11_matmul_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n_tokens, uint32_t in_features,
                       uint32_t out_features, float *y, void *hip_stream, void *start_event, void *stop_event);
 
+/* df11_matmul for several weight matrices in one launch, each with its own
+ * x and y (a transformer block's q, k and v on one x, or gate and up; or
+ * every product of a step), the grid split between them in proportion to
+ * their work: small matrices alone cannot fill the GPU, and one launch pays
+ * one start and one tail.
+ *   ws            host array of n_streams device streams, as for df11_matmul;
+ *                 the non-empty ones must share decode_table_bits
+ *   xs            host array of device x pointers (xs[i]: n_tokens x
+ *                 in_features[i] BF16), may repeat
+ *   in_features, out_features   host arrays, as for df11_matmul
+ *   ys            host array of device outputs, n_tokens x out_features[i]
+ *                 floats, overlapping neither each other, any x nor any
+ *                 stream's buffers
+ *   accumulate    0: every output is overwritten (one zeroing kernel runs
+ *                 first); else ys[i] += xs[i] W_i^T
+ *   start_event, stop_event   hipEvent_t or NULL, recorded at the fused
+ *                 kernel's own start and end
+ * Errors: DF11_E_TOO_LARGE (n_streams > DF11_MAX_BATCH, the outputs' total
+ * >= 2^32 floats), as for df11_matmul otherwise.  Nothing is launched unless
+ * every stream is valid. */
+int df11_matmul_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *const *xs, uint32_t n_tokens,
+                      const uint32_t *in_features, const uint32_t *out_features, float *const *ys, int accumulate,
+                      void *hip_stream, void *start_event, void *stop_event);
+
 /* ---------------------------------------------------------------------------
  * rANS exponent coder.  The discussion on the page ("Opini Hacker News")
  * names rANS as an entropy coder that suits SIMD-style instruction sets better

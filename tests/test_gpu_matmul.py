@@ -170,3 +170,58 @@ def test_matmul_full_size_block_matrix(torch_cuda, name, n_tokens):
     err = np.abs(got - ref)
     assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
     assert np.all(np.isfinite(y.cpu().numpy()))
+
+
+@pytest.mark.parametrize("n_tokens", [1, 16, 40])
+def test_matmul_batch_matches_oracle(torch_cuda, n_tokens):
+    """Several products in one launch (df11_matmul_batch): shapes of a
+    block's projections scaled down, two of them sharing one x, an empty
+    weight skipped; then accumulating into the outputs."""
+    torch = torch_cuda
+    _note(f"matmul batch tokens={n_tokens}")
+    shapes = [(256, 1024), (64, 1024), (64, 1024), (0, 1024), (512, 2048), (128, 4096)]
+    ws, ts, xs, refs, bounds = [], [], [], [], []
+    x_by_cols = {}
+    for i, (r, c) in enumerate(shapes):
+        w = _weights("student_t" if i % 2 else "normal", r * c, 40 + i)
+        if c not in x_by_cols:
+            x_by_cols[c] = _tokens(n_tokens, c, c + n_tokens)
+        xb = x_by_cols[c]
+        ws.append(w)
+        ts.append(df11.compress(w, shape=(r, c), layout="mfma_tiles"))
+        xs.append(_device_x(torch, xb))
+        refs.append(oracle.linear(oracle.encode(w), xb, r) if r else np.zeros((n_tokens, 0)))
+        bounds.append(_bound(xb, w, r, c) if r else np.zeros((n_tokens, 0)))
+    xs[2] = xs[1]  # the same x for two weights
+    ys = df11.matmul_batch(ts, xs)
+    torch.cuda.synchronize()
+    for y, ref, bound in zip(ys, refs, bounds):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+    df11.matmul_batch(ts, xs, outs=ys, accumulate=True)
+    torch.cuda.synchronize()
+    for y, ref, bound in zip(ys, refs, bounds):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - 2 * ref)
+        assert np.all(err <= 2 * bound), (float(err.max()), float((err - 2 * bound).max()))
+
+
+def test_matmul_batch_full_block_one_token(torch_cuda):
+    """The whole Llama-3-8B block's seven products in one launch at one token:
+    every output row against the oracle."""
+    torch = torch_cuda
+    flat, views = workloads.gen_block()
+    _note("matmul batch: full block, 1 token")
+    ts, xs, checks = [], [], []
+    for nm, off, (r, c) in views:
+        w = np.ascontiguousarray(flat[off:off + r * c])
+        xb = _tokens(1, c, r)
+        ts.append(df11.compress(w, shape=(r, c), layout="mfma_tiles"))
+        xs.append(_device_x(torch, xb))
+        checks.append((w, xb, r, c))
+    del flat
+    ys = df11.matmul_batch(ts, xs)
+    torch.cuda.synchronize()
+    for y, (w, xb, r, c) in zip(ys, checks):
+        ref = oracle.linear(oracle.encode(w), xb, r)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= _bound(xb, w, r, c))

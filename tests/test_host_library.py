@@ -661,3 +661,35 @@ def test_matmul_validation_runs_before_any_launch():
     bad = _lib.DeviceStream.from_buffer_copy(s)
     bad.tile_cols = 96
     assert lib.df11_decompress(ctypes.byref(bad), ctypes.c_void_p(1 << 48), None) == -1
+
+
+def test_matmul_batch_validation_runs_before_any_launch():
+    lib = _lib_or_skip()
+    w = workloads.gen_single_matrix(rows=128, cols=1024)
+    host = df11.encode(df11.tile_order(w, 128, 1024))
+    s = _fake_device_stream(host)
+    s.tile_cols = 1024
+    x = 1 << 46
+
+    def call(streams, xs, ys, t=2, ins=None, outs_f=None, acc=0):
+        n = len(streams)
+        arr = (_lib.DeviceStream * max(n, 1))(*streams)
+        xp = (ctypes.c_void_p * max(n, 1))(*xs)
+        yp = (ctypes.c_void_p * max(n, 1))(*ys)
+        inf = np.array(ins or [1024] * n, np.uint32)
+        outf = np.array(outs_f or [128] * n, np.uint32)
+        return lib.df11_matmul_batch(arr, n, xp, t, inf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                     outf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), yp, acc, None, None, None)
+
+    assert lib.df11_matmul_batch(None, 0, None, 1, None, None, None, 0, None, None, None) == 0  # empty batch
+    assert lib.df11_matmul_batch(None, 1, None, 1, None, None, None, 0, None, None, None) == -1
+    y0, y1 = 1 << 47, (1 << 47) + (1 << 20)
+    assert call([s] * 17, [x] * 17, [y0 + (i << 20) for i in range(17)]) == -7  # too many streams
+    assert call([s, s], [x, x], [y0, y0 + 64]) == -1          # outputs overlap
+    assert call([s, s], [x, y1 + 8], [y0, y1]) == -1          # an output overlaps another product's x
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.tile_cols = 0
+    assert call([s, bad], [x, x], [y0, y1]) == -1             # one stream in row order: nothing launches
+    bad = _lib.DeviceStream.from_buffer_copy(s)
+    bad.h.enc_bytes += 16
+    assert call([s, bad], [x, x], [y0, y1], acc=1) == -6
