@@ -407,13 +407,14 @@ def integration(args, dev) -> int:
     graphs and replayed."""
     import torch
     from entropy_decoding_df11_amd import df11, runtime, workloads
-    blocks, resident, per_weight = [], [], []
+    blocks, resident, per_weight, tiled = [], [], [], []
     t0 = time.perf_counter()
     for b in range(args.blocks):
         flat, views = workloads.gen_block(seed=1000 + b)
         parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
         blocks.append(df11.compress_block(parts, device=dev))
         per_weight.append(df11.compress_block(parts, device=dev, codebook="per_weight"))
+        tiled.append(df11.compress_block(parts, device=dev, codebook="per_weight", layout="mfma_tiles"))
         resident.append({nm: torch.from_numpy(a.astype(np.int16)).to(dev).view(torch.bfloat16) for nm, a in parts})
     t_prep = time.perf_counter() - t0
     overlap = runtime.BlockDecoder(blocks, device=dev, overlap=True, decode_workgroups=args.overlap_workgroups)
@@ -422,6 +423,11 @@ def integration(args, dev) -> int:
 
     def fused_forward(x):
         for blk in per_weight:
+            x = runtime.fused_block_forward(x, blk)
+        return x
+
+    def tiled_forward(x):
+        for blk in tiled:
             x = runtime.fused_block_forward(x, blk)
         return x
 
@@ -450,24 +456,26 @@ def integration(args, dev) -> int:
         row = {"tokens": tokens, "ms_per_forward": res,
                "df11_overlap_vs_resident": round(res["df11_overlap"] / res["resident"], 3),
                "df11_inline_vs_resident": round(res["df11_inline"] / res["resident"], 3)}
-        if tokens <= 8:
+        for name, fwd, limit in (("df11_fused", fused_forward, 8), ("df11_fused_tiles", tiled_forward, 256)):
+            if tokens > limit:
+                continue
             for _ in range(3):
-                y = fused_forward(x)
+                y = fwd(x)
             torch.cuda.synchronize()
             # float32 sums in another order: close to, not equal to, the resident forward
             dev_max = float((y.float() - ref.float()).abs().max())
             if dev_max > 0.05 * float(ref.float().abs().max()):
-                print("integration: the fused forward is far from the resident-weight forward", file=sys.stderr)
+                print(f"integration: the {name} forward is far from the resident-weight forward", file=sys.stderr)
                 return 1
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(10):
-                fused_forward(x)
+                fwd(x)
             e1.record()
             torch.cuda.synchronize()
-            res["df11_fused"] = round(e0.elapsed_time(e1) / 10, 4)
-            row["df11_fused_vs_resident"] = round(res["df11_fused"] / res["resident"], 3)
-            row["df11_fused_max_abs_diff_over_max_abs"] = round(dev_max / float(ref.float().abs().max()), 5)
+            res[name] = round(e0.elapsed_time(e1) / 10, 4)
+            row[f"{name}_vs_resident"] = round(res[name] / res["resident"], 3)
+            row[f"{name}_max_abs_diff_over_max_abs"] = round(dev_max / float(ref.float().abs().max()), 5)
         if tokens <= 16:
             # The same forwards captured into HIP graphs (runtime.CapturedForward):
             # at a few tokens a forward is many small launches.
@@ -475,11 +483,12 @@ def integration(args, dev) -> int:
                       "df11_inline_graph": lambda x: runtime.model_forward(x, inline)}
             if tokens <= 8:
                 graphs["df11_fused_graph"] = fused_forward
+            graphs["df11_fused_tiles_graph"] = tiled_forward
             for name, fwd in graphs.items():
                 g = runtime.CapturedForward(fwd, x)
                 y = g(x)
                 torch.cuda.synchronize()
-                if name == "df11_fused_graph":
+                if name.startswith("df11_fused"):
                     ok = float((y.float() - ref.float()).abs().max()) <= 0.05 * float(ref.float().abs().max())
                 else:
                     ok = torch.equal(y.view(torch.int16), ref.view(torch.int16))
@@ -497,14 +506,17 @@ def integration(args, dev) -> int:
             row["df11_inline_graph_vs_resident_graph"] = round(res["df11_inline_graph"] / res["resident_graph"], 3)
             if tokens <= 8:
                 row["df11_fused_graph_vs_resident_graph"] = round(res["df11_fused_graph"] / res["resident_graph"], 3)
+            row["df11_fused_tiles_graph_vs_resident_graph"] = round(res["df11_fused_tiles_graph"]
+                                                                   / res["resident_graph"], 3)
         rows.append(row)
     comp = sum(b.tensor.compressed_bytes() for b in blocks)
     raw = sum(2 * b.n_elements for b in blocks)
     print(json.dumps({"integration": "synthetic model forward", "blocks": args.blocks,
                       "weights_per_block": int(blocks[0].n_elements),
                       "overlap_decode_workgroups": args.overlap_workgroups, "compressed_over_bf16": round(comp / raw, 4),
-                      "outputs": "in line and overlapped: bit-identical to the resident-weight forward; fused: "
-                                 "float32 sums in another order",
+                      "outputs": "in line and overlapped: bit-identical to the resident-weight forward; fused "
+                                 "(row-order product up to 8 tokens, matrix-core product on tile-ordered weights up "
+                                 "to 256): float32 sums in another order",
                       "host_prep_s": round(t_prep, 1),
                       "results": rows}), flush=True)
     return 0
@@ -832,6 +844,9 @@ def main() -> int:
                     help="the Llama-3-8B block (default), the same with a codebook per weight (one batched "
                          "launch), or one of the single-stream workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=["rows", "mfma_tiles"], default="rows",
+                    help="element order of each weight (llama3_8b_block_per_weight): its own, or the matrix-core "
+                         "product's tile order (decompressed back to row-major)")
     ap.add_argument("--no-decode-table", action="store_true",
                     help="launch with the page's arrays alone: every workgroup derives the first-level decode "
                          "table in LDS from the LUTs and CodeLengths")
@@ -939,7 +954,10 @@ def main() -> int:
     elif views is not None:
         codebook = "per_weight" if wl.endswith("_per_weight") else "shared"
         first = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views], device=dev,
-                                    decode_table_bits=args.decode_table_bits, codebook=codebook)
+                                    decode_table_bits=args.decode_table_bits, codebook=codebook,
+                                    layout=args.layout)
+        if args.layout != "rows":
+            config["layout"] = args.layout
         config["shapes"] = {name: list(shape) for name, _, shape in views}
         config["codebook"] = codebook
         if codebook == "shared":

@@ -684,19 +684,25 @@ class DF11BlockBatch:
 
 def compress_block(weights: Union[Dict[str, ArrayLike], List[Tuple[str, ArrayLike]]], device="cuda",
                    decode_table_bits: int = DEFAULT_DECODE_TABLE_BITS,
-                   codebook: str = "shared") -> Union[DF11Block, DF11BlockBatch]:
+                   codebook: str = "shared", layout: str = "rows") -> Union[DF11Block, DF11BlockBatch]:
     """Encode a block's weights for decompression in one launch.
 
     codebook="shared": concatenate them row-major in the given order, build
     one codebook from the summed histogram and encode one stream (DF11Block).
     codebook="per_weight": one stream and codebook per weight, decoded by a
-    batched launch (DF11BlockBatch, at most 16 weights)."""
+    batched launch (DF11BlockBatch, at most 16 weights); with
+    layout="mfma_tiles" each weight is stored in the order of the
+    matrix-core product (DF11Tensor.matmul, matmul_batch) and still
+    decompresses row-major."""
     items = list(weights.items()) if isinstance(weights, dict) else list(weights)
+    if layout != "rows" and codebook != "per_weight":
+        raise ValueError("layout='mfma_tiles' needs codebook='per_weight'")
     if codebook == "per_weight":
         tensors, views, off = [], [], 0
         for name, w in items:
             shape = tuple(int(s) for s in w.shape)
-            tensors.append(compress(_u16(w), shape=shape, device=device, decode_table_bits=decode_table_bits))
+            tensors.append(compress(_u16(w), shape=shape, device=device, decode_table_bits=decode_table_bits,
+                                    layout=layout))
             views.append((name, off, shape))
             off += (int(np.prod(shape)) + 7) // 8 * 8
         return DF11BlockBatch(tensors, views, off)

@@ -119,17 +119,31 @@ def block_forward(x, w: Dict, eps: float = 1e-5):
 
 
 def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
-    """block_forward with each projection's decode fused into its product
-    (df11_linear_batch for q, k, v and for gate, up; df11_linear for o and
-    down), for 1..8 tokens: blk holds one DF11 stream per weight, and no
-    weight is ever decompressed to HBM.  The products accumulate in float32
-    and are rounded to x's dtype, like the resident path's outputs, but in
-    another order, so the last bits can differ from block_forward's."""
+    """block_forward with each projection's decode fused into its product:
+    blk holds one DF11 stream per weight, and no weight is ever decompressed
+    to HBM.  Weights in MFMA tile order (compress_block(..., layout=
+    "mfma_tiles")) go through the matrix-core product (df11_matmul_batch:
+    q, k and v in one launch, o, gate and up in one, down), for any token
+    count; weights in row order through the row-order product
+    (df11_linear_batch / df11_linear), for 1..8 tokens.  The products
+    accumulate in float32 and are rounded to x's dtype, like the resident
+    path's outputs, but in another order, so the last bits can differ from
+    block_forward's."""
     import torch
     import torch.nn.functional as F
-    from .df11 import linear_batch
+    from .df11 import linear_batch, matmul_batch
 
     w = {nm: t for (nm, _, _), t in zip(blk.views, blk.tensors)}
+    tiled = all(t.tile_cols for t in blk.tensors)
+
+    def products(names_, xin, outs):
+        ts = [w[nm] for nm in names_]
+        if tiled:
+            matmul_batch(ts, [xin] * len(ts), outs=outs, accumulate=True)
+        elif len(ts) == 1:
+            ts[0].linear(xin, out=outs[0], accumulate=True)
+        else:
+            linear_batch(ts, xin, outs=outs, accumulate=True)
 
     def rms(h):
         return h * torch.rsqrt(h.float().pow(2).mean(-1, keepdim=True) + eps).to(h.dtype)
@@ -143,21 +157,22 @@ def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
     y = {nm: part.view(tokens, w[nm].shape[0]) for nm, part in zip(names, torch.split(buf, sizes))}
 
     h = rms(x).contiguous()
-    linear_batch([w["q_proj"], w["k_proj"], w["v_proj"]], h, outs=[y["q_proj"], y["k_proj"], y["v_proj"]],
-                 accumulate=True)
+    products(("q_proj", "k_proj", "v_proj"), h, [y["q_proj"], y["k_proj"], y["v_proj"]])
     q, k, v = (y[nm].to(x.dtype) for nm in ("q_proj", "k_proj", "v_proj"))
     rep = q.shape[-1] // k.shape[-1]
     a = q + (k * v).repeat_interleave(rep, dim=-1)
-    x = x + w["o_proj"].linear(a.contiguous(), out=y["o_proj"], accumulate=True).to(x.dtype)
+    products(("o_proj",), a.contiguous(), [y["o_proj"]])
+    x = x + y["o_proj"].to(x.dtype)
     h = rms(x).contiguous()
-    linear_batch([w["gate_proj"], w["up_proj"]], h, outs=[y["gate_proj"], y["up_proj"]], accumulate=True)
+    products(("gate_proj", "up_proj"), h, [y["gate_proj"], y["up_proj"]])
     g, u = (y[nm].to(x.dtype) for nm in ("gate_proj", "up_proj"))
-    x = x + w["down_proj"].linear((F.silu(g) * u).contiguous(), out=y["down_proj"], accumulate=True).to(x.dtype)
+    products(("down_proj",), (F.silu(g) * u).contiguous(), [y["down_proj"]])
+    x = x + y["down_proj"].to(x.dtype)
     return x
 
 
 def fused_model_forward(x, blocks: Sequence[DF11BlockBatch]):
-    """fused_block_forward over every block in order (1..8 tokens)."""
+    """fused_block_forward over every block in order."""
     for blk in blocks:
         x = fused_block_forward(x, blk)
     return x

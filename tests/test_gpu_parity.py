@@ -751,18 +751,19 @@ def test_linear_batch_full_size_qkv(torch_cuda):
         assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= _linear_bound(x, w, r, c))
 
 
-@pytest.mark.parametrize("n_tokens", [1, 4, 8])
-def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens):
+@pytest.mark.parametrize("n_tokens,layout", [(1, "rows"), (4, "rows"), (8, "rows"), (1, "mfma_tiles"),
+                                             (16, "mfma_tiles"), (100, "mfma_tiles")])
+def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens, layout):
     """A block forward whose projections decode inside their products gives
     what the forward on the original BF16 weights gives, up to the order of
     the float32 sums (outputs rounded to bf16 either way): within 2% of the
     output's largest magnitude after one block."""
     torch = torch_cuda
     from entropy_decoding_df11_amd import runtime
-    _note(f"fused block forward tokens={n_tokens}")
+    _note(f"fused block forward tokens={n_tokens} layout={layout}")
     flat, views = workloads.gen_block(seed=7, shapes=SMALL_BLOCK)
     parts = [(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views]
-    blk = df11.compress_block(parts, codebook="per_weight")
+    blk = df11.compress_block(parts, codebook="per_weight", layout=layout)
     resident = {nm: torch.from_numpy(a.astype(np.int16)).to("cuda").view(torch.bfloat16) for nm, a in parts}
     x = workloads.f32_to_bf16_bits(np.random.default_rng(n_tokens).standard_normal(n_tokens * 1024) * 0.5)
     x = torch.from_numpy(x.astype(np.int16).reshape(n_tokens, 1024)).to("cuda").view(torch.bfloat16)
@@ -773,7 +774,7 @@ def test_fused_block_forward_close_to_resident(torch_cuda, n_tokens):
     assert float((got - ref).abs().max()) <= 0.02 * float(ref.abs().max())
 
 
-@pytest.mark.parametrize("path", ["resident", "inline", "fused"])
+@pytest.mark.parametrize("path", ["resident", "inline", "fused", "fused_tiles"])
 def test_captured_forward_replays_match_eager(torch_cuda, path):
     """A 3-block forward captured into a HIP graph (runtime.CapturedForward)
     and replayed on five inputs, with eager forwards and synchronisations
@@ -792,8 +793,9 @@ def test_captured_forward_replays_match_eager(torch_cuda, path):
                          for nm, a in parts})
         if path == "inline":
             shared.append(df11.compress_block(parts, codebook="shared"))
-        if path == "fused":
-            per_weight.append(df11.compress_block(parts, codebook="per_weight"))
+        if path.startswith("fused"):
+            per_weight.append(df11.compress_block(parts, codebook="per_weight",
+                                                  layout="mfma_tiles" if path == "fused_tiles" else "rows"))
     xs = []
     for i in range(5):
         xb = workloads.f32_to_bf16_bits(np.random.default_rng(30 + i).standard_normal(4 * 1024) * 0.5)
@@ -810,7 +812,7 @@ def test_captured_forward_replays_match_eager(torch_cuda, path):
     for i, x in enumerate(xs):
         got = g(x).clone()
         torch.cuda.synchronize()
-        if path == "fused":
+        if path.startswith("fused"):
             err = float((got.float() - refs[i].float()).abs().max())
             assert err <= 0.05 * float(refs[i].float().abs().max()), (i, err)
         else:
