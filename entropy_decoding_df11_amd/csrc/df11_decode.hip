@@ -1343,7 +1343,7 @@ constexpr int kGemmGPW = 2;
 // Waves per SIMD the matrix-core kernels are built for (registers per lane:
 // 80 at six waves, the decoder's occupancy).
 template <int MT>
-constexpr int kGemmWaves = MT == 1 ? 6 : MT == 2 ? 5 : 4;
+constexpr int kGemmWaves = MT == 1 ? 6 : MT == 2 ? 6 : 4;
 
 template <int K, int MT>
 __global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) __attribute__((amdgpu_waves_per_eu(kGemmWaves<MT>)))

@@ -118,7 +118,15 @@ def block_forward(x, w: Dict, eps: float = 1e-5):
     return x
 
 
-def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
+# Token counts up to which the fused products beat decoding the block first
+# and calling torch's GEMM (Llama-3-8B block, measured): the matrix-core
+# product sweeps the stream once per 64 tokens, the row-order product takes
+# up to 8 tokens.
+FUSED_MAX_TOKENS_TILES = 64
+FUSED_MAX_TOKENS_ROWS = 8
+
+
+def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5, scratch=None):
     """block_forward with each projection's decode fused into its product:
     blk holds one DF11 stream per weight, and no weight is ever decompressed
     to HBM.  Weights in MFMA tile order (compress_block(..., layout=
@@ -128,13 +136,18 @@ def fused_block_forward(x, blk: DF11BlockBatch, eps: float = 1e-5):
     (df11_linear_batch / df11_linear), for 1..8 tokens.  The products
     accumulate in float32 and are rounded to x's dtype, like the resident
     path's outputs, but in another order, so the last bits can differ from
-    block_forward's."""
+    block_forward's.  Above FUSED_MAX_TOKENS_TILES (tile order) or
+    FUSED_MAX_TOKENS_ROWS (row order) tokens the block is decoded (into
+    scratch, if given) and block_forward runs on it: there the GEMM's reuse
+    of W across tokens outweighs the decode."""
     import torch
     import torch.nn.functional as F
     from .df11 import linear_batch, matmul_batch
 
     w = {nm: t for (nm, _, _), t in zip(blk.views, blk.tensors)}
     tiled = all(t.tile_cols for t in blk.tensors)
+    if x.shape[0] > (FUSED_MAX_TOKENS_TILES if tiled else FUSED_MAX_TOKENS_ROWS):
+        return block_forward(x, blk.decompress(scratch=scratch), eps)
 
     def products(names_, xin, outs):
         ts = [w[nm] for nm in names_]
