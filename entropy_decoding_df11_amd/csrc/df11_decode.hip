@@ -849,19 +849,31 @@ __device__ __forceinline__ bool boundary_codes(uint64_t pair, uint32_t q, uint32
 }
 
 // Dynamic schedule.  Workgroups run at different speeds (a CU favours its
-// oldest waves), so after three static rounds (super-groups wg, wg + grid,
-// wg + 2 grid) each workgroup takes its next super-groups from one of P <= 8
-// pools: pool x = wg mod P hands out 3 grid + x + P v for v = 0, 1, ... from
-// its own counter, so that the ticket fetches of the whole grid are spread
-// over P addresses (one address would serialise them).  Thread 0 fetches
-// a ticket every iteration, three iterations before the loads that need it,
-// and hands it to the other waves through LDS.  A workgroup's tickets
+// oldest waves), so after two static rounds (super-groups wg, wg + grid)
+// each workgroup takes its next super-groups from one of P <= 8 pools: pool
+// x hands out 2 grid + x + P v for v = 0, 1, ... from its own counter, so
+// that the ticket fetches of the whole grid are spread over P addresses (one
+// address would serialise them).  Thread 0 fetches a ticket at the top of
+// every iteration and, after that iteration's scan barrier, hands it to the
+// other waves through LDS; the next iteration issues its loads and the one
+// after decodes it.  A workgroup thus commits to a super-group two
+// iterations before it decodes it (three measured 1-2% slower on the block:
+// at the end the workgroups finish further apart).  A workgroup's tickets
 // increase, so it stops at its first ticket past the end having processed
 // every earlier one.  On exit every workgroup counts itself in the done word;
 // the last one zeroes every word for the next launch.  A pool's share of the
 // work is fixed, so P divides the workgroup count (schedule_pools).
 using df11::kPools;
 constexpr uint32_t kPoolStride = DF11_SCHEDULE_WORDS / (kPools + 1);  // words: one cache line per counter
+
+// The pool of workgroup wg.  Workgroup i runs on XCD i mod 8, so pools
+// wg mod P would each sit on one XCD (for P = 8) and a slower XCD would end
+// last with its fixed share; (wg + wg / 8) mod P gives every pool the same
+// number of workgroups of every XCD when P divides 8 (and P divides the
+// workgroup count, so each pool gets the same number).
+__device__ __forceinline__ uint32_t pool_of(uint32_t wg, uint32_t pools) {
+    return (wg + (8u % pools == 0u ? wg / 8u : 0u)) % pools;
+}
 
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *sched, uint32_t pool) {
     return __hip_atomic_fetch_add(sched + pool * kPoolStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1100,7 +1112,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         __syncthreads();
     }
 
-    uint32_t s_cur = s_first_it, ticket = 0;
+    uint32_t s_cur = s_first_it;
     for (uint32_t it = 0; s_cur < v_end; ++it) {
         // Wave priorities by phase (the SIMD issues the higher one first
         // among ready waves): the next loads 2, the merge and its stores 0,
@@ -1109,10 +1121,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         // their merge keep the memory busy.
         __builtin_amdgcn_s_setprio(2);
         const uint32_t g = super_of(s_cur) * GPW + slot;
-        // Rounds 0..2 are static; the ticket for round it + 1 >= 3 was
-        // written to LDS in iteration it - 1.
+        // Rounds 0 and 1 are static; the ticket for round it + 1 >= 2 was
+        // fetched and written to LDS in iteration it - 1.
         const uint32_t s_nx = kMfma                  ? s_cur + 1u
-                              : (sched && it >= 2u) ? __builtin_amdgcn_readfirstlane(*s_ticket)
+                              : (sched && it >= 1u) ? __builtin_amdgcn_readfirstlane(*s_ticket)
                                                     : min(s_cur + n_wg, n_super);
 
         // 1. Loads of the next super-group's thread inputs and output range
@@ -1134,7 +1146,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         }
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
-        if (sched && tid == 0) fetched = take_ticket(sched, wg % a.pools);  // for round it + 3
+        if (sched && tid == 0) fetched = take_ticket(sched, pool_of(wg, a.pools));  // for round it + 2
         __builtin_amdgcn_s_setprio(0);
 
         // 2. Merge and store the super-group decoded in the previous
@@ -1214,9 +1226,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
 #pragma unroll
         for (uint32_t w = 0; w < kWaves - 1; ++w) wave_off += w < wave ? s_wsum[w] : 0u;
         const uint32_t o_start = min(lead + wave_off + incl - cnt, a.ebuf_cap - kDecodeReach);
-        // Round it + 2's ticket (fetched last iteration) for the other waves;
-        // they read it after the next barrier, at the top of iteration it + 1.
-        if (sched && tid == 0 && it >= 1u) *s_ticket = 3u * n_wg + wg % a.pools + a.pools * ticket;
+        // Round it + 2's ticket (fetched at the top of this iteration) for
+        // the other waves; they read it after the next barrier, at the top of
+        // iteration it + 1.
+        if (sched && tid == 0) *s_ticket = 2u * n_wg + pool_of(wg, a.pools) + a.pools * fetched;
 
         // Phase 2: OR the (rotated) exponents into the zeroed LDS buffer at
         // their output positions (accumulator x = LDS byte address).  A
@@ -1273,7 +1286,6 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         cur = nx;
         cur_base = nx_base;
         cur_end = nx_end;
-        ticket = fetched;
         s_cur = s_nx;
     }
     if constexpr (TB == 0) {
