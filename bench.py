@@ -397,6 +397,73 @@ def summarize_counters(prof_dir: str, kernel: str, title: str, bench_args: str, 
         f.write("\n".join(lines))
 
 
+def _per_step_counters(prof_dir: str, kernel: str, first: int, per_step: int) -> tuple:
+    """Counters of `kernel` from the COUNTER_PASSES runs in prof_dir/<kernel>_<pass>:
+    per-step totals of the SQ_ counters (the first `first` dispatches in
+    dispatch order if first > 0, `per_step` dispatches to a step) and the
+    medians of rocprofv3's derived percentages."""
+    totals, pct, steps = {}, {}, 0.0
+    for sub in COUNTER_PASSES:
+        per = {}
+        for r in _read_csv(os.path.join(prof_dir, f"{kernel}_{sub}", "run_counter_collection.csv")):
+            if kernel in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"summarize: no {kernel} dispatches in the {sub} counter run")
+        for name, by_dispatch in per.items():
+            ids = sorted(by_dispatch)
+            if first:
+                ids = ids[:first]
+            vals = [by_dispatch[i] for i in ids]
+            if name.startswith("SQ_"):
+                steps = len(ids) / per_step
+                totals[name] = sum(vals) / steps
+            else:
+                pct[name] = float(np.median(vals))
+    return totals, pct
+
+
+def summarize_product_counters(prof_dir: str) -> None:
+    """profiles/ comparison of the one-token fused products' counters: the
+    row-order product (df11_linear_kernel, seven launches a step, bench.py
+    --linear-tokens 1) against the matrix-core product (df11_gemm_batch_kernel,
+    one launch a step, bench.py --matmul-tokens 1), as totals per step over
+    the block's seven matrices."""
+    lin, lin_pct = _per_step_counters(prof_dir, "df11_linear_kernel", 0, 7)
+    with open(os.path.join(prof_dir, "mm_pmc.json")) as f:
+        launches = json.loads(f.read().strip().splitlines()[-1])["launches"]
+    first = launches["check"] + launches["settle"] + launches["warmup"] + launches["timed"]
+    mm, mm_pct = _per_step_counters(prof_dir, "df11_gemm_batch_kernel", first, 1)
+    pre = "cd /tmp && export TMPDIR=/tmp && "
+    lines = ["# One-token fused product on llama3_8b_block: row-order against matrix-core kernel counters", "",
+             "Commands (from the repository root on a one-GPU MI355X box; R = repository root, "
+             "D = R/gpurun_out/prof):", ""]
+    for kernel, bench_args in (("df11_linear_kernel", "--linear-tokens 1 --steps 3 --warmup 2 --no-cpu-baseline"),
+                               ("df11_gemm_batch_kernel", "--matmul-tokens 1 --steps 3 --warmup 2")):
+        for sub, counters in COUNTER_PASSES.items():
+            lines.append(f"    {pre}rocprofv3 --pmc {counters} -d $D/{kernel}_{sub} -o run --output-format csv "
+                         f"-- python3 $R/bench.py {bench_args}")
+    lines += ["", "Before: the row-order product (`df11_linear_kernel`, dot products, one launch per matrix). "
+              "After: the matrix-core product (`df11_gemm_batch_kernel`, tiles fed to "
+              "`v_mfma_f32_16x16x32_bf16`, the seven matrices in one launch). Instruction and cycle counts "
+              "are totals per step (all seven matrices); percentages are medians over the dispatches.", "",
+              "| counter | row-order (before) | matrix-core (after) | after / before |", "|---|---|---|---|"]
+    for name in sorted(lin):
+        if name in mm:
+            lines.append(f"| {name} | {lin[name]:.4g} | {mm[name]:.4g} | {mm[name] / lin[name]:.2f} |")
+    for name in sorted(lin_pct):
+        if name in mm_pct:
+            lines.append(f"| {name} (%) | {lin_pct[name]:.1f} | {mm_pct[name]:.1f} | |")
+    moved = sorted(((mm[n] / lin[n], n) for n in lin if n in mm and n.startswith("SQ_INSTS") and lin[n] > 0))
+    lines += ["", "Instruction counts that moved most (after / before): "
+              + ", ".join(f"{n} {r:.2f}" for r, n in moved[:3]) + ".",
+              f"Wave-cycles per step {lin['SQ_WAVE_CYCLES']:.4g} before, {mm['SQ_WAVE_CYCLES']:.4g} after; waves "
+              f"wait on something {100 * lin['SQ_WAIT_ANY'] / lin['SQ_WAVE_CYCLES']:.0f}% of their cycles before, "
+              f"{100 * mm['SQ_WAIT_ANY'] / mm['SQ_WAVE_CYCLES']:.0f}% after.", ""]
+    with open(os.path.join(REPO, "profiles", "fused_product_llama3_8b_block_t1_counters.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
     weights, DF11 blocks decoded in line before each block, DF11 blocks
@@ -775,6 +842,14 @@ def matmul_bench(args, dev) -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps, (time.perf_counter() - w0) * 1e3 / reps
 
+    # Settle the clocks as the decode line does (the first launches of a
+    # process run slow), then the warmup steps.
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        step()
+        settle += 1
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     fused_ms, wall_ms = timed(step, args.steps)
@@ -824,7 +899,7 @@ def matmul_bench(args, dev) -> int:
         "outputs": "within the float32 summation bound of a float64 product (every token up to 64, a sample above)",
         # launches of the batched fused kernel with all seven products, in order (then the forward's
         # four batches per step, then single-product kernels)
-        "launches": {"check": 1, "warmup": args.warmup + 3, "timed": args.steps},
+        "launches": {"check": 1, "settle": settle, "warmup": args.warmup + 3, "timed": args.steps},
         "host_prep_s": round(t_prep, 1),
     }
     print(json.dumps(result), flush=True)
@@ -912,6 +987,9 @@ def main() -> int:
         for kernel, title, bench_args, source, out_name in counter_runs:
             if all(have(f"{kernel}_{sub}") for sub in COUNTER_PASSES):
                 summarize_counters(args.summarize_profiles, kernel, title, bench_args, source, out_name)
+        if all(have(f"{k}_{sub}") for k in ("df11_linear_kernel", "df11_gemm_batch_kernel") for sub in COUNTER_PASSES) \
+                and os.path.exists(os.path.join(args.summarize_profiles, "mm_pmc.json")):
+            summarize_product_counters(args.summarize_profiles)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
