@@ -583,7 +583,8 @@ def integration(args, dev) -> int:
                       "overlap_decode_workgroups": args.overlap_workgroups, "compressed_over_bf16": round(comp / raw, 4),
                       "outputs": "in line and overlapped: bit-identical to the resident-weight forward; fused "
                                  "(row-order product up to 8 tokens, matrix-core product on tile-ordered weights up "
-                                 "to 256): float32 sums in another order",
+                                 "to 64): float32 sums in another order; the tile-ordered forward at 256 tokens "
+                                 "decodes each block and runs the resident GEMMs (runtime.FUSED_MAX_TOKENS_TILES)",
                       "host_prep_s": round(t_prep, 1),
                       "results": rows}), flush=True)
     return 0

@@ -217,8 +217,9 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
     every launch must leave them zero, and back-to-back launches must all be
     bit-exact.  The stream (64M weights with ~6-bit exponent codes, ~23K
     groups) is long enough for the dynamic schedule at two groups per
-    workgroup; one group per workgroup, four, the static schedule and grids
-    capped below one workgroup per CU must give the same bytes."""
+    workgroup; one group per workgroup, four, the static schedule and capped
+    grids (with every count of work counters, and below one workgroup per
+    CU) must give the same bytes."""
     torch = torch_cuda
     w = _case("uniform_bits", 64 << 20, 11)
     _note(f"schedule dynamic={dynamic}")
@@ -237,7 +238,9 @@ def test_schedule_repeat_launches_and_counter_reset(torch_cuda, dynamic):
         assert not t._schedule.cpu().numpy().any()
         del outs
     t.set_groups_per_workgroup(2)
-    for cap in (100, 7, 1):
+    # (672, 576, 480 and 270 workgroups take 7, 6, 5 and 3 work counters,
+    # which do not divide the 8 XCDs; 100 takes 2, 7 and 1 one)
+    for cap in (672, 576, 480, 270, 100, 7, 1):
         t.set_max_workgroups(cap)
         out = torch.full(t.shape, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
         t.decompress(out=out)
