@@ -113,7 +113,7 @@ struct MatmulArgs {
     uint32_t n_tokens;     // 1 .. the kernel's token slots (any count for the matrix-core product)
     uint32_t yacc_rows;    // rows of W that one group's outputs can touch
     uint32_t passes;       // matrix-core product: sweeps of the stream, 16 MT tokens each
-    uint32_t pad;
+    uint32_t fixed_len;    // matrix-core product with a dealt tail: super-groups of each fixed range
 };
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x00010203u); }
@@ -981,7 +981,12 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 //
 // TB > 0 turns the merge into the fused matmul with up to TB tokens
 // (merge_matmul and flush_rows in place of merge_group).
-template <int K, int GPW, int TB>
+//
+// kTail (matrix-core product, one pass): workgroup wg first sweeps the fixed
+// range [wg L, (wg + 1) L) of L = m.fixed_len super-groups, then takes the
+// rest, [n_wg L, n_super), one super-group per ticket from the work
+// counters, as the decoder does.
+template <int K, int GPW, int TB, bool kTail = false>
 __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulArgs &m, const uint32_t wg,
                                               const uint32_t n_wg) {
     // Static LDS: the first-level table (2^K (lo, aux) word pairs, then 2^K
@@ -1036,11 +1041,19 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     // are numbered v = pass * len + (super-group - r0).
     constexpr bool kMfma = TB < 0;
     constexpr int MT = kMfma ? -TB : 1;
-    const uint32_t r0 = kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg) * n_super / n_wg) : 0u;
-    const uint32_t len = kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg + 1) * n_super / n_wg) - r0 : 1u;
-    const uint32_t v_end = kMfma ? len * m.passes : n_super;
+    static_assert(!kTail || TB == -1, "a dealt tail only for the one-tile matrix-core product");
+    const uint32_t r0 = kTail   ? wg * m.fixed_len
+                        : kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg) * n_super / n_wg)
+                                : 0u;
+    const uint32_t len = kTail   ? m.fixed_len
+                         : kMfma ? static_cast<uint32_t>(static_cast<uint64_t>(wg + 1) * n_super / n_wg) - r0
+                                 : 1u;
+    // (with kTail, iterations are numbered by super-group, as the decoder's)
+    const uint32_t v_end = kMfma && !kTail ? len * m.passes : n_super;
     // Super-group of iteration v (n_super past the end).
-    auto super_of = [&](uint32_t v) -> uint32_t { return kMfma ? (v < v_end ? r0 + v % len : n_super) : v; };
+    auto super_of = [&](uint32_t v) -> uint32_t {
+        return kMfma && !kTail ? (v < v_end ? r0 + v % len : n_super) : v;
+    };
     PanelSums<MT> ps;
     // matrix-core product: the next merge's staged x tiles (stage_x)
     uint8_t *s_x = reinterpret_cast<uint8_t *>(s_ticket + 4) + slot * kXTiles<MT> * MT * 1024u * (kMfma ? 1u : 0u);
@@ -1055,7 +1068,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
     // Pipeline state: the group's output range (scalar) and thread inputs one
     // super-group ahead; the sign/mantissa chunks of the group waiting to be
     // merged.
-    const uint32_t s_first_it = kMfma ? 0u : wg;
+    const uint32_t s_first_it = kTail ? r0 : kMfma ? 0u : wg;
     const uint32_t g_first = super_of(s_first_it) * GPW + slot;
     uint32_t cur_base = out_pos_at(a, g_first), cur_end = out_pos_at(a, g_first + 1);
     GroupLoad cur = load_group(a, g_first, ltid);
@@ -1123,7 +1136,11 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         const uint32_t g = super_of(s_cur) * GPW + slot;
         // Rounds 0 and 1 are static; the ticket for round it + 1 >= 2 was
         // fetched and written to LDS in iteration it - 1.
-        const uint32_t s_nx = kMfma                  ? s_cur + 1u
+        // (kTail: the fixed range, then the tickets, the first fetched two
+        // iterations before the range ends)
+        const uint32_t s_nx = kTail                  ? (it + 1u < len ? s_cur + 1u
+                                                                      : __builtin_amdgcn_readfirstlane(*s_ticket))
+                              : kMfma                ? s_cur + 1u
                               : (sched && it >= 1u) ? __builtin_amdgcn_readfirstlane(*s_ticket)
                                                     : min(s_cur + n_wg, n_super);
 
@@ -1146,7 +1163,8 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         }
         const GroupLoad nx = load_group(a, g_nx, ltid);
         uint32_t fetched = 0;
-        if (sched && tid == 0) fetched = take_ticket(sched, pool_of(wg, a.pools));  // for round it + 2
+        if (sched && tid == 0 && (!kTail || it + 2u >= len))
+            fetched = take_ticket(sched, pool_of(wg, a.pools));  // for round it + 2
         __builtin_amdgcn_s_setprio(0);
 
         // 2. Merge and store the super-group decoded in the previous
@@ -1219,7 +1237,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
             y_rows = 0;
         } else if constexpr (kMfma) {
             // Every wave's merge has read the staged tiles: stage this group's.
-            stage_x<MT>(a, m, base, s_cur / len, wave, lane, s_x);
+            stage_x<MT>(a, m, base, kTail ? 0u : s_cur / len, wave, lane, s_x);
         }
         __builtin_amdgcn_s_setprio(1);
         uint32_t wave_off = 0;
@@ -1229,7 +1247,11 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         // Round it + 2's ticket (fetched at the top of this iteration) for
         // the other waves; they read it after the next barrier, at the top of
         // iteration it + 1.
-        if (sched && tid == 0) *s_ticket = 2u * n_wg + pool_of(wg, a.pools) + a.pools * fetched;
+        if constexpr (kTail) {
+            if (tid == 0 && it + 2u >= len) *s_ticket = n_wg * len + pool_of(wg, a.pools) + a.pools * fetched;
+        } else {
+            if (sched && tid == 0) *s_ticket = 2u * n_wg + pool_of(wg, a.pools) + a.pools * fetched;
+        }
 
         // Phase 2: OR the (rotated) exponents into the zeroed LDS buffer at
         // their output positions (accumulator x = LDS byte address).  A
@@ -1282,7 +1304,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
 
         prev_base = base;
         prev_end = end;
-        if constexpr (kMfma) prev_pass = s_cur / len;
+        if constexpr (kMfma) prev_pass = kTail ? 0u : s_cur / len;
         cur = nx;
         cur_base = nx_base;
         cur_end = nx_end;
@@ -1357,10 +1379,10 @@ constexpr int kGemmGPW = 2;
 template <int MT>
 constexpr int kGemmWaves = MT == 1 ? 6 : MT == 2 ? 6 : 4;
 
-template <int K, int MT>
+template <int K, int MT, bool kTail = false>
 __global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) __attribute__((amdgpu_waves_per_eu(kGemmWaves<MT>)))
 void df11_gemm_kernel(DecodeArgs a, MatmulArgs m) {
-    decode_stream<K, kGemmGPW, -MT>(a, m, blockIdx.x, gridDim.x);
+    decode_stream<K, kGemmGPW, -MT, kTail>(a, m, blockIdx.x, gridDim.x);
 }
 
 
@@ -1386,13 +1408,13 @@ __global__ __launch_bounds__(kThreadsPerGroup *kLinearGPW) void df11_linear_batc
 // Several matrix-core products in one launch, the grid split between them
 // as for df11_decode_batch_kernel (LinearBatchArgs: each stream with its
 // own x, y and shape).
-template <int K, int MT>
+template <int K, int MT, bool kTail = false>
 __global__ __launch_bounds__(kThreadsPerGroup *kGemmGPW) __attribute__((amdgpu_waves_per_eu(kGemmWaves<MT>)))
 void df11_gemm_batch_kernel(LinearBatchArgs b) {
     const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
     uint32_t i = 0;
     while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
-    decode_stream<K, kGemmGPW, -MT>(b.s[i], b.m[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+    decode_stream<K, kGemmGPW, -MT, kTail>(b.s[i], b.m[i], id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
 }
 
 // Zero several outputs: y[i] has end[i] - end[i - 1] floats (end[-1] = 0).
@@ -1891,6 +1913,40 @@ int linear_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *
 template <int MT>
 constexpr size_t kGemmXBytes = kGemmGPW * kXTiles<MT> * MT * 1024u;
 
+// The dealt tail of the one-tile matrix-core product (decode_stream with
+// kTail): at up to kTailMaxTokens tokens (a flush of a wave's sums is then
+// at most 128 atomics) a stream with work counters and at least
+// kDynamicMinRounds super-groups per workgroup sweeps fixed ranges over
+// kTailFixedPercent of its super-groups and deals the rest out by tickets.
+// The fixed ranges keep a panel's sums in registers; the dealt rest absorbs
+// the workgroups' different speeds (the three on a CU differ by ~3% each
+// step, CUs by a few percent), which fixed ranges alone left as ~20 us
+// between the first and the last workgroup to end.  On the block at one
+// token: 125.5 us against 135.5 with fixed ranges alone (70% fixed 128,
+// 80% 127, 90% 126, 95% and 97% 125.5); at 16 tokens, where a flush is 256
+// atomics per wave, the dealt tail lost (140 against 137).
+constexpr uint32_t kTailMaxTokens = 8;
+constexpr uint64_t kTailFixedPercent = 95;
+
+// Sets up the dealt tail for a stream given `want` workgroups: pools and
+// m.fixed_len; returns the workgroup count, or 0 (a.sched cleared) when the
+// stream does not qualify.
+uint32_t tail_schedule(DecodeArgs &a, MatmulArgs &m, uint64_t n_super, uint64_t want) {
+    m.fixed_len = 0;
+    if (!a.sched || m.n_tokens > kTailMaxTokens) {
+        a.sched = nullptr;
+        return 0;
+    }
+    const uint32_t n_wg = schedule_pools(a, n_super, want);
+    const uint64_t fixed = n_super * kTailFixedPercent / 100 / n_wg;
+    if (!a.sched || fixed < 2) {
+        a.sched = nullptr;
+        return 0;
+    }
+    m.fixed_len = static_cast<uint32_t>(fixed);
+    return n_wg;
+}
+
 template <int K, int MT>
 int launch_gemm(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipStream_t stream, hipEvent_t start,
                 hipEvent_t stop, bool zero) {
@@ -1898,17 +1954,25 @@ int launch_gemm(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipSt
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_gemm_kernel<K, MT>);
+    // (the dealt-tail instance has the same register and LDS needs)
     const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + kGemmGPW - 1) / kGemmGPW;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     if (max_wg) resident = std::min<uint64_t>(resident, max_wg);
-    const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min(resident, n_super)));
+    uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min(resident, n_super)));
     (void)hipGetLastError();
     DecodeArgs args = a;
-    args.sched = nullptr;  // (contiguous ranges: no dynamic schedule)
     MatmulArgs margs = m;
     margs.passes = (m.n_tokens + 16u * MT - 1u) / (16u * MT);
+    if constexpr (MT == 1) {
+        if (const uint32_t n_wg = tail_schedule(args, margs, n_super, resident)) {
+            grid = n_wg;
+            fn = reinterpret_cast<const void *>(&df11_gemm_kernel<K, 1, true>);
+        }
+    } else {
+        args.sched = nullptr;  // (contiguous ranges: no dynamic schedule)
+    }
     if (zero) {
         float *y = m.y;
         const uint32_t n_y = m.n_tokens * m.out_features;
@@ -2002,12 +2066,27 @@ int launch_gemm_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStrea
     uint64_t sup[kMaxBatch], want[kMaxBatch];
     for (uint32_t i = 0; i < b.n; ++i) sup[i] = (b.s[i].n_groups + kGemmGPW - 1) / kGemmGPW;
     df11::split_grid(sup, b.n, resident, want);
+    // The dealt tail when every stream qualifies (one kernel serves them all).
+    bool tail = MT == 1;
+    uint32_t share[kMaxBatch];
+    for (uint32_t i = 0; i < b.n; ++i) {
+        b.m[i].passes = (b.m[i].n_tokens + 16u * MT - 1u) / (16u * MT);
+        DecodeArgs s = b.s[i];
+        share[i] = tail ? tail_schedule(s, b.m[i], sup[i], want[i]) : 0u;
+        tail = tail && share[i] != 0;
+        if (share[i]) b.s[i].pools = s.pools;
+    }
     uint32_t next = 0;
     for (uint32_t i = 0; i < b.n; ++i) {
-        b.s[i].sched = nullptr;  // (contiguous ranges: no dynamic schedule)
-        b.m[i].passes = (b.m[i].n_tokens + 16u * MT - 1u) / (16u * MT);
+        if (!tail) {
+            b.s[i].sched = nullptr;  // (contiguous ranges: no dynamic schedule)
+            b.m[i].fixed_len = 0;
+        }
         b.wg_begin[i] = next;
-        next += static_cast<uint32_t>(want[i]);
+        next += tail ? share[i] : static_cast<uint32_t>(want[i]);
+    }
+    if constexpr (MT == 1) {
+        if (tail) fn = reinterpret_cast<const void *>(&df11_gemm_batch_kernel<K, 1, true>);
     }
     b.wg_begin[b.n] = next;
     b.stride = df11::coprime_stride(next);
@@ -2062,6 +2141,7 @@ int gemm_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *co
         total += n_tokens * out_features[i];
         z.y[b.n] = ys[i];
         z.end[b.n] = total;
+        if (shares_schedule(ws, i)) a.sched = nullptr;  // (the same tensor twice, say)
         b.s[b.n] = a;
         b.m[b.n] = m;
         ++b.n;

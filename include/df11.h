@@ -424,7 +424,11 @@ int df11_linear_batch_acc(const df11_device_stream *ws, uint32_t n_streams, cons
  * sums in float in an unspecified order (partial sums of a row from several
  * workgroups meet in float atomics), so the low bits can differ between
  * calls.  Enqueued on hip_stream: a zeroing kernel for y, then the fused
- * kernel; the stream's schedule counters are not used.  Errors:
+ * kernel.  Up to 8 tokens, a stream with schedule counters and at least 12
+ * super-groups (2 groups) per workgroup sweeps fixed ranges over 95% of them
+ * and hands the rest out with its counters (which launches sharing them
+ * must not overlap in time, as for df11_decompress); otherwise the counters
+ * are not used.  Not on the page (a load-balancing choice).  Errors:
  * DF11_E_INVALID_ARG (sizes, alignment, overlap, a stream not in tile order,
  * or as for df11_decompress), DF11_E_BAD_STREAM, DF11_E_TOO_LARGE
  * (n_tokens * out_features >= 2^32), DF11_E_HIP. */
@@ -457,9 +461,12 @@ int df11_matmul_timed(const df11_device_stream *w, const uint16_t *x, uint32_t n
  *                 first); else ys[i] += xs[i] W_i^T
  *   start_event, stop_event   hipEvent_t or NULL, recorded at the fused
  *                 kernel's own start and end
- * Errors: DF11_E_TOO_LARGE (n_streams > DF11_MAX_BATCH, the outputs' total
- * >= 2^32 floats), as for df11_matmul otherwise.  Nothing is launched unless
- * every stream is valid. */
+ * The schedule counters serve as for df11_matmul when every non-empty stream
+ * qualifies and none shares its counters with an earlier stream of the
+ * batch; otherwise the whole launch sweeps fixed ranges.  Errors:
+ * DF11_E_TOO_LARGE (n_streams > DF11_MAX_BATCH, the outputs' total >= 2^32
+ * floats), as for df11_matmul otherwise.  Nothing is launched unless every
+ * stream is valid. */
 int df11_matmul_batch(const df11_device_stream *ws, uint32_t n_streams, const uint16_t *const *xs, uint32_t n_tokens,
                       const uint32_t *in_features, const uint32_t *out_features, float *const *ys, int accumulate,
                       void *hip_stream, void *start_event, void *stop_event);

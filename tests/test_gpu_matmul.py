@@ -205,23 +205,62 @@ def test_matmul_batch_matches_oracle(torch_cuda, n_tokens):
         assert np.all(err <= 2 * bound), (float(err.max()), float((err - 2 * bound).max()))
 
 
-def test_matmul_batch_full_block_one_token(torch_cuda):
-    """The whole Llama-3-8B block's seven products in one launch at one token:
-    every output row against the oracle."""
-    torch = torch_cuda
+@pytest.fixture(scope="module")
+def full_block(torch_cuda):
+    """The Llama-3-8B block's seven matrices: original bits, shape, the
+    tile-ordered DF11 stream on the GPU and the oracle's encoding."""
     flat, views = workloads.gen_block()
-    _note("matmul batch: full block, 1 token")
-    ts, xs, checks = [], [], []
+    items = []
     for nm, off, (r, c) in views:
         w = np.ascontiguousarray(flat[off:off + r * c])
-        xb = _tokens(1, c, r)
-        ts.append(df11.compress(w, shape=(r, c), layout="mfma_tiles"))
-        xs.append(_device_x(torch, xb))
-        checks.append((w, xb, r, c))
+        items.append((nm, w, r, c, df11.compress(w, shape=(r, c), layout="mfma_tiles"), oracle.encode(w)))
     del flat
+    return items
+
+
+@pytest.mark.parametrize("n_tokens", [1, 2, 8, 16])
+def test_matmul_batch_full_block(torch_cuda, full_block, n_tokens):
+    """The whole block's seven products in one launch, every output against
+    the oracle.  Up to 8 tokens each stream sweeps fixed ranges over most of
+    its super-groups and deals the rest out with its work counters; at 16
+    only fixed ranges run.  Launched twice in a row (the second time
+    accumulating), the counters must be zero after each launch."""
+    torch = torch_cuda
+    _note(f"matmul batch: full block, {n_tokens} tokens")
+    ts = [it[4] for it in full_block]
+    xbs = [_tokens(n_tokens, c, r + n_tokens) for _, _, r, c, _, _ in full_block]
+    xs = [_device_x(torch, xb) for xb in xbs]
+    refs = [oracle.linear(enc, xb, r) for (_, _, r, _, _, enc), xb in zip(full_block, xbs)]
+    bounds = [_bound(xb, w, r, c) for (_, w, r, c, _, _), xb in zip(full_block, xbs)]
     ys = df11.matmul_batch(ts, xs)
     torch.cuda.synchronize()
-    for y, (w, xb, r, c) in zip(ys, checks):
-        ref = oracle.linear(oracle.encode(w), xb, r)
+    for t in ts:
+        assert not t._schedule.cpu().numpy().any()
+    for y, ref, bound in zip(ys, refs, bounds):
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
-        assert np.all(err <= _bound(xb, w, r, c))
+        assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+    df11.matmul_batch(ts, xs, outs=ys, accumulate=True)
+    torch.cuda.synchronize()
+    for t in ts:
+        assert not t._schedule.cpu().numpy().any()
+    for y, ref, bound in zip(ys, refs, bounds):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - 2 * ref)
+        assert np.all(err <= 2 * bound), (float(err.max()), float((err - 2 * bound).max()))
+
+
+def test_matmul_batch_same_tensor_twice(torch_cuda, full_block):
+    """One tensor named twice in a batch at one token: the two entries share
+    work counters, so the launch sweeps fixed ranges only; both outputs must
+    match the oracle and the counters stay zero."""
+    torch = torch_cuda
+    _note("matmul batch: gate_proj twice, 1 token")
+    nm, w, r, c, t, enc = next(it for it in full_block if it[0] == "gate_proj")
+    xb = _tokens(1, c, 7)
+    x = _device_x(torch, xb)
+    ys = df11.matmul_batch([t, t], [x, x])
+    torch.cuda.synchronize()
+    ref, bound = oracle.linear(enc, xb, r), _bound(xb, w, r, c)
+    for y in ys:
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound)
+    assert not t._schedule.cpu().numpy().any()
