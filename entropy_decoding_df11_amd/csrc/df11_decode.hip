@@ -1954,8 +1954,11 @@ int launch_gemm(const DecodeArgs &a, const MatmulArgs &m, uint32_t max_wg, hipSt
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_gemm_kernel<K, MT>);
-    // (the dealt-tail instance has the same register and LDS needs)
-    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    // (the persistent grid must fit whichever instance launches)
+    int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    if constexpr (MT == 1)
+        per_cu = std::min(per_cu, resident_per_cu(reinterpret_cast<const void *>(&df11_gemm_kernel<K, 1, true>),
+                                                  kThreadsPerGroup * kGemmGPW, dev, lds));
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + kGemmGPW - 1) / kGemmGPW;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
@@ -2059,7 +2062,11 @@ int launch_gemm_batch(LinearBatchArgs &b, ZeroArgs &z, uint32_t max_wg, hipStrea
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
     const void *fn = reinterpret_cast<const void *>(&df11_gemm_batch_kernel<K, MT>);
-    const int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    // (the persistent grid must fit whichever instance launches)
+    int per_cu = resident_per_cu(fn, kThreadsPerGroup * kGemmGPW, dev, lds);
+    if constexpr (MT == 1)
+        per_cu = std::min(per_cu, resident_per_cu(reinterpret_cast<const void *>(&df11_gemm_batch_kernel<K, 1, true>),
+                                                  kThreadsPerGroup * kGemmGPW, dev, lds));
     if (per_cu < 1) return DF11_E_HIP;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
     if (max_wg) resident = std::min<uint64_t>(resident, std::max<uint32_t>(max_wg, b.n));
