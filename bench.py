@@ -72,8 +72,8 @@ def _traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
-# Host threads of the CPU baseline: the GPU machine gives one GPU's job a share
-# of 16 cores, whatever the machine's core count.
+# Host threads of the CPU baseline: a one-GPU job gets a share of 16 of the
+# host's cores, whatever the machine's core count.
 CPU_SHARE = 16
 
 
@@ -119,15 +119,15 @@ def _cpu_baselines(flat: np.ndarray, args) -> dict:
     out1 = oracle.decode_treewalk(s)
     dt_one = time.perf_counter() - t0
     ok_one = bool(np.array_equal(out1, flat))
-    verdict = lambda ok: "matches" if ok else "DIFFERS FROM"  # noqa: E731
+    outcome = lambda ok: "matches" if ok else "DIFFERS FROM"  # noqa: E731
     return {
         "value": round(algo / dt_all / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"the whole {args.workload} data as one stream ({flat.size} weights), tree-walk decode split by "
                   f"groups over {threads} threads (the job's share of the host, {usable} CPUs usable) in "
-                  f"{dt_all:.2f} s; output {verdict(ok_all)} the original weights",
+                  f"{dt_all:.2f} s; output {outcome(ok_all)} the original weights",
         "one_core": {"value": round(algo / dt_one / 1e9, 4), "unit": "GB/s", "cores": 1,
                      "sample": f"the same stream, tree-walk decode of every code in order on one thread in "
-                               f"{dt_one:.2f} s; output {verdict(ok_one)} the original weights"},
+                               f"{dt_one:.2f} s; output {outcome(ok_one)} the original weights"},
         **cpu,
     }
 
@@ -178,7 +178,7 @@ def summarize_decode_trace(prof_dir: str, sub: str, kernel: str, title: str, com
     us = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]  # noqa: E731
     lines = [f"# {title}: rocprofv3 kernel trace", "",
              "Command (from the repository root on a one-GPU MI355X box; R = repository root, "
-             "D = R/gpurun_out/prof):", "", "    " + command, "",
+             "D = a directory for the raw results):", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:6]:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -322,7 +322,7 @@ def summarize_matmul_profile(prof_dir: str, sub: str, command: str) -> None:
     hbm = bench["config"]["compressed_bytes"] + sum(2 * T * c + 4 * T * r for r, c in bench["config"]["shapes"].values())
     lines = [f"# df11_gemm_batch_kernel on llama3_8b_block_matmul ({T} token{'s' if T > 1 else ''}): "
              "rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box; "
-             "R = repository root, D = R/gpurun_out/prof):", "", "    " + command, "",
+             "R = repository root, D = a directory for the raw results):", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:8]:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -372,7 +372,7 @@ def summarize_counters(prof_dir: str, kernel: str, title: str, bench_args: str, 
     pre = "cd /tmp && export TMPDIR=/tmp && "
     lines = [f"# {title}: rocprofv3 counters", "",
              f"Kernel source `{source}`, sha256 prefix {src_hash}.  Commands (from the repository root on a "
-             "one-GPU MI355X box; R = repository root, D = R/gpurun_out/prof):", ""]
+             "one-GPU MI355X box; R = repository root, D = a directory for the raw results):", ""]
     for sub, counters in COUNTER_PASSES.items():
         lines.append(f"    {pre}rocprofv3 --pmc {counters} -d $D/{kernel}_{sub} -o run --output-format csv "
                      f"-- python3 $R/bench.py {bench_args}")
@@ -437,7 +437,7 @@ def summarize_product_counters(prof_dir: str) -> None:
     pre = "cd /tmp && export TMPDIR=/tmp && "
     lines = ["# One-token fused product on llama3_8b_block: row-order against matrix-core kernel counters", "",
              "Commands (from the repository root on a one-GPU MI355X box; R = repository root, "
-             "D = R/gpurun_out/prof):", ""]
+             "D = a directory for the raw results):", ""]
     for kernel, bench_args in (("df11_linear_kernel", "--linear-tokens 1 --steps 3 --warmup 2 --no-cpu-baseline"),
                                ("df11_gemm_batch_kernel", "--matmul-tokens 1 --steps 3 --warmup 2")):
         for sub, counters in COUNTER_PASSES.items():
@@ -948,7 +948,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.summarize_profiles:
-        pre = "cd /tmp && export TMPDIR=/tmp && "   # R = repository root, D = R/gpurun_out/prof
+        pre = "cd /tmp && export TMPDIR=/tmp && "   # R = repository root, D = a directory for the raw results
         have = lambda sub: os.path.isdir(os.path.join(args.summarize_profiles, sub))
         trace = pre + "rocprofv3 --kernel-trace --stats -d $D/{sub} -o run --output-format csv -- python3 " \
                       "$R/bench.py {args} > $D/{sub}.json"

@@ -15,12 +15,12 @@ CSRC = os.path.join(REPO, "entropy_decoding_df11_amd", "csrc")
 
 
 @pytest.fixture(scope="module")
-def driver(tmp_path_factory):
-    exe = str(tmp_path_factory.mktemp("launch") / "launch_shape_driver")
+def cli(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("launch") / "launch_shape_cli")
     # (built under AddressSanitizer and UndefinedBehaviorSanitizer, every report fatal)
     subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Wextra", "-Werror", "-fsanitize=address,undefined",
                     "-fno-sanitize-recover=all", f"-I{CSRC}",
-                    os.path.join(REPO, "tests", "cpp", "launch_shape_driver.cpp"), "-o", exe], check=True)
+                    os.path.join(REPO, "tests", "cpp", "launch_shape_cli.cpp"), "-o", exe], check=True)
 
     def run(lines):
         res = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, check=True)
@@ -41,7 +41,7 @@ def _best_max_ratio(sup, resident):
     return best
 
 
-def test_split_grid_never_exceeds_the_cap(driver):
+def test_split_grid_never_exceeds_the_cap(cli):
     # the case that overshot before: one big stream and six of one super-group each
     cases = [(8, [1000, 1, 1, 1, 1, 1, 1]), (7, [1000, 1, 1, 1, 1, 1, 1]), (768, [5000, 1250, 1250, 5000, 17000, 17000, 17000])]
     rng = np.random.default_rng(0)
@@ -51,7 +51,7 @@ def test_split_grid_never_exceeds_the_cap(driver):
         if rng.random() < 0.5:
             sup = [int(v) for v in np.where(rng.random(n) < 0.6, 1, sup)]
         cases.append((int(rng.integers(n, 1200)), sup))
-    out = driver([f"S {len(s)} {r} " + " ".join(map(str, s)) for r, s in cases])
+    out = cli([f"S {len(s)} {r} " + " ".join(map(str, s)) for r, s in cases])
     for (resident, sup), want in zip(cases, out):
         assert len(want) == len(sup)
         assert sum(want) <= max(resident, len(sup)), (resident, sup, want)
@@ -61,24 +61,24 @@ def test_split_grid_never_exceeds_the_cap(driver):
             assert want == sup
 
 
-def test_split_grid_minimises_the_largest_share(driver):
+def test_split_grid_minimises_the_largest_share(cli):
     rng = np.random.default_rng(1)
     cases = []
     for _ in range(120):
         n = int(rng.integers(1, 5))
         sup = [int(v) for v in rng.integers(1, 9, n)]
         cases.append((int(rng.integers(n, sum(sup) + 2)), sup))
-    out = driver([f"S {len(s)} {r} " + " ".join(map(str, s)) for r, s in cases])
+    out = cli([f"S {len(s)} {r} " + " ".join(map(str, s)) for r, s in cases])
     for (resident, sup), want in zip(cases, out):
         got = max(s / w for s, w in zip(sup, want))
         assert math.isclose(got, _best_max_ratio(sup, resident)), (resident, sup, want)
 
 
-def test_pool_shape(driver):
+def test_pool_shape(cli):
     rng = np.random.default_rng(2)
     cases = [(1, 1), (5, 768), (100000, 768), (100000, 1), (100000, 97), (100000, 770), (40, 13)]
     cases += [(int(rng.integers(1, 200000)), int(rng.integers(1, 2000))) for _ in range(400)]
-    out = driver([f"P {ns} {w}" for ns, w in cases])
+    out = cli([f"P {ns} {w}" for ns, w in cases])
     for (n_super, want), (n_wg, pools, dynamic) in zip(cases, out):
         assert 1 <= n_wg <= max(1, min(want, n_super))
         assert 1 <= pools <= 8 and n_wg % pools == 0
@@ -89,8 +89,8 @@ def test_pool_shape(driver):
         assert n_wg >= min(want, n_super) - 8
 
 
-def test_coprime_stride(driver):
+def test_coprime_stride(cli):
     grids = list(range(1, 400)) + [768, 1024, 1536]
-    out = driver([f"C {g}" for g in grids])
+    out = cli([f"C {g}" for g in grids])
     for g, (stride,) in zip(grids, out):
         assert math.gcd(stride, g) == 1 and 1 <= stride <= 2 * g + 1
