@@ -177,7 +177,7 @@ def summarize_decode_trace(prof_dir: str, sub: str, kernel: str, title: str, com
     algo = bench["config"]["compressed_bytes"] + 2 * bench["config"]["n_elements"]
     us = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]  # noqa: E731
     lines = [f"# {title}: rocprofv3 kernel trace", "",
-             "Command (from the repository root on a one-GPU MI355X box; R = repository root, "
+             "Command (from the repository root on a one-GPU MI355X machine; R = repository root, "
              "D = a directory for the raw results):", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:6]:
@@ -281,7 +281,7 @@ def summarize_linear_profile(prof_dir: str, command: str) -> None:
     T = bench["config"]["tokens"]
     lines = [f"# df11_linear_kernel on llama3_8b_block_linear ({T} token{'s' if T > 1 else ''}): "
              "rocprofv3 kernel trace", "",
-             "Command (from the repository root on a one-GPU MI355X box):", "", "    " + command, "",
+             "Command (from the repository root on a one-GPU MI355X machine):", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:8]:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -321,7 +321,7 @@ def summarize_matmul_profile(prof_dir: str, sub: str, command: str) -> None:
     avg = float(np.mean(us))
     hbm = bench["config"]["compressed_bytes"] + sum(2 * T * c + 4 * T * r for r, c in bench["config"]["shapes"].values())
     lines = [f"# df11_gemm_batch_kernel on llama3_8b_block_matmul ({T} token{'s' if T > 1 else ''}): "
-             "rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X box; "
+             "rocprofv3 kernel trace", "", "Command (from the repository root on a one-GPU MI355X machine; "
              "R = repository root, D = a directory for the raw results):", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:8]:
@@ -372,7 +372,7 @@ def summarize_counters(prof_dir: str, kernel: str, title: str, bench_args: str, 
     pre = "cd /tmp && export TMPDIR=/tmp && "
     lines = [f"# {title}: rocprofv3 counters", "",
              f"Kernel source `{source}`, sha256 prefix {src_hash}.  Commands (from the repository root on a "
-             "one-GPU MI355X box; R = repository root, D = a directory for the raw results):", ""]
+             "one-GPU MI355X machine; R = repository root, D = a directory for the raw results):", ""]
     for sub, counters in COUNTER_PASSES.items():
         lines.append(f"    {pre}rocprofv3 --pmc {counters} -d $D/{kernel}_{sub} -o run --output-format csv "
                      f"-- python3 $R/bench.py {bench_args}")
@@ -436,7 +436,7 @@ def summarize_product_counters(prof_dir: str) -> None:
     mm, mm_pct = _per_step_counters(prof_dir, "df11_gemm_batch_kernel", first, 1)
     pre = "cd /tmp && export TMPDIR=/tmp && "
     lines = ["# One-token fused product on llama3_8b_block: row-order against matrix-core kernel counters", "",
-             "Commands (from the repository root on a one-GPU MI355X box; R = repository root, "
+             "Commands (from the repository root on a one-GPU MI355X machine; R = repository root, "
              "D = a directory for the raw results):", ""]
     for kernel, bench_args in (("df11_linear_kernel", "--linear-tokens 1 --steps 3 --warmup 2 --no-cpu-baseline"),
                                ("df11_gemm_batch_kernel", "--matmul-tokens 1 --steps 3 --warmup 2")):
