@@ -264,3 +264,29 @@ def test_matmul_batch_same_tensor_twice(torch_cuda, full_block):
         err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
         assert np.all(err <= bound)
     assert not t._schedule.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("cap", [270, 97])
+def test_matmul_batch_full_block_capped_grid(torch_cuda, full_block, cap):
+    """The block's seven products at one token on a capped grid (cap
+    workgroups shared by the seven streams: 2 to 72 each, one work counter
+    each, long fixed ranges): the fixed ranges and the dealt rest still
+    cover every super-group once, and the counters are left zero."""
+    torch = torch_cuda
+    _note(f"matmul batch: full block, 1 token, {cap} workgroups")
+    ts = [it[4] for it in full_block]
+    xbs = [_tokens(1, c, r + 3) for _, _, r, c, _, _ in full_block]
+    xs = [_device_x(torch, xb) for xb in xbs]
+    try:
+        for t in ts:
+            t.set_max_workgroups(cap)
+        ys = df11.matmul_batch(ts, xs)
+        torch.cuda.synchronize()
+    finally:
+        for t in ts:
+            t.set_max_workgroups(0)
+    for t in ts:
+        assert not t._schedule.cpu().numpy().any()
+    for y, (_, w, r, c, _, enc), xb in zip(ys, full_block, xbs):
+        err = np.abs(y.cpu().numpy().astype(np.float64) - oracle.linear(enc, xb, r))
+        assert np.all(err <= _bound(xb, w, r, c))
