@@ -464,6 +464,61 @@ def summarize_product_counters(prof_dir: str) -> None:
         f.write("\n".join(lines))
 
 
+def summarize_product_traffic(prof_dir: str) -> None:
+    """profiles/ summary of the one-token matrix-core product's HBM traffic:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the batched kernel's
+    seven-product launches in two PMC runs of bench.py --matmul-tokens 1
+    (prof_dir/mm_fetch, prof_dir/mm_write, the first run's bench line in
+    prof_dir/mm_fetch.json), scaled by the copy-kernel factors of the
+    decoder's committed traffic summary (the same counters on the same GPU).
+    Reads should be about the compressed weights plus x, and writes about y
+    alone: W's BF16 never reaches HBM."""
+    with open(PMC_SUMMARY) as f:
+        cal = json.load(f)
+    with open(os.path.join(prof_dir, "mm_fetch.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    launches = bench["launches"]
+    first = launches["check"] + launches["settle"] + launches["warmup"] + launches["timed"]
+
+    def kib(sub, counter):
+        per = _pmc_per_dispatch(os.path.join(prof_dir, sub), counter)
+        ids = sorted(d for d, (name, _, _) in per.items() if "df11_gemm_batch_kernel" in name)[:first]
+        if not ids:
+            raise SystemExit(f"summarize: no df11_gemm_batch_kernel dispatches in {sub}")
+        return float(np.median([per[d][2] for d in ids])), len(ids)
+
+    fetch_kib, n_f = kib("mm_fetch", "FETCH_SIZE")
+    write_kib, n_w = kib("mm_write", "WRITE_SIZE")
+    read_b = fetch_kib * 1024 * cal["fetch_scale"]
+    write_b = write_kib * 1024 * cal["write_scale"]
+    cfg = bench["config"]
+    T = cfg["tokens"]
+    comp = cfg["compressed_bytes"]
+    shapes = list(cfg["shapes"].values())
+    x_b = 2 * T * sum({c for _, c in shapes})  # matrices with the same in_features share one x
+    y_b = 4 * T * sum(r for r, _ in shapes)
+    bf16_b = 2 * cfg["n_elements"]
+    pre = "cd /tmp && export TMPDIR=/tmp && "
+    cmd = pre + "rocprofv3 --pmc {c} -d $D/{sub} -o run --output-format csv -- python3 $R/bench.py --matmul-tokens 1 " \
+                "--steps 3 --warmup 2"
+    lines = ["# df11_gemm_batch_kernel on llama3_8b_block (1 token): HBM traffic", "",
+             "Commands (from the repository root on a one-GPU MI355X machine; R = repository root, D = a directory "
+             "for the raw results):", "",
+             "    " + cmd.format(c="FETCH_SIZE", sub="mm_fetch") + " > $D/mm_fetch.json",
+             "    " + cmd.format(c="WRITE_SIZE", sub="mm_write"), "",
+             f"Medians over the {n_f} and {n_w} seven-product launches of the runs; KiB scaled by the copy-kernel "
+             f"factors of `df11_decode_kernel_llama3_8b_block_pmc.json` (FETCH_SIZE x{cal['fetch_scale']}, "
+             f"WRITE_SIZE x{cal['write_scale']}).", "",
+             "| | bytes per launch | against |", "|---|---|---|",
+             f"| HBM reads | {read_b / 1e6:.1f} MB | compressed weights {comp / 1e6:.1f} MB + x {x_b / 1e3:.1f} KB: "
+             f"{read_b / (comp + x_b):.3f}x |",
+             f"| HBM writes | {write_b / 1e6:.3f} MB | y {y_b / 1e3:.1f} KB; the BF16 weights would be "
+             f"{bf16_b / 1e6:.1f} MB |", "",
+             f"Raw: FETCH_SIZE {fetch_kib:.1f} KiB, WRITE_SIZE {write_kib:.1f} KiB per dispatch.", ""]
+    with open(os.path.join(REPO, "profiles", "df11_gemm_batch_kernel_llama3_8b_block_t1_traffic.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def integration(args, dev) -> int:
     """Forward of a synthetic model of Llama-3-8B-shaped blocks: resident BF16
     weights, DF11 blocks decoded in line before each block, DF11 blocks
@@ -988,6 +1043,8 @@ def main() -> int:
         for kernel, title, bench_args, source, out_name in counter_runs:
             if all(have(f"{kernel}_{sub}") for sub in COUNTER_PASSES):
                 summarize_counters(args.summarize_profiles, kernel, title, bench_args, source, out_name)
+        if have("mm_fetch") and have("mm_write"):
+            summarize_product_traffic(args.summarize_profiles)
         if all(have(f"{k}_{sub}") for k in ("df11_linear_kernel", "df11_gemm_batch_kernel") for sub in COUNTER_PASSES) \
                 and os.path.exists(os.path.join(args.summarize_profiles, "mm_pmc.json")):
             summarize_product_counters(args.summarize_profiles)
