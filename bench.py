@@ -863,9 +863,17 @@ def matmul_bench(args, dev) -> int:
 
     by = {m[0]: m for m in mats}
 
-    def step_forward():  # as a forward issues them: q, k, v; o; gate, up; down
+    # As runtime.fused_block_forward issues them: the seven outputs are views
+    # of one buffer zeroed by one fill, then four accumulating launches (q, k,
+    # v; o; gate, up; down).
+    fwd_buf = torch.empty(sum(T * m[1] for m in mats), dtype=torch.float32, device=dev)
+    fwd_y = dict(zip(by, torch.split(fwd_buf, [T * m[1] for m in mats])))
+
+    def step_forward():
+        fwd_buf.zero_()
         for group in (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",)):
-            df11.matmul_batch([by[g][3] for g in group], [by[g][5] for g in group], outs=[by[g][6] for g in group])
+            df11.matmul_batch([by[g][3] for g in group], [by[g][5] for g in group],
+                              outs=[fwd_y[g].view(T, by[g][1]) for g in group], accumulate=True)
 
     def step_seven():  # one launch per product
         for _, _, _, t, _, x, y in mats:

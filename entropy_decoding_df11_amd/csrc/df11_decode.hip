@@ -397,6 +397,103 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
 }
 
+// merge_group for a matrix in MFMA tile order whose panels hold an even
+// number of k-steps: it goes back to row-major in whole 128-byte lines.  Two
+// consecutive k-steps of a panel are 64 consecutive columns of its rows, so
+// the group's chunks are taken in pair-rounds aligned to 512 chunks (the
+// first starts at c0 rounded down to 512): in pair-round p, wave w merges
+// n-tile w of both k-steps, lane l the chunks A + 512 p + 256 h + 64 w + l
+// (h = 0, 1), reading its LDS exponent cells in order as merge_group does.
+// The merged chunks go through a per-wave LDS stage (two 64-chunk halves,
+// a 16-byte pad after every 16 chunks so that both the writes and the
+// transposed reads below fall on distinct banks) and are stored row by row:
+// in store s, lane L writes row 8 s + L / 8 of the n-tile, columns
+// 8 (L mod 8) .. + 7 of the pair's 64, so eight lanes fill one line.
+// (Stored in the order merged, each 16-row, 32-column block left half
+// lines: the per-weight block decoded in 211 us that way against 131 us in
+// row order.)  Chunks outside the group are neither read nor stored.
+constexpr uint32_t kPairUnits = 68;                         // 16-byte units per stage half (64 + 4 pads)
+constexpr uint32_t kPairStageBytes = 2u * kPairUnits * 16u;  // per wave
+
+__device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *ebuf,
+                                                  const uint64_t (&sm)[kPrefetchChunks], uint32_t base, uint32_t end,
+                                                  uint32_t ltid, bool skip_first, bool whole_last, uint4 *stage) {
+    const uint32_t c0 = base >> 3;
+    const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
+    const uint32_t store_base = skip_first ? (base + 7u) & ~7u : base;
+    const uint32_t store_end = whole_last ? min((end + 7u) & ~7u, a.n_elements) : end;
+    uint32_t lane = ltid & (kWaveSize - 1u);
+    // (recomputed at every merge: the lane constants below, hoisted out of
+    // the decoder's loop, would hold registers through the decode)
+    asm volatile("" : "+v"(lane));
+    const uint32_t a0 = c0 & ~511u;
+    // chunk of this wave's lane 0 in half 0 of pair-round 0
+    const uint32_t wave_c = a0 + (ltid & ~(kWaveSize - 1u));
+    // The stage's source of this lane's stores: half q / 4, lane (L / 8 + 8 s) + 16 (q mod 4), q = L mod 8;
+    // its destination: row 64 panel + 16 w + 8 s + L / 8, column 32 ks + 8 q (ks even, the pair's first
+    // k-step; tiled_chunk_origin of that chunk), the lane's part taken once.
+    const uint32_t q = lane & 7u, h_src = q >> 2, l_src0 = (lane >> 3) + 16u * (q & 3u);
+    const uint32_t lane_dst = (lane >> 3) * a.tile_cols + 8u * q;
+    const uint32_t n_pr = n_chunks ? (c0 + n_chunks - a0 + 511u) / 512u : 0u;
+    auto pair_round = [&](uint32_t p, uint64_t s0, uint64_t s1) {
+        const uint32_t cb = wave_c + 512u * p;
+        const uint32_t g = (a0 >> 8) + 2u * p;  // global k-step of half 0
+        const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
+        const uint32_t wave_dst = (64u * panel + 16u * (ltid >> 6)) * a.tile_cols + 32u * (g - panel * a.tile_ks);
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t k = cb + 256u * h + lane - c0;  // (wraps past n_chunks before c0)
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (k < n_chunks) {
+                uint64_t *cell = reinterpret_cast<uint64_t *>(ebuf + 8u * k);
+                const uint64_t r8 = *cell;
+                *cell = 0;
+                v = merge8(h ? s1 : s0, r8);
+            }
+            stage[kPairUnits * h + lane + (lane >> 4)] = v;
+        }
+        // The wave's own LDS operations complete in order; this keeps the
+        // compiler from moving the reads of other lanes' values above the writes.
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+        for (uint32_t s = 0; s < 2; ++s) {
+            const uint32_t l_src = l_src0 + 8u * s;
+            const uint32_t c = cb + 256u * h_src + l_src;
+            if (c - c0 < n_chunks) {
+                const uint4 v = stage[kPairUnits * h_src + l_src + (l_src >> 4)];
+                const uint32_t dst = wave_dst + lane_dst + 8u * s * a.tile_cols;
+                // The line's 8 chunks lie between its first (half 0, run 0) and last (half 1, run 3) in
+                // the stream; a line that the group holds whole bypasses the caches, one whose other
+                // part a neighbouring group writes goes through them (partial lines written
+                // non-temporally from two workgroups are several times slower).
+                const uint32_t line0 = cb + (l_src & 15u);
+                if (line0 - c0 < n_chunks && line0 + 304u - c0 < n_chunks && 8u * c >= store_base &&
+                    8u * c + 8u <= store_end) {
+                    u32x4 x = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(a.out + dst));
+                } else if (8u * c >= store_base && 8u * c + 8u <= store_end) {
+                    *reinterpret_cast<uint4 *>(a.out + dst) = v;
+                } else {
+                    store_chunk_at(a.out, dst, 8u * c, v, store_base, store_end);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    if (n_pr > 0u) pair_round(0, sm[0], sm[1]);
+    if (n_pr > 1u) pair_round(1, sm[2], sm[3]);
+    for (uint32_t p = 2; p < n_pr; ++p) {  // (groups of more than 1024 chunks)
+        const uint32_t c = wave_c + 512u * p + lane;
+        pair_round(p, __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(c, a.sm_chunks - 1u))),
+                   __builtin_nontemporal_load(
+                       reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(c + 256u, a.sm_chunks - 1u))));
+    }
+    // Codes past the group's last output reach at most 4 bytes into the next chunk.
+    if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
+}
+
 // Fused matmul (y = x W^T) in place of the store.  A group's chunks are
 // split into four contiguous runs, one per wave, taken 64 chunks (one per
 // lane) per round; chunk k holds W's elements 8 (c0 + k) .. + 7, all in one
@@ -418,17 +515,19 @@ __device__ __forceinline__ uint32_t run_chunk(uint32_t wave, uint32_t lane, uint
     return (wave * wave_rounds(n_chunks) + j) * kWaveSize + lane;
 }
 
-template <int TB>
+template <int TB, bool kPairs = false>
 __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint32_t end, uint32_t ltid,
                                         uint64_t (&sm)[kPrefetchChunks]) {
     const uint32_t c0 = base >> 3;
     const uint32_t nch = min(group_chunks(base, end), a.ebuf_cap / 8u);
 #pragma unroll
     for (int j = 0; j < kPrefetchChunks; ++j) {
-        // (the matrix-core product takes rounds aligned to 256 chunks: mfma_chunk)
-        const uint32_t k = TB == 0  ? ltid + j * kThreadsPerGroup
-                           : TB > 0 ? run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch)
-                                    : ltid + j * kThreadsPerGroup - (c0 & 255u);
+        // (the matrix-core product takes rounds aligned to 256 chunks: mfma_chunk; merge_group_pairs
+        // pair-rounds aligned to 512, register j holding half j mod 2 of pair-round j / 2)
+        const uint32_t k = kPairs   ? (c0 & ~511u) + 512u * (j >> 1) + 256u * (j & 1) + ltid - c0
+                           : TB == 0 ? ltid + j * kThreadsPerGroup
+                           : TB > 0  ? run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch)
+                                     : ltid + j * kThreadsPerGroup - (c0 & 255u);
         const uint32_t c = min(c0 + (k < nch ? k : 0u), a.sm_chunks - 1u);
         sm[j] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * c));
     }
@@ -986,7 +1085,10 @@ __device__ __forceinline__ void decode_half(uint64_t pair, uint32_t end, uint32_
 // range [wg L, (wg + 1) L) of L = m.fixed_len super-groups, then takes the
 // rest, [n_wg L, n_super), one super-group per ticket from the work
 // counters, as the decoder does.
-template <int K, int GPW, int TB, bool kTail = false>
+// kPairs (decompression of a tile-ordered stream with an even number of
+// k-steps per panel): the merge writes whole row-major lines
+// (merge_group_pairs) through a per-wave LDS stage after the dynamic LDS.
+template <int K, int GPW, int TB, bool kTail = false, bool kPairs = false>
 __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulArgs &m, const uint32_t wg,
                                               const uint32_t n_wg) {
     // Static LDS: the first-level table (2^K (lo, aux) word pairs, then 2^K
@@ -1025,6 +1127,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
                                                          reinterpret_cast<float *>(s_ticket + 4) + GPW * m.yacc_rows * kRowTB) +
                                                      kXBytes);
     uint32_t y_row0 = 0, y_rows = 0;  // rows of the merged group awaiting flush_rows
+    static_assert(!kPairs || TB == 0, "whole-line stores only when decompressing");
+    uint4 *s_pair = reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(s_first) + (a.dtab ? 0u : 2u << K) +
+                                              (slot * kWaves + wave) * kPairStageBytes);
 
     const uint32_t n_super = (a.n_groups + GPW - 1) / GPW;
     uint32_t *const sched = a.sched;
@@ -1172,9 +1277,14 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         // load this group's sign/mantissa chunks (into the registers the
         // merge has just consumed) for the next one.
         if constexpr (TB == 0) {
-            if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+            if constexpr (kPairs) {
+                if (it > 0)
+                    merge_group_pairs(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_pair);
+            } else {
+                if (it > 0) merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
+            }
         }
-        load_sm<TB>(a, base, end, ltid, sm);
+        load_sm<TB, kPairs>(a, base, end, ltid, sm);
         __builtin_amdgcn_s_setprio(3);
 
         // 3. Decode this super-group.
@@ -1310,7 +1420,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         cur_end = nx_end;
         s_cur = s_nx;
     }
-    if constexpr (TB == 0) {
+    if constexpr (kPairs) {
+        merge_group_pairs(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0, s_pair);
+    } else if constexpr (TB == 0) {
         merge_group(a, s_ebuf, sm, prev_base, prev_end, ltid, s_edge[0] != 0, s_edge[1] != 0);
     } else if constexpr (kMfma) {
         merge_mfma<MT>(a, m, s_ebuf, sm, prev_base, prev_end, prev_pass, ltid, ps, s_x);
@@ -1328,6 +1440,14 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
 template <int K, int GPW>
 __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_kernel(DecodeArgs a) {
     decode_stream<K, GPW, 0>(a, MatmulArgs{}, blockIdx.x, gridDim.x);
+}
+
+// The decoder for tile-ordered streams that go back to row-major in whole
+// lines (merge_group_pairs), held to the plain decoder's six waves per SIMD.
+template <int K, int GPW>
+__global__ __launch_bounds__(kThreadsPerGroup *GPW) __attribute__((amdgpu_waves_per_eu(6))) void df11_decode_pairs_kernel(
+    DecodeArgs a) {
+    decode_stream<K, GPW, 0, false, true>(a, MatmulArgs{}, blockIdx.x, gridDim.x);
 }
 
 // Several independent streams (each with its own codebook and output) in one
@@ -1354,6 +1474,16 @@ __global__ __launch_bounds__(kThreadsPerGroup *GPW) void df11_decode_batch_kerne
     uint32_t i = 0;
     while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
     decode_stream<K, GPW, 0>(b.s[i], MatmulArgs{}, id - b.wg_begin[i], b.wg_begin[i + 1] - b.wg_begin[i]);
+}
+
+template <int K, int GPW>
+__global__ __launch_bounds__(kThreadsPerGroup *GPW) __attribute__((amdgpu_waves_per_eu(6))) void df11_decode_pairs_batch_kernel(
+    BatchArgs b) {
+    const uint32_t id = static_cast<uint32_t>((static_cast<uint64_t>(blockIdx.x) * b.stride) % gridDim.x);
+    uint32_t i = 0;
+    while (i + 1u < b.n && id >= b.wg_begin[i + 1]) ++i;
+    decode_stream<K, GPW, 0, false, true>(b.s[i], MatmulArgs{}, id - b.wg_begin[i],
+                                          b.wg_begin[i + 1] - b.wg_begin[i]);
 }
 
 // Decode fused with y = x W^T for up to TB tokens: W's BF16 never leaves the
@@ -1492,12 +1622,35 @@ size_t dynamic_lds(const DecodeArgs &a, size_t extra = 0) {
     return a.n_luts * 256u + 256u + GPW * (a.ebuf_cap + 4u * kWaves + 8u) + 16u + extra + (a.dtab ? 0u : 2u << K);
 }
 
+// Whether a stream decompresses through merge_group_pairs: MFMA tile order
+// with an even number of k-steps per panel.
+bool pairs_layout(const DecodeArgs &a) { return a.tile_cols && a.tile_ks % 2u == 0u; }
+
+// The instance (and its dynamic LDS) a decompression of these streams uses:
+// the whole-line one when every stream is paired and its LDS stage leaves as
+// many workgroups resident per CU.
+template <int K, int GPW, typename Kernel>
+const void *pick_pairs(const DecodeArgs *s, uint32_t n, Kernel plain, Kernel paired, int dev, size_t &lds) {
+    bool pairs = n > 0;
+    for (uint32_t i = 0; i < n; ++i) pairs = pairs && pairs_layout(s[i]);
+    if (!pairs) return reinterpret_cast<const void *>(plain);
+    size_t lds_p = 0;
+    for (uint32_t i = 0; i < n; ++i)
+        lds_p = std::max(lds_p, dynamic_lds<K, GPW>(s[i], GPW * kWaves * kPairStageBytes));
+    const int plain_cu = resident_per_cu(reinterpret_cast<const void *>(plain), kThreadsPerGroup * GPW, dev, lds);
+    const int pair_cu = resident_per_cu(reinterpret_cast<const void *>(paired), kThreadsPerGroup * GPW, dev, lds_p);
+    if (pair_cu < plain_cu) return reinterpret_cast<const void *>(plain);
+    lds = lds_p;
+    return reinterpret_cast<const void *>(paired);
+}
+
 template <int K, int GPW>
 int launch(const DecodeArgs &a, uint32_t max_wg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    const size_t lds = dynamic_lds<K, GPW>(a);
+    size_t lds = dynamic_lds<K, GPW>(a);
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
-    const void *fn = reinterpret_cast<const void *>(&df11_decode_kernel<K, GPW>);
+    const void *fn = pick_pairs<K, GPW>(&a, 1, &df11_decode_kernel<K, GPW>, &df11_decode_pairs_kernel<K, GPW>, dev,
+                                        lds);
     const int per_cu = resident_per_cu(fn, kThreadsPerGroup * GPW, dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     const uint64_t n_super = (a.n_groups + GPW - 1) / GPW;
@@ -1532,7 +1685,8 @@ int launch_batch(BatchArgs &b, uint32_t max_wg, hipStream_t stream, hipEvent_t s
     for (uint32_t i = 0; i < b.n; ++i) lds = std::max(lds, dynamic_lds<K, GPW>(b.s[i]));
     int dev = 0, cus = 0;
     if (device_cus(dev, cus)) return DF11_E_HIP;
-    const void *fn = reinterpret_cast<const void *>(&df11_decode_batch_kernel<K, GPW>);
+    const void *fn = pick_pairs<K, GPW>(b.s, b.n, &df11_decode_batch_kernel<K, GPW>,
+                                        &df11_decode_pairs_batch_kernel<K, GPW>, dev, lds);
     const int per_cu = resident_per_cu(fn, kThreadsPerGroup * GPW, dev, lds);
     if (per_cu < 1) return DF11_E_HIP;
     uint64_t resident = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);

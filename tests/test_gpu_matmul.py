@@ -71,8 +71,12 @@ def _device_x(torch, xb):
     return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("rows,cols", [(64, 32), (128, 1024), (192, 4096), (64, 14336), (1024, 4096)])
-@pytest.mark.parametrize("kind", ["normal", "stress_tuned"])
+# (64, 32) and (64, 96) have an odd number of k-steps per panel and take
+# the chunk-by-chunk stores; the others go back in whole lines (pair-rounds).
+# "zeros" (1-bit codes) gives groups of 2048 chunks, more pair-rounds than
+# the sign/mantissa registers prefetch.
+@pytest.mark.parametrize("rows,cols", [(64, 32), (64, 96), (128, 1024), (192, 4096), (64, 14336), (1024, 4096)])
+@pytest.mark.parametrize("kind", ["normal", "stress_tuned", "zeros"])
 def test_tiled_decompress_is_row_major(torch_cuda, rows, cols, kind):
     torch = torch_cuda
     _note(f"tiled decompress {kind} {rows}x{cols}")
@@ -82,6 +86,32 @@ def test_tiled_decompress_is_row_major(torch_cuda, rows, cols, kind):
     t.decompress(out=out)
     torch.cuda.synchronize()
     assert np.array_equal(_u16(out), w)
+
+
+def test_tiled_decompress_batch_mixed_and_full_block(torch_cuda):
+    """Batched decompression of tile-ordered streams: a batch mixing an odd
+    k-step count (chunk-by-chunk stores for the whole launch) with even ones,
+    then the full-size per-weight block in MFMA tile order (whole-line
+    stores), each weight bit-exact in row-major order."""
+    torch = torch_cuda
+    _note("tiled decompress: mixed batch")
+    shapes = [(128, 1024), (64, 96), (192, 4096)]
+    ws = [_weights("normal", r * c, r + c) for r, c in shapes]
+    ts = [df11.compress(w, shape=s, layout="mfma_tiles") for w, s in zip(ws, shapes)]
+    outs = [torch.full(s, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16) for s in shapes]
+    df11.decompress_batch(ts, outs)
+    df11.decompress_batch([ts[0], ts[2]], [outs[0], outs[2]])  # (every stream paired)
+    torch.cuda.synchronize()
+    for w, o in zip(ws, outs):
+        assert np.array_equal(_u16(o), w)
+    _note("tiled decompress: full-size per-weight block")
+    flat, views = workloads.gen_block()
+    blk = df11.compress_block([(nm, flat[o:o + r * c].reshape(r, c)) for nm, o, (r, c) in views],
+                              codebook="per_weight", layout="mfma_tiles")
+    scratch = torch.full((blk.n_elements,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    blk.decompress(scratch=scratch)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(scratch), flat)
 
 
 MATMUL_CASES = [  # (weights, rows, cols)
