@@ -923,6 +923,26 @@ def matmul_bench(args, dev) -> int:
     resident_ms, _ = timed(lambda: [F.linear(m[5], m[4]) for m in mats], max(3, args.steps // 2))
     decode_gemm_ms, _ = timed(lambda: [F.linear(m[5], m[3].decompress(out=scratch[:m[1] * m[2]].view(m[1], m[2])))
                                        for m in mats], max(3, args.steps // 2))
+
+    # The forward's launches and the resident products captured into HIP
+    # graphs and replayed: the kernels alone, without the host issuing them.
+    def captured(fn):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                fn()
+        stream.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    g_forward = captured(step_forward)
+    g_resident = captured(lambda: [F.linear(m[5], m[4]) for m in mats])
+    forward_graph_ms, _ = timed(g_forward.replay, max(3, args.steps // 2))
+    resident_graph_ms, _ = timed(g_resident.replay, max(3, args.steps // 2))
+    del g_forward, g_resident
     intensity = flops / hbm_bytes
     compute_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     tflops = flops / (fused_ms * 1e-3) / 1e12
@@ -959,7 +979,9 @@ def matmul_bench(args, dev) -> int:
                                  "fused_df11_matmul_as_a_forward_issues_it": round(forward_ms, 4),
                                  "fused_df11_matmul_seven_launches": round(seven_ms, 4),
                                  "resident_bf16_F_linear": round(resident_ms, 4),
-                                 "decode_then_F_linear": round(decode_gemm_ms, 4)},
+                                 "decode_then_F_linear": round(decode_gemm_ms, 4),
+                                 "fused_df11_matmul_as_a_forward_issues_it_graph": round(forward_graph_ms, 4),
+                                 "resident_bf16_F_linear_graph": round(resident_graph_ms, 4)},
         "outputs": "within the float32 summation bound of a float64 product (every token up to 64, a sample above)",
         # launches of the batched fused kernel with all seven products, in order (then the forward's
         # four batches per step, then single-product kernels)
