@@ -1057,6 +1057,14 @@ def main() -> int:
             if have(f"mm{T}"):
                 summarize_matmul_profile(args.summarize_profiles, f"mm{T}",
                                          trace.format(sub=f"mm{T}", args=f"--matmul-tokens {T} --steps 20 --warmup 5"))
+        if have("pw_tiles_trace"):
+            summarize_decode_trace(args.summarize_profiles, "pw_tiles_trace", "df11_decode_pairs_batch_kernel",
+                                   "df11_decode_pairs_batch_kernel on llama3_8b_block_per_weight (MFMA tile order "
+                                   "back to row-major)",
+                                   trace.format(sub="pw_tiles_trace",
+                                                args="--workload llama3_8b_block_per_weight --layout mfma_tiles "
+                                                     "--steps 20 --warmup 5 --no-cpu-baseline"),
+                                   "df11_decode_pairs_batch_kernel_llama3_8b_block_per_weight_tiles_trace.md")
         if have("rans_trace"):
             summarize_decode_trace(args.summarize_profiles, "rans_trace", "df11_rans_decode",
                                    "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
