@@ -43,6 +43,7 @@
 #include "df11_device.h"
 #include "df11_internal.h"
 #include "df11_launch.h"
+#include "df11_pairs.h"
 
 namespace {
 
@@ -400,19 +401,15 @@ __device__ __forceinline__ void merge_group(const DecodeArgs &a, uint8_t *ebuf, 
 // merge_group for a matrix in MFMA tile order whose panels hold an even
 // number of k-steps: it goes back to row-major in whole 128-byte lines.  Two
 // consecutive k-steps of a panel are 64 consecutive columns of its rows, so
-// the group's chunks are taken in pair-rounds aligned to 512 chunks (the
-// first starts at c0 rounded down to 512): in pair-round p, wave w merges
-// n-tile w of both k-steps, lane l the chunks A + 512 p + 256 h + 64 w + l
-// (h = 0, 1), reading its LDS exponent cells in order as merge_group does.
-// The merged chunks go through a per-wave LDS stage (two 64-chunk halves,
-// a 16-byte pad after every 16 chunks so that both the writes and the
-// transposed reads below fall on distinct banks) and are stored row by row:
-// in store s, lane L writes row 8 s + L / 8 of the n-tile, columns
-// 8 (L mod 8) .. + 7 of the pair's 64, so eight lanes fill one line.
-// (Stored in the order merged, each 16-row, 32-column block left half
-// lines: the per-weight block decoded in 211 us that way against 131 us in
-// row order.)  Chunks outside the group are neither read nor stored.
-constexpr uint32_t kPairUnits = 68;                         // 16-byte units per stage half (64 + 4 pads)
+// the group's chunks are taken in pair-rounds aligned to 512 chunks
+// (df11_pairs.h): in pair-round p, wave w merges n-tile w of both k-steps,
+// reading its LDS exponent cells in order as merge_group does, puts the
+// merged chunks into a per-wave LDS stage, and stores them row by row, eight
+// lanes to a line.  (Stored in the order merged, each 16-row, 32-column
+// block left half lines: the per-weight block decoded in 211 us that way
+// against 131 us in row order.)  Chunks outside the group are neither read
+// nor stored.
+using df11::kPairUnits;
 constexpr uint32_t kPairStageBytes = 2u * kPairUnits * 16u;  // per wave
 
 __device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *ebuf,
@@ -426,20 +423,15 @@ __device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *
     // (recomputed at every merge: the lane constants below, hoisted out of
     // the decoder's loop, would hold registers through the decode)
     asm volatile("" : "+v"(lane));
-    const uint32_t a0 = c0 & ~511u;
-    // chunk of this wave's lane 0 in half 0 of pair-round 0
-    const uint32_t wave_c = a0 + (ltid & ~(kWaveSize - 1u));
-    // The stage's source of this lane's stores: half q / 4, lane (L / 8 + 8 s) + 16 (q mod 4), q = L mod 8;
-    // its destination: row 64 panel + 16 w + 8 s + L / 8, column 32 ks + 8 q (ks even, the pair's first
-    // k-step; tiled_chunk_origin of that chunk), the lane's part taken once.
-    const uint32_t q = lane & 7u, h_src = q >> 2, l_src0 = (lane >> 3) + 16u * (q & 3u);
-    const uint32_t lane_dst = (lane >> 3) * a.tile_cols + 8u * q;
-    const uint32_t n_pr = n_chunks ? (c0 + n_chunks - a0 + 511u) / 512u : 0u;
+    const uint32_t wave = ltid / kWaveSize;
+    const uint32_t h_src = df11::pair_src_half(lane), l_src0 = df11::pair_src_lane(lane, 0);
+    const uint32_t lane_dst = df11::pair_lane_dst(lane, 0, a.tile_cols);
+    const uint32_t n_pr = df11::pair_rounds(c0, n_chunks);
     auto pair_round = [&](uint32_t p, uint64_t s0, uint64_t s1) {
-        const uint32_t cb = wave_c + 512u * p;
-        const uint32_t g = (a0 >> 8) + 2u * p;  // global k-step of half 0
+        const uint32_t cb = df11::pair_chunk(c0, p, 0, ltid - lane);  // the wave's lane 0, half 0
+        const uint32_t g = cb >> 8;                                    // global k-step of half 0 (even)
         const uint32_t panel = static_cast<uint32_t>(__umul64hi(g, a.tile_magic));
-        const uint32_t wave_dst = (64u * panel + 16u * (ltid >> 6)) * a.tile_cols + 32u * (g - panel * a.tile_ks);
+        const uint32_t wave_dst = df11::pair_wave_dst(panel, g - panel * a.tile_ks, a.tile_cols, wave);
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {
             const uint32_t k = cb + 256u * h + lane - c0;  // (wraps past n_chunks before c0)
@@ -450,7 +442,7 @@ __device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *
                 *cell = 0;
                 v = merge8(h ? s1 : s0, r8);
             }
-            stage[kPairUnits * h + lane + (lane >> 4)] = v;
+            stage[df11::pair_unit(h, lane)] = v;
         }
         // The wave's own LDS operations complete in order; this keeps the
         // compiler from moving the reads of other lanes' values above the writes.
@@ -461,18 +453,17 @@ __device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *
             const uint32_t l_src = l_src0 + 8u * s;
             const uint32_t c = cb + 256u * h_src + l_src;
             if (c - c0 < n_chunks) {
-                const uint4 v = stage[kPairUnits * h_src + l_src + (l_src >> 4)];
+                const uint4 v = stage[df11::pair_unit(h_src, l_src)];
                 const uint32_t dst = wave_dst + lane_dst + 8u * s * a.tile_cols;
-                // The line's 8 chunks lie between its first (half 0, run 0) and last (half 1, run 3) in
-                // the stream; a line that the group holds whole bypasses the caches, one whose other
-                // part a neighbouring group writes goes through them (partial lines written
-                // non-temporally from two workgroups are several times slower).
-                const uint32_t line0 = cb + (l_src & 15u);
-                if (line0 - c0 < n_chunks && line0 + 304u - c0 < n_chunks && 8u * c >= store_base &&
-                    8u * c + 8u <= store_end) {
+                // A line the group holds whole bypasses the caches; one whose
+                // other part a neighbouring group writes goes through them
+                // (partial lines written non-temporally from two workgroups
+                // are several times slower).
+                const bool whole = 8u * c >= store_base && 8u * c + 8u <= store_end;
+                if (whole && df11::pair_line_whole(cb, l_src, c0, n_chunks)) {
                     u32x4 x = {v.x, v.y, v.z, v.w};
                     __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(a.out + dst));
-                } else if (8u * c >= store_base && 8u * c + 8u <= store_end) {
+                } else if (whole) {
                     *reinterpret_cast<uint4 *>(a.out + dst) = v;
                 } else {
                     store_chunk_at(a.out, dst, 8u * c, v, store_base, store_end);
@@ -485,7 +476,7 @@ __device__ __forceinline__ void merge_group_pairs(const DecodeArgs &a, uint8_t *
     if (n_pr > 0u) pair_round(0, sm[0], sm[1]);
     if (n_pr > 1u) pair_round(1, sm[2], sm[3]);
     for (uint32_t p = 2; p < n_pr; ++p) {  // (groups of more than 1024 chunks)
-        const uint32_t c = wave_c + 512u * p + lane;
+        const uint32_t c = df11::pair_chunk(c0, p, 0, ltid);
         pair_round(p, __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(c, a.sm_chunks - 1u))),
                    __builtin_nontemporal_load(
                        reinterpret_cast<const uint64_t *>(a.sm + 8ull * min(c + 256u, a.sm_chunks - 1u))));
@@ -524,7 +515,7 @@ __device__ __forceinline__ void load_sm(const DecodeArgs &a, uint32_t base, uint
     for (int j = 0; j < kPrefetchChunks; ++j) {
         // (the matrix-core product takes rounds aligned to 256 chunks: mfma_chunk; merge_group_pairs
         // pair-rounds aligned to 512, register j holding half j mod 2 of pair-round j / 2)
-        const uint32_t k = kPairs   ? (c0 & ~511u) + 512u * (j >> 1) + 256u * (j & 1) + ltid - c0
+        const uint32_t k = kPairs   ? df11::pair_chunk(c0, j >> 1, j & 1, ltid) - c0
                            : TB == 0 ? ltid + j * kThreadsPerGroup
                            : TB > 0  ? run_chunk(ltid / kWaveSize, ltid & (kWaveSize - 1), j, nch)
                                      : ltid + j * kThreadsPerGroup - (c0 & 255u);
