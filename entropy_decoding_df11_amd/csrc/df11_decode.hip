@@ -2299,6 +2299,24 @@ int gemm_batch_impl(const df11_device_stream *ws, uint32_t n, const uint16_t *co
         ++b.n;
     }
     if (b.n == 0) return DF11_OK;
+    if (b.n == 1) {
+        // One product: the one-stream kernel, whose loop keeps the stream's
+        // arguments in scalar registers instead of indexing the batch's.
+#define DF11_GEMM_ONE_CASE(KB)                                                                         \
+    case KB:                                                                                           \
+        switch (gemm_tiles(n_tokens)) {                                                                \
+        case 1: return launch_gemm<KB, 1>(b.s[0], b.m[0], max_wg, stream, start, stop, zero);          \
+        case 2: return launch_gemm<KB, 2>(b.s[0], b.m[0], max_wg, stream, start, stop, zero);          \
+        default: return launch_gemm<KB, 4>(b.s[0], b.m[0], max_wg, stream, start, stop, zero);         \
+        }
+        switch (bits) {
+            DF11_GEMM_ONE_CASE(10)
+            DF11_GEMM_ONE_CASE(11)
+            DF11_GEMM_ONE_CASE(12)
+        default: return DF11_E_INVALID_ARG;
+        }
+#undef DF11_GEMM_ONE_CASE
+    }
     z.n = b.n;
 #define DF11_GEMM_BATCH_CASE(KB)                                                                \
     case KB:                                                                                    \
