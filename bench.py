@@ -935,14 +935,25 @@ def matmul_bench(args, dev) -> int:
         stream.wait_stream(side)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn()
-        return g
+            out = fn()
+        return g, out
 
-    g_forward = captured(step_forward)
-    g_resident = captured(lambda: [F.linear(m[5], m[4]) for m in mats])
+    step_forward()
+    torch.cuda.synchronize()
+    eager_forward = fwd_buf.clone()
+    g_forward, _ = captured(step_forward)
+    g_resident, resident_outs = captured(lambda: [F.linear(m[5], m[4]) for m in mats])
     forward_graph_ms, _ = timed(g_forward.replay, max(3, args.steps // 2))
     resident_graph_ms, _ = timed(g_resident.replay, max(3, args.steps // 2))
-    del g_forward, g_resident
+    # the last replays against the eager results (float32 sums in another order for the fused products)
+    torch.cuda.synchronize()
+    scale = float(eager_forward.abs().max())
+    resident_far = any(float((o.float() - F.linear(m[5], m[4]).float()).abs().max())
+                       > 1e-2 * float(o.float().abs().max()) for o, m in zip(resident_outs, mats))
+    if float((fwd_buf - eager_forward).abs().max()) > 1e-4 * scale or resident_far:
+        print("bench: a graph replay differs from the eager products", file=sys.stderr)
+        return 1
+    del g_forward, g_resident, resident_outs, eager_forward
     intensity = flops / hbm_bytes
     compute_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     tflops = flops / (fused_ms * 1e-3) / 1e12
