@@ -56,6 +56,31 @@ def test_noalloc_batch_matches_batch_on_two_calls():
         del ts, ref, got
 
 
+def test_noalloc_batch_matches_batch_tile_ordered():
+    """Tile-ordered streams (decompressed back to row-major in whole lines)
+    through both entry points, two calls in a row, the second smaller."""
+    import torch
+    assert torch.cuda.is_available()
+    lib = _lib.load()
+    st = torch.cuda.current_stream()
+    rng = np.random.default_rng(8)
+    calls = (("3 tiled matrices", [(1024, 4096), (64, 14336), (192, 128)]), ("1 tiled matrix", [(128, 1024)]))
+    for call, shapes in calls:
+        _note(f"noalloc batch: {call}")
+        ws = [workloads.f32_to_bf16_bits(rng.standard_normal(r * c) * 0.02) for r, c in shapes]
+        ts = [df11.compress(w, shape=s, layout="mfma_tiles") for w, s in zip(ws, shapes)]
+        ref = [torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16) for w in ws]
+        got = [torch.full((w.size,), 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16) for w in ws]
+        torch.cuda.synchronize()
+        assert _call(lib.df11_decompress_batch, ts, ref, st) == 0
+        assert _call(lib.df11_decompress_batch_noalloc, ts, got, st) == 0
+        torch.cuda.synchronize()
+        for w, a, b in zip(ws, ref, got):
+            assert np.array_equal(_u16(b), _u16(a))
+            assert np.array_equal(_u16(b), w)
+        del ts, ref, got
+
+
 def test_noalloc_batch_rejects_too_many_streams():
     import torch
     assert torch.cuda.is_available()
