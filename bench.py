@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -333,7 +334,36 @@ def summarize_matmul_profile(prof_dir: str, sub: str, command: str) -> None:
               f"compressed weights + x + y, {hbm / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s; "
               f"{2.0 * T * bench['config']['n_elements'] / (avg * 1e-6) / 1e12:.2f} TFLOP/s.  The bench line's "
               f"events give {bench['kernel_ms'] * 1e3:.2f} us per step (the fused kernel plus one zeroing kernel).",
-              "", "Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
+              ""]
+    # The forward's launches: one fill of the seven outputs, then q, k, v; o; gate, up; down (a batched
+    # kernel for two or three products, the one-stream kernel for one), eagerly issued and graph-replayed.
+    trace = sorted(_read_csv(os.path.join(prof_dir, sub, "run_kernel_trace.csv")),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    is_gemm = lambda r: "df11_gemm_kernel" in r["Kernel_Name"] or "df11_gemm_batch_kernel" in r["Kernel_Name"]  # noqa: E731
+    seqs = [trace[i:i + 5] for i in range(len(trace) - 4)
+            if "Fill" in trace[i]["Kernel_Name"] and all(is_gemm(r) for r in trace[i + 1:i + 5])]
+    if seqs:
+        names = ["fill", "q, k, v", "o", "gate, up", "down"]
+        shapes = bench["config"]["shapes"]
+        weights = [0, sum(r * c for k, (r, c) in shapes.items() if k in ("q_proj", "k_proj", "v_proj")),
+                   shapes["o_proj"][0] * shapes["o_proj"][1],
+                   sum(r * c for k, (r, c) in shapes.items() if k in ("gate_proj", "up_proj")),
+                   shapes["down_proj"][0] * shapes["down_proj"][1]]
+        rate = avg / bench["config"]["n_elements"]  # us per weight in the one-launch product
+        lines += [f"The forward's launches ({len(seqs)} sequences of a fill and four products, eager and graph "
+                  "replays; medians): each launch against its weights at the one-launch product's rate.", "",
+                  "| launch | kernel | us | gap before, us | us at the one-launch rate |", "|---|---|---|---|---|"]
+        for j, nm in enumerate(names):
+            dur = float(np.median([(int(q[j]["End_Timestamp"]) - int(q[j]["Start_Timestamp"])) / 1e3 for q in seqs]))
+            gap = float(np.median([(int(q[j]["Start_Timestamp"]) - int(q[j - 1]["End_Timestamp"])) / 1e3
+                                   for q in seqs])) if j else 0.0
+            found = re.search(r"(df11_\w+<[^(]*?>|\w*Fill\w*)", seqs[0][j]["Kernel_Name"])
+            kern = found.group(1) if found else seqs[0][j]["Kernel_Name"][:40]
+            lines.append(f"| {nm} | `{kern}` | {dur:.2f} | {gap:.2f} | "
+                         + (f"{weights[j] * rate:.2f} |" if weights[j] else "|"))
+        total = float(np.median([(int(q[4]["End_Timestamp"]) - int(q[0]["Start_Timestamp"])) / 1e3 for q in seqs]))
+        lines += ["", f"Fill start to down's end: {total:.2f} us (median).", ""]
+    lines += ["Bench line of the traced run:", "", "    " + json.dumps(bench), ""]
     with open(os.path.join(REPO, "profiles", f"df11_gemm_kernel_llama3_8b_block_t{T}_trace.md"), "w") as f:
         f.write("\n".join(lines))
 
