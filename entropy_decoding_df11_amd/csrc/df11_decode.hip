@@ -825,7 +825,13 @@ __device__ __forceinline__ void merge_mfma(const DecodeArgs &a, const MatmulArgs
     const uint32_t n_chunks = min(group_chunks(base, end), a.ebuf_cap / 8u);
     const uint32_t lead = c0 & 255u;
     const uint32_t rounds = (lead + n_chunks + 255u) >> 8;
-    const uint32_t lane = ltid & (kWaveSize - 1), wave = __builtin_amdgcn_readfirstlane(ltid / kWaveSize);
+    uint32_t lane = ltid & (kWaveSize - 1);
+    // Two token tiles: the lane constants are recomputed at every merge (hoisted
+    // out of the decoder's loop they held registers through the decode, and
+    // the kernel spilled; 32 tokens 0.167 -> 0.155 ms per block).  At one and
+    // four tiles the hoisted form measured faster.
+    if constexpr (MT == 2) asm volatile("" : "+v"(lane));
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(ltid / kWaveSize);
     if (ltid == 0 && 8u * (n_chunks + 1u) <= a.ebuf_cap) *reinterpret_cast<uint64_t *>(ebuf + 8u * n_chunks) = 0;
     if (n_chunks == 0) return;
     const uint32_t g0 = c0 >> 8;
