@@ -248,6 +248,33 @@ def full_block(torch_cuda):
     return items
 
 
+@pytest.mark.parametrize("n_tokens", [1, 17, 40])
+def test_matmul_batch_of_one_matches_oracle(torch_cuda, n_tokens):
+    """A batch holding one product (alone, or beside an empty weight) takes
+    the one-stream kernel; its output, then accumulated once more, against
+    the oracle."""
+    torch = torch_cuda
+    _note(f"matmul batch of one, tokens={n_tokens}")
+    r, c = 1024, 4096
+    w = _weights("normal", r * c, 77)
+    t = df11.compress(w, shape=(r, c), layout="mfma_tiles")
+    empty = df11.compress(np.zeros(0, np.uint16), shape=(0, 1024), layout="mfma_tiles")
+    xb = _tokens(n_tokens, c, 78)
+    x = _device_x(torch, xb)
+    ref = oracle.linear(oracle.encode(w), xb, r)
+    bound = _bound(xb, w, r, c)
+    for tensors, xs in (([t], [x]), ([empty, t], [_device_x(torch, _tokens(n_tokens, 1024, 79)), x])):
+        ys = df11.matmul_batch(tensors, xs)
+        y = ys[-1]
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= bound), (float(err.max()), float((err - bound).max()))
+        df11.matmul_batch(tensors, xs, outs=ys, accumulate=True)
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - 2 * ref)
+        assert np.all(err <= 2 * bound), (float(err.max()), float((err - 2 * bound).max()))
+
+
 @pytest.mark.parametrize("n_tokens", [1, 2, 8, 16])
 def test_matmul_batch_full_block(torch_cuda, full_block, n_tokens):
     """The whole block's seven products in one launch, every output against
