@@ -114,6 +114,38 @@ def test_tiled_decompress_batch_mixed_and_full_block(torch_cuda):
     assert np.array_equal(_u16(scratch), flat)
 
 
+def test_tiled_streams_with_the_derived_decode_table(torch_cuda):
+    """Tile-ordered streams launched with the page's arrays alone (the
+    first-level table derived in LDS, whose space precedes the whole-line
+    stage): decompression, single and batched, bit-exact; the matrix-core
+    product at one and twenty tokens within the float32 bound."""
+    torch = torch_cuda
+    shapes = [(1024, 4096), (64, 96), (192, 128)]
+    ws = [_weights("stress_tuned" if i == 0 else "normal", r * c, 90 + i) for i, (r, c) in enumerate(shapes)]
+    ts = [df11.compress(w, shape=s, layout="mfma_tiles") for w, s in zip(ws, shapes)]
+    for t in ts:
+        t.use_decode_table(False)
+    _note("tiled, derived table: decompress")
+    for w, t, s in zip(ws, ts, shapes):
+        out = torch.full(s, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        t.decompress(out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(_u16(out), w), s
+    _note("tiled, derived table: batched decompress")
+    outs = [torch.full(s, 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16) for s in shapes]
+    df11.decompress_batch([ts[0], ts[2]], [outs[0], outs[2]])
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(outs[0]), ws[0]) and np.array_equal(_u16(outs[2]), ws[2])
+    for n_tokens in (1, 20):
+        _note(f"tiled, derived table: matmul tokens={n_tokens}")
+        r, c = shapes[0]
+        xb = _tokens(n_tokens, c, 91 + n_tokens)
+        y = ts[0].matmul(_device_x(torch, xb))
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - oracle.linear(oracle.encode(ws[0]), xb, r))
+        assert np.all(err <= _bound(xb, ws[0], r, c)), float(err.max())
+
+
 MATMUL_CASES = [  # (weights, rows, cols)
     ("normal", 64, 32),          # one panel of one k-step: groups span many panels
     ("normal", 128, 1024),       # groups across panel edges
