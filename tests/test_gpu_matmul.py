@@ -114,6 +114,22 @@ def test_tiled_decompress_batch_mixed_and_full_block(torch_cuda):
     assert np.array_equal(_u16(scratch), flat)
 
 
+@pytest.mark.parametrize("bits,gpw", [(10, 2), (12, 2), (11, 1), (11, 4)])
+def test_tiled_decompress_table_widths_and_group_counts(torch_cuda, bits, gpw):
+    """The whole-line decompression at every decode-table width and every
+    number of groups per workgroup, bit-exact."""
+    torch = torch_cuda
+    _note(f"tiled decompress bits={bits} gpw={gpw}")
+    r, c = 1024, 4096
+    w = _weights("student_t", r * c, 95)
+    t = df11.compress(w, shape=(r, c), layout="mfma_tiles", decode_table_bits=bits)
+    t.set_groups_per_workgroup(gpw)
+    out = torch.full((r, c), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    t.decompress(out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out), w)
+
+
 def test_tiled_streams_with_the_derived_decode_table(torch_cuda):
     """Tile-ordered streams launched with the page's arrays alone (the
     first-level table derived in LDS, whose space precedes the whole-line
