@@ -1267,7 +1267,9 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a, const MatmulA
         uint32_t fetched = 0;
         if (sched && tid == 0 && (!kTail || it + 2u >= len))
             fetched = take_ticket(sched, pool_of(wg, a.pools));  // for round it + 2
-        __builtin_amdgcn_s_setprio(0);
+        // (the whole-line merge, with its stage round trips, at the loads' priority:
+        // per-weight block 162.4 -> 159.2 us hot; at 1 or 3, 163.4 and 160.6)
+        __builtin_amdgcn_s_setprio(kPairs ? 2 : 0);
 
         // 2. Merge and store the super-group decoded in the previous
         // iteration (the fused matmul merged it before step 1's loads), then
