@@ -1115,6 +1115,16 @@ def main() -> int:
         counter_runs = [("df11_decode_kernel", "df11_decode_kernel on llama3_8b_block",
                          "--steps 3 --warmup 2 --no-cpu-baseline", "entropy_decoding_df11_amd/csrc/df11_decode.hip",
                          "df11_decode_kernel_llama3_8b_block_counters.md"),
+                        ("df11_decode_pairs_batch_kernel",
+                         "df11_decode_pairs_batch_kernel on llama3_8b_block_per_weight (MFMA tile order back to "
+                         "row-major)",
+                         "--workload llama3_8b_block_per_weight --layout mfma_tiles --steps 3 --warmup 2 "
+                         "--no-cpu-baseline", "entropy_decoding_df11_amd/csrc/df11_decode.hip",
+                         "df11_decode_pairs_batch_kernel_llama3_8b_block_per_weight_tiles_counters.md"),
+                        ("df11_decode_batch_kernel", "df11_decode_batch_kernel on llama3_8b_block_per_weight (row order)",
+                         "--workload llama3_8b_block_per_weight --steps 3 --warmup 2 --no-cpu-baseline",
+                         "entropy_decoding_df11_amd/csrc/df11_decode.hip",
+                         "df11_decode_batch_kernel_llama3_8b_block_per_weight_counters.md"),
                         ("df11_rans_decode_kernel", "df11_rans_decode_kernel on llama3_8b_block (rANS coder)",
                          "--coder rans --steps 3 --warmup 2 --no-cpu-baseline",
                          "entropy_decoding_df11_amd/csrc/df11_rans_decode.hip",
